@@ -1,0 +1,292 @@
+"""Pins that tie the CPU oracle to what the pages and the mathematics fix.
+
+Each pin takes an oracle object (``oracle.Oracle``) and raises AssertionError if
+the oracle disagrees with something that does not come from the oracle itself:
+closed forms, exact rational brute force, invariants, or identities between two
+different oracle functions. ``test_oracle_pins.py`` runs them on the oracle;
+``test_oracle_mutants.py`` runs them on copies with planted mistakes and
+requires that every mistake trips at least one pin.
+
+Pages: "Persistent Kernels: Bridging GPU-CPU Execution" (P1), section "The
+problem" and its "Derivation" (5-point update, grid, spacing 1/(N-1)), and
+section "Implementation details and correctness" (Jacobi into a separate
+matrix); "Grid-Wide Barriers and Persistent Work Queues", "What the barrier
+buys" (convergence check as a grid reduction).
+"""
+
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+from iterative_stencil_pde_amd import inputs
+
+F32_EPS = float(np.finfo(np.float32).eps)
+F64_EPS = float(np.finfo(np.float64).eps)
+
+
+def _ring_from(full: np.ndarray) -> np.ndarray:
+    u = np.zeros_like(full)
+    u[0, :], u[-1, :], u[:, 0], u[:, -1] = full[0, :], full[-1, :], full[:, 0], full[:, -1]
+    return u
+
+
+# --- P-a: 4x4 brute force with a closed form ---------------------------------
+def pin_top_row_4x4(orc):
+    """4x4 grid, top row (i = 3) = 1, rest 0. By symmetry the upper interior pair
+    a_k and the lower pair b_k obey a_{k+1} = (1 + a_k + b_k)/4, b_{k+1} = (a_k + b_k)/4,
+    whose solution from zero is a_k = 3/8 - 2^-(k+2), b_k = 1/8 - 2^-(k+2): exact
+    dyadics, so exact in floating point while they fit the mantissa."""
+    for dtype, kmax in ((np.float32, 20), (np.float64, 48)):
+        u0 = np.zeros((4, 4), dtype=dtype)
+        u0[3, :] = 1
+        for k in (1, 2, 3, 7, kmax):
+            out, _ = orc.jacobi(u0, k)
+            a = 0.375 - 2.0 ** (-(k + 2))
+            b = 0.125 - 2.0 ** (-(k + 2))
+            want = np.zeros((4, 4), dtype=dtype)
+            want[3, :] = 1
+            want[2, 1:3] = a
+            want[1, 1:3] = b
+            assert np.array_equal(out, want), (dtype, k, out)
+
+
+def pin_harmonic_4x4_one_sweep(orc):
+    """Ring x^2 - y^2 with h = 1/3: the discrete Laplacian of x^2 - y^2 is zero, and
+    on a 4x4 grid every interior stencil reads only ring nodes plus interior nodes
+    that are zero at the start whose exact value is 0 or +-1/3; one sweep from zero
+    lands on the fixed point (0, 1/3, -1/3, 0) to within rounding."""
+    n = 4
+    x = np.arange(n) / 3.0
+    full = x[None, :] ** 2 - x[:, None] ** 2
+    for dtype, tol in ((np.float32, 2 * F32_EPS), (np.float64, 4 * F64_EPS)):
+        u0 = _ring_from(full).astype(dtype)
+        for k in (1, 2, 25):
+            out, _ = orc.jacobi(u0, k)
+            interior = out[1:3, 1:3].astype(np.float64)
+            want = np.array([[0.0, 1 / 3], [-1 / 3, 0.0]])
+            assert np.abs(interior - want).max() <= tol, (dtype, k, interior)
+            assert out[1, 1] == 0 and out[2, 2] == 0
+
+
+def pin_poisson_sign_3x3(orc):
+    """-Lap(u) = f with f = 1, h = 1/2, zero ring: the single interior node becomes
+    (0 + h^2 * 1)/4 = 1/16 > 0 (a positive source raises the solution)."""
+    for dtype in (np.float32, np.float64):
+        u0 = np.zeros((3, 3), dtype=dtype)
+        f = np.ones((3, 3), dtype=dtype)
+        out, _ = orc.jacobi(u0, 1, f=f, h=0.5)
+        assert out[1, 1] == 0.0625, out
+        out, _ = orc.jacobi(u0, 2, f=f, h=0.5)
+        assert out[1, 1] == 0.0625  # ring-only neighbours: already the fixed point
+
+
+def _exact_sweep(u, f, h):
+    """One Jacobi sweep in exact rational arithmetic (brute force on tiny grids)."""
+    ny, nx = u.shape
+    U = [[Fraction(float(v)) for v in row] for row in u]
+    hh = Fraction(h) * Fraction(h)
+    out = [row[:] for row in U]
+    for i in range(1, ny - 1):
+        for j in range(1, nx - 1):
+            s = U[i][j - 1] + U[i][j + 1] + U[i - 1][j] + U[i + 1][j]
+            if f is not None:
+                s += hh * Fraction(float(f[i, j]))
+            out[i][j] = s / 4
+    return out
+
+
+def pin_exact_rational_small(orc):
+    """Random 5x7 and 6x4 grids (non-square, so a swapped index changes the result):
+    each oracle sweep is compared with the exact rational sweep of its own input;
+    the difference must stay within the rounding bound of the 5-term sum."""
+    rng = np.random.default_rng(1234)
+    for (ny, nx) in ((5, 7), (6, 4), (7, 5)):
+        for dtype, eps in ((np.float32, F32_EPS), (np.float64, F64_EPS)):
+            u = rng.uniform(-1, 1, (ny, nx)).astype(dtype)
+            f = rng.uniform(-4, 4, (ny, nx)).astype(dtype)
+            h = 0.37
+            for src in (None, f):
+                cur = u
+                for _ in range(3):
+                    nxt, _ = orc.jacobi(cur, 1, f=src, h=h)
+                    ex = _exact_sweep(cur, src, h)
+                    for i in range(ny):
+                        for j in range(nx):
+                            e = ex[i][j]
+                            if i in (0, ny - 1) or j in (0, nx - 1):
+                                assert nxt[i, j] == cur[i, j]
+                                continue
+                            mag = (abs(float(cur[i, j - 1])) + abs(float(cur[i, j + 1]))
+                                   + abs(float(cur[i - 1, j])) + abs(float(cur[i + 1, j])))
+                            if src is not None:
+                                mag += h * h * abs(float(src[i, j]))
+                            bound = 5 * eps * mag / 4 + 1e-300
+                            assert abs(Fraction(float(nxt[i, j])) - e) <= Fraction(bound), (
+                                dtype, ny, nx, i, j, float(nxt[i, j]), float(e))
+                    cur = nxt
+
+
+# --- P-b: discrete harmonic boundary ------------------------------------------
+def pin_harmonic_fixed_point(orc):
+    """u = x^2 - y^2 has zero 5-point Laplacian, so started AT it the iteration stays
+    (up to rounding); started from zero the error decays at the slowest
+    antisymmetric eigenvalue mu = (cos(pi h) + cos(2 pi h))/2 per sweep."""
+    n = 64
+    x = np.arange(n) / (n - 1)
+    full = x[None, :] ** 2 - x[:, None] ** 2
+    out, _ = orc.jacobi(full.astype(np.float32), 1000)
+    assert np.abs(out - full.astype(np.float32)).max() <= 2e-6
+    out, _ = orc.jacobi(full, 1000)
+    assert np.abs(out - full).max() <= 1e-13
+    u0 = _ring_from(full)
+    e1 = np.abs(orc.jacobi(u0, 2000)[0] - full).max()
+    e2 = np.abs(orc.jacobi(u0, 3000)[0] - full).max()
+    mu = (np.cos(np.pi / (n - 1)) + np.cos(2 * np.pi / (n - 1))) / 2
+    assert abs(e2 / e1 - mu ** 1000) <= 1e-3 * mu ** 1000, (e1, e2, mu ** 1000)
+    assert np.abs(orc.jacobi(u0, 8000)[0] - full).max() <= 1e-10
+
+
+def pin_antisymmetry(orc):
+    """With ring x^2 - y^2 (antisymmetric under x <-> y) and a commutative canonical
+    sum, the field stays bitwise antisymmetric: u[i][j] == -u[j][i], diagonal 0."""
+    w = inputs.laplace_harmonic(64, 10)
+    for dtype in (np.float32, np.float64):
+        u0 = w.u0.astype(dtype)
+        for k in (1, 37, 400):
+            out, _ = orc.jacobi(u0, k)
+            assert np.array_equal(out, -out.T)
+            assert np.all(np.diag(out) == 0)
+
+
+# --- P-c: eigenmode decay, any size ------------------------------------------
+def pin_eigenmode_decay(orc):
+    """Laplace on a zero ring with u0 = sin(p pi x) sin(q pi y): the mode is an
+    eigenvector of the Jacobi map with eigenvalue mu = (cos(p pi hx) + cos(q pi hy))/2,
+    so u_K = mu^K u0, and its residual is 4 (1 - mu) mu^K ||u0||. Non-square grid
+    with p != q, so swapping x and y changes mu."""
+    nx, ny, p, q = 37, 23, 3, 2
+    sx = inputs.sinpi_samples(nx, 1 / (nx - 1), p)
+    sy = inputs.sinpi_samples(ny, 1 / (ny - 1), q)
+    phi = sy[:, None] * sx[None, :]
+    phi[0, :] = phi[-1, :] = 0
+    phi[:, 0] = phi[:, -1] = 0
+    mu = (np.cos(p * np.pi / (nx - 1)) + np.cos(q * np.pi / (ny - 1))) / 2
+    K = 40
+    out, res = orc.jacobi(phi, K, checkpoints=[0, K])
+    assert np.abs(out - mu ** K * phi).max() <= 1e-14
+    norm = np.sqrt(np.sum(phi[1:-1, 1:-1] ** 2))
+    assert abs(res[0] - 4 * (1 - mu) * norm) <= 1e-13 * res[0]
+    assert abs(res[1] - 4 * (1 - mu) * mu ** K * norm) <= 1e-12 * res[1]
+    out32, _ = orc.jacobi(phi.astype(np.float32), K)
+    assert np.abs(out32 - mu ** K * phi).max() <= 1e-6
+
+
+def pin_sine_source(orc):
+    """f = sin(pi x) sin(pi y), zero ring and start: u_K = a_K f with
+    a_{k+1} = mu a_k + h^2/4, mu = cos(pi h), so a_K = (h^2/4)(1 - mu^K)/(1 - mu).
+    Pins the sign and the h^2 scaling of the source, and R_0 = h^2 ||f||."""
+    n = 65
+    h = 1 / (n - 1)
+    s = inputs.sinpi_samples(n, h, 1)
+    f = s[:, None] * s[None, :]
+    mu = np.cos(np.pi * h)
+    for K in (1, 50, 300):
+        out, res = orc.jacobi(np.zeros((n, n)), K, f=f, checkpoints=[0])
+        a = (h * h / 4) * (1 - mu ** K) / (1 - mu)
+        assert np.abs(out[1:-1, 1:-1] - a * f[1:-1, 1:-1]).max() <= 1e-12 * a
+        r0 = h * h * np.sqrt(np.sum(f[1:-1, 1:-1] ** 2))
+        assert abs(res[0] - r0) <= 1e-13 * r0
+    out32, _ = orc.jacobi(np.zeros((n, n), np.float32), 50, f=f.astype(np.float32))
+    a = (h * h / 4) * (1 - mu ** 50) / (1 - mu)
+    assert np.abs(out32[1:-1, 1:-1] - a * f[1:-1, 1:-1]).max() <= 1e-6 * a
+
+
+# --- P-d / P-e: maximum principle, monotone residual ---------------------------
+def pin_max_principle(orc):
+    """Laplace with a zero ring and interior in [0, 1]: each sweep averages values in
+    [m, M], and IEEE rounding is monotone, so max never rises, min never falls."""
+    u = inputs.uniform(3, 0, 80 * 96, 0, 1).reshape(80, 96).astype(np.float32)
+    u = u - _ring_from(u)
+    hi, lo = float(u.max()), float(u.min())
+    start_hi = hi
+    for _ in range(12):
+        u, _ = orc.jacobi(u, 25)
+        assert float(u.max()) <= hi and float(u.min()) >= lo
+        assert 0.0 <= float(u.min()) and float(u.max()) <= 1.0
+        hi, lo = float(u.max()), float(u.min())
+    assert hi < start_hi - 0.1  # it does move
+
+
+def pin_monotone_residual(orc):
+    """Poisson, f ~ U[-1,1]: the residual obeys r_{k+1} = G r_k with G = (1/4)
+    adjacency, ||G||_2 = cos(pi h) < 1, so ||r|| strictly decreases."""
+    n = 48
+    f = inputs.uniform(2, 0, n * n, -1, 1).reshape(n, n).astype(np.float32)
+    ck = list(range(0, 2001, 50))
+    _, res = orc.jacobi(np.zeros((n, n), np.float32), 2000, f=f, checkpoints=ck)
+    assert np.all(np.diff(res) < 0), res
+    assert res[-1] < 0.5 * res[0]
+    # the rate: after the transient, the ratio per 50 sweeps approaches cos(pi h)^50
+    mu = np.cos(np.pi / (n - 1))
+    assert abs(res[-1] / res[-2] - mu ** 50) <= 0.02
+
+
+def pin_residual_identity(orc):
+    """For Jacobi, u^{k+1} - u^k = rho^k / 4 exactly in real arithmetic, so the
+    residual (one oracle function) equals 4 ||u^{k+1} - u^k|| built from two sweep
+    results (another oracle function)."""
+    rng = np.random.default_rng(7)
+    ny, nx, h = 32, 40, 0.03
+    u = rng.uniform(-1, 1, (ny, nx))
+    f = rng.uniform(-50, 50, (ny, nx))
+    for k in (0, 3, 30):
+        uk, res = orc.jacobi(u, k, f=f, h=h, checkpoints=[k])
+        uk1, _ = orc.jacobi(uk, 1, f=f, h=h)
+        d = 4 * np.sqrt(np.sum((uk1 - uk)[1:-1, 1:-1] ** 2))
+        assert abs(res[0] - d) <= 1e-12 * res[0], (k, res[0], d)
+        assert abs(orc.residual(uk, f=f, h=h) - res[0]) <= 1e-14 * res[0]
+
+
+# --- P-f: finite propagation and mirror symmetry --------------------------------
+def pin_finite_propagation_mirror(orc):
+    """Top row = 1, all else 0: after K sweeps a cell more than K rows below the top
+    row is still exactly 0; the field is bitwise mirror-symmetric in x."""
+    n = 64
+    u0 = np.zeros((n, n), np.float32)
+    u0[-1, :] = 1
+    for K in (1, 5, 20, 50):
+        out, _ = orc.jacobi(u0, K)
+        assert np.all(out[: n - 1 - K, :] == 0)
+        assert np.any(out[n - 1 - K, 1:-1] != 0)
+        assert np.array_equal(out, out[:, ::-1])
+
+
+def pin_checkpoint_semantics(orc):
+    """A residual checkpoint at k is the residual of the field after k sweeps."""
+    n = 24
+    f = inputs.uniform(9, 0, n * n, -1, 1).reshape(n, n)
+    u0 = np.zeros((n, n))
+    _, res = orc.jacobi(u0, 30, f=f, checkpoints=[0, 0, 7, 30])
+    assert res[0] == res[1]
+    for c, k in ((2, 7), (3, 30)):
+        uk, _ = orc.jacobi(u0, k, f=f)
+        assert res[c] == orc.residual(uk, f=f)
+
+
+ALL_PINS = [
+    pin_top_row_4x4,
+    pin_harmonic_4x4_one_sweep,
+    pin_poisson_sign_3x3,
+    pin_exact_rational_small,
+    pin_harmonic_fixed_point,
+    pin_antisymmetry,
+    pin_eigenmode_decay,
+    pin_sine_source,
+    pin_max_principle,
+    pin_monotone_residual,
+    pin_residual_identity,
+    pin_finite_propagation_mirror,
+    pin_checkpoint_semantics,
+]
