@@ -1,0 +1,199 @@
+"""Benchmark: persistent Jacobi engine vs one kernel launch per sweep, one MI355X.
+
+A step is one pass of the workload's whole task script (all its sweeps and
+residual checks) on inputs already resident in device memory. Default workload:
+256x256 fp32 Poisson, 10,000 sweeps with an L2 residual every 100 sweeps.
+
+Prints one JSON line. The persistent kernel is timed from the host (task
+submission to completion of the last task of the last step) and, for the
+roofline, by HIP events recorded around its single launch on its own stream.
+torch.cuda.synchronize() is deliberately not called while the persistent
+kernel is resident: a device-wide synchronize would wait for that kernel,
+which only leaves on EXIT. Completion of the last task is the device-side
+synchronization point instead.
+"""
+
+from __future__ import annotations
+
+import argparse
+import collections
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from iterative_stencil_pde_amd import inputs, pk  # noqa: E402
+
+METRIC = ("µs/iteration + Gcell-updates/s (persistent vs per-launch); "
+          "HBM GB/s % of peak")
+HBM_PEAK_GBS = 8000.0
+
+
+def step_tasks(w):
+    return [s for s in w.script if s[0] in ("sweep", "residual")]
+
+
+def run_steps(e, w, steps: int, timeout_s: float = 600.0):
+    """Submit `steps` passes of the script, keeping the task ring full."""
+    pending = collections.deque()
+    last = None
+    for _ in range(steps):
+        for s in step_tasks(w):
+            kind = pk.PK_SWEEP if s[0] == "sweep" else pk.PK_RESIDUAL
+            n = s[1] if s[0] == "sweep" else 0
+            while True:
+                rc, t = pk.pk_submit_status(e.h, kind, n)
+                if rc == pk.PK_EBUSY:
+                    last = e.wait(pending.popleft(), timeout_s)
+                    continue
+                if rc != pk.PK_OK:
+                    raise pk.PkError(rc, "pk_submit")
+                pending.append(t)
+                break
+    while pending:
+        last = e.wait(pending.popleft(), timeout_s)
+    return last
+
+
+def algorithmic_bytes(w):
+    """Minimum bytes a step must move: every interior cell read and written once
+    per sweep (plus b read once when present); each residual reads u (and b)."""
+    es = np.dtype(w.dtype).itemsize
+    has_b = w.f is not None
+    per_sweep = w.interior_cells * es * (2 + (1 if has_b else 0))
+    per_residual = w.interior_cells * es * (1 + (1 if has_b else 0))
+    n_res = sum(1 for s in step_tasks(w) if s[0] == "residual")
+    return w.sweeps * per_sweep + n_res * per_residual, per_sweep
+
+
+def measure(w, steps, warmup, **opts):
+    with pk.Engine(w.u0, w.f, h=w.h, **opts) as e:
+        info0 = e.info()
+        run_steps(e, w, warmup)
+        t0 = time.perf_counter()
+        run_steps(e, w, steps)
+        t1 = time.perf_counter()
+        if opts.get("mode", pk.PK_PERSISTENT) == pk.PK_PERSISTENT:
+            e.wait(e.submit(pk.PK_EXIT))
+        info1 = e.info()
+    return t1 - t0, info0, info1
+
+
+def cpu_baseline(w, budget_s: float = 10.0):
+    import oracle
+    ck = w.residual_checkpoints
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.jacobi(w.u0, w.sweeps, f=w.f, h=w.h, checkpoints=ck)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    cells = w.interior_cells * w.sweeps * reps
+    return {"value": round(cells / dt / 1e9, 4), "unit": "Gcell-updates/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} full run(s) of the {w.name} script ({w.sweeps} sweeps, "
+                      f"{len(ck)} residuals), single-threaded C++ oracle, {dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="poisson256", choices=sorted(inputs.WORKLOADS))
+    ap.add_argument("--layout", default="auto", choices=["auto", "stream", "resident"])
+    ap.add_argument("--threads", type=int, default=0)
+    ap.add_argument("--max-blocks", type=int, default=0)
+    ap.add_argument("--halo", type=int, default=0)
+    ap.add_argument("--launch-steps", type=int, default=0,
+                    help="steps for the per-launch comparison (default: same as --steps)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this engine runs on one GPU; --gpus must be 1 "
+                          "(the multi-GPU row-band design is described, not built)"}))
+        sys.exit(2)
+
+    w = inputs.make(args.workload)
+    layout = {"auto": pk.PK_LAYOUT_AUTO, "stream": pk.PK_LAYOUT_STREAM,
+              "resident": pk.PK_LAYOUT_RESIDENT}[args.layout]
+    opts = dict(layout=layout, threads=args.threads, max_blocks=args.max_blocks,
+                halo_depth=args.halo)
+    step_bytes, sweep_bytes = algorithmic_bytes(w)
+    cells_per_step = w.interior_cells * w.sweeps
+
+    # persistent engine
+    dt, info, info_end = measure(w, args.steps, args.warmup, mode=pk.PK_PERSISTENT, **opts)
+    value = cells_per_step * args.steps / dt / 1e9
+    us_iter = dt / (w.sweeps * args.steps) * 1e6
+    kernel_s = info_end.kernel_ms / 1e3
+    launch_bytes = step_bytes * (args.steps + args.warmup)
+    achieved = launch_bytes / kernel_s / 1e9 if kernel_s > 0 else None
+
+    # per-launch baseline, same block count as the persistent grid
+    lsteps = args.launch_steps or args.steps
+    ldt, linfo, _ = measure(w, lsteps, 1, mode=pk.PK_LAUNCH, threads=info.threads,
+                            max_blocks=info.grid_blocks)
+    lvalue = cells_per_step * lsteps / ldt / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "Gcell-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt / args.steps * 1e3, 4),
+        "us_per_iteration": round(us_iter, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64" if w.dtype == np.float64 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "shape": [w.ny, w.nx],
+            "sweeps_per_step": w.sweeps,
+            "residuals_per_step": sum(1 for s in step_tasks(w) if s[0] == "residual"),
+            "mode": "persistent",
+            "layout": {1: "stream", 2: "resident"}[info.layout],
+            "grid_blocks": info.grid_blocks,
+            "threads": info.threads,
+            "halo_depth": info.halo_depth,
+            "band_rows": info.band_rows,
+        },
+        "per_launch": {
+            "value": round(lvalue, 4),
+            "us_per_iteration": round(ldt / (w.sweeps * lsteps) * 1e6, 4),
+            "steps": lsteps,
+            "grid_blocks": linfo.grid_blocks,
+            "kernel_launches_per_step": w.sweeps + 2 * sum(1 for s in step_tasks(w) if s[0] == "residual"),
+            "speedup_persistent": round(value / lvalue, 3),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2) if achieved else None,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 5) if achieved else None,
+            "traffic": None,
+            "kernel": "pk_persistent",
+            "kernel_ms": round(info_end.kernel_ms, 3),
+            "algorithmic_bytes_per_launch": launch_bytes,
+            "algorithmic_bytes_per_sweep": sweep_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

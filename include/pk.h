@@ -1,0 +1,210 @@
+/*
+ * pk.h - C ABI of the persistent-kernel Jacobi engine for AMD MI355X (gfx950).
+ *
+ * The engine advances one 2-D field by 5-point Jacobi sweeps of
+ * -Lap(u) = f (Laplace when f is absent) on a regular grid with Dirichlet data
+ * on the outer ring ("Persistent Kernels: Bridging GPU-CPU Execution", section
+ * "The problem (another PDE solver)" and its "Derivation"; Jacobi as a
+ * separate result matrix per iteration: section "Implementation details and
+ * correctness"). One sweep replaces every interior node by
+ *     0.25 * (((W + E) + (S + N)) + b),   b = (T)((h*h) * f),
+ * in the element type T, IEEE round-to-nearest, no contraction, subnormals kept.
+ *
+ * In PK_PERSISTENT mode the engine launches one co-resident (cooperative)
+ * kernel at create time and drives it through a task ring in fine-grained
+ * pinned host memory: "Persistent Kernels", sections "What if this launch and
+ * execution overhead didn't exist?" and "Base implementation"; sweeps are
+ * separated by a grid-wide barrier made of an arrival counter and a
+ * generation word with release/acquire ordering ("Grid-Wide Barriers and
+ * Persistent Work Queues", section "The barrier is a counter and a
+ * generation"). The grid is sized once from the occupancy query ("@persistent"
+ * page, section "What it promises"), and a grid that is not co-resident is
+ * refused rather than run ("Grid-Wide Barriers", section "The residency
+ * requirement"). PK_LAUNCH mode runs the same sweep body as one ordinary
+ * kernel launch per sweep, with the same block count, as the baseline the
+ * first page compares against (section "Comparing the kernels").
+ *
+ * Conventions
+ *   - Every call returns PK_OK (0) or a negative PK_E* status; nothing aborts
+ *     or throws across this interface.
+ *   - Host arrays are row-major ny x nx of the engine's element type (float
+ *     for PK_F32, double for PK_F64): element (i, j) is at [i * nx + j], row i
+ *     is y = i*h, column j is x = j*h, row ny-1 is the top edge (y = 1).
+ *   - Host arrays passed in are borrowed for the duration of the call only.
+ *   - An engine is used from one host thread at a time. At most one
+ *     PK_PERSISTENT engine per device: its cooperative kernel holds the CUs
+ *     it was sized for until PK_EXIT or pk_destroy. While it runs, do not make
+ *     the host wait on other GPU work queued on the same device.
+ */
+#ifndef PK_H
+#define PK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PK_OK 0
+#define PK_EINVAL (-1)    /* bad argument                                           */
+#define PK_ENOMEM (-2)    /* device or pinned host allocation failed                */
+#define PK_ELAUNCH (-3)   /* kernel launch failed, or cooperative grid not resident */
+#define PK_EDEVICE (-4)   /* HIP runtime error, or the device reported a fault      */
+#define PK_EBUSY (-5)     /* task ring full, or tasks still in flight               */
+#define PK_ESTATE (-6)    /* call not valid in the engine's mode or state           */
+#define PK_ETIMEDOUT (-7) /* pk_wait gave up; the engine is poisoned from then on   */
+
+/* ---- element types, modes, layouts ------------------------------------- */
+#define PK_F32 0
+#define PK_F64 1
+
+#define PK_PERSISTENT 0 /* one co-resident launch driven through the task ring */
+#define PK_LAUNCH 1     /* one kernel launch per sweep (baseline)               */
+
+/* Work layout of the persistent SWEEP task.
+ * STREAM: every sweep streams the field through HBM (grid-stride over bands
+ *   of rows x 64-lane column strips, 128-bit row loads, 3-row register window).
+ * RESIDENT: each block keeps its band of rows (plus halo rows) in LDS for the
+ *   whole task; only the halo rows go through HBM, once every halo_depth sweeps
+ *   (the wider-halo scheme of "Persistent Kernels", "Reflections and next
+ *   steps", "Fewer handshakes", with exact Jacobi semantics).
+ * AUTO: RESIDENT when the field's bands fit in LDS, else STREAM.            */
+#define PK_LAYOUT_AUTO 0
+#define PK_LAYOUT_STREAM 1
+#define PK_LAYOUT_RESIDENT 2
+
+/* ---- tasks -------------------------------------------------------------- */
+#define PK_SWEEP 1    /* n Jacobi sweeps (n >= 0)                                   */
+#define PK_RESIDUAL 2 /* R = sqrt(sum over interior of rho^2),                      */
+                      /*   rho = (((W+E)+(S+N)) + b) - 4u, all in double            */
+#define PK_EXIT 3     /* the persistent kernel returns; the engine stays readable   */
+#define PK_BARRIER 4  /* n grid barriers and nothing else (persistent only; timing) */
+#define PK_STAMP 5    /* n rounds of the barrier visibility check (persistent only):*/
+                      /*   each block stamps its slot, barrier, then checks that a  */
+                      /*   neighbour's and a remote block's slots carry the stamp;  */
+                      /*   pk_result.errors counts mismatches                       */
+
+/* ---- option flags ------------------------------------------------------- */
+/* Debug only: the grid barrier drops its release/acquire ordering (relaxed
+ * atomics, no fences). Every wait still ends and every access stays in bounds;
+ * only the visibility of other blocks' writes is no longer guaranteed, so the
+ * field is expected to diverge from the oracle. A negative control.          */
+#define PK_DBG_BROKEN_BARRIER 0x1u
+
+typedef struct pk_opts {
+    int dtype;             /* PK_F32 or PK_F64                                       */
+    double h;              /* grid spacing; 0 => 1/(nx-1), which requires nx == ny  */
+    int mode;              /* PK_PERSISTENT or PK_LAUNCH                             */
+    int layout;            /* PK_LAYOUT_*; PK_LAUNCH always streams                  */
+    int threads;           /* threads per block, multiple of 64, <= 1024; 0 = auto   */
+    int max_blocks;        /* grid size in blocks; 0 = automatic. STREAM uses it as */
+                           /* given (PK_ELAUNCH if that grid cannot be co-resident),*/
+                           /* RESIDENT as an upper bound (one band per block)       */
+    int halo_depth;        /* RESIDENT: sweeps per halo exchange; 0 = automatic     */
+    unsigned flags;        /* PK_DBG_* flags                                         */
+    void* stream;          /* hipStream_t to use; NULL => the engine makes its own  */
+                           /* non-blocking stream (the persistent kernel must not   */
+                           /* sit on a stream that other work waits behind)         */
+    double idle_timeout_s; /* the persistent kernel leaves by itself after this     */
+                           /* long without a task; 0 => 120 s                       */
+    int reserved[8];       /* must be zero                                           */
+} pk_opts;
+
+typedef struct pk_task {
+    int kind; /* PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP */
+    int n;    /* count for SWEEP, BARRIER and STAMP; ignored otherwise */
+} pk_task;
+
+typedef struct pk_result {
+    double residual;     /* PK_RESIDUAL: R; otherwise 0                               */
+    int64_t sweeps_done; /* sweeps applied to the field when this task ended          */
+    double device_us;    /* task time on the device clock (persistent), else 0        */
+    int64_t errors;      /* PK_STAMP: mismatches seen; otherwise 0                    */
+    int kind;            /* the task's kind                                           */
+    int status;          /* PK_OK, or PK_EDEVICE if the device flagged a fault        */
+} pk_result;
+
+typedef struct pk_info {
+    int nx, ny, dtype, mode, layout;
+    int pitch;              /* device row stride in elements (rows are 256-B aligned)  */
+    int grid_blocks;        /* blocks in the grid (both modes use the same count)       */
+    int threads;            /* threads per block                                         */
+    int blocks_per_cu_max;  /* occupancy query result for the persistent kernel          */
+    int cus;                /* compute units on the device                               */
+    int halo_depth;         /* RESIDENT: sweeps per exchange; 0 otherwise                */
+    int band_rows;          /* rows per band (RESIDENT: per block; STREAM: per unit)     */
+    int strips;             /* STREAM: column strips                                     */
+    size_t lds_bytes;       /* dynamic LDS per block                                     */
+    double kernel_ms;       /* PERSISTENT: launch-to-exit time of the kernel (HIP        */
+                            /* events on its stream), valid after EXIT; LAUNCH: total   */
+                            /* device time of the last pk_run_launch_per_iter batch     */
+    int64_t sweeps_done;
+    int64_t tasks_done;
+    int64_t kernel_launches; /* launches made so far (persistent: 1)                     */
+} pk_info;
+
+typedef struct pk_engine pk_engine;
+
+/* Fill *o with the defaults (PK_F32, h = 0, PK_PERSISTENT, PK_LAYOUT_AUTO, ...). */
+void pk_opts_default(pk_opts* o);
+
+/* Create an engine for an nx x ny field (nx, ny >= 3).
+ *   bc  - host array: the outer ring is the fixed Dirichlet data, the interior
+ *         is the initial guess; copied into both device buffers.
+ *   src - host array of f for -Lap(u) = f, or NULL for Laplace; b = (T)(h*h*f)
+ *         is computed on the device once.
+ * In PK_PERSISTENT mode the cooperative kernel is launched before returning.
+ * Errors: PK_EINVAL (sizes, opts, NULL bc or out, h <= 0 when required),
+ * PK_ENOMEM, PK_ELAUNCH (grid not co-resident / launch refused), PK_EDEVICE.
+ * On error *out is left unchanged and nothing stays allocated. */
+int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* o,
+              pk_engine** out);
+
+/* Queue a task; tasks run in FIFO order. *ticket (may be NULL) receives the
+ * task's sequence number (1, 2, ...). Does not block.
+ * Errors: PK_EINVAL (unknown kind, n < 0, persistent-only kind in PK_LAUNCH
+ * mode), PK_EBUSY (ring full: wait on an older ticket first), PK_ESTATE
+ * (after EXIT, or on a poisoned engine). */
+int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket);
+
+/* Busy-poll (no sleep) until ticket has completed, at most timeout_s seconds
+ * (<= 0 => 60 s). r (may be NULL) receives that task's result.
+ * Errors: PK_EINVAL (ticket never issued), PK_ETIMEDOUT (poisons the engine:
+ * a persistent kernel cannot be pre-empted, so only pk_destroy remains, which
+ * then leaks rather than free memory the kernel may still use), PK_EDEVICE. */
+int pk_wait(pk_engine* e, uint64_t ticket, double timeout_s, pk_result* r);
+
+/* Copy the current field (ny x nx, ring included, row-major, the engine's
+ * element type) into the caller-owned dst of at least ny*nx*elem bytes.
+ * While the persistent kernel runs this is an in-kernel copy task into pinned
+ * host memory (no DMA is queued behind the resident kernel).
+ * Errors: PK_EINVAL (dst NULL, bytes too small), PK_EBUSY (tasks in flight),
+ * PK_ESTATE (poisoned), PK_EDEVICE. */
+int pk_readback(pk_engine* e, void* dst, size_t bytes);
+
+/* PK_LAUNCH engines only: advance the field by n sweeps as n kernel launches
+ * with the engine's block count, back to back (sync_each = 0) or with a
+ * stream synchronize after each launch (sync_each = 1). *elapsed_us (may be
+ * NULL) receives the host wall time from the first launch until the last
+ * sweep finished. Errors: PK_ESTATE (persistent engine: its kernel holds the
+ * CUs, extra launches could not run), PK_EBUSY (tasks in flight), PK_EINVAL. */
+int pk_run_launch_per_iter(pk_engine* e, int n, int sync_each, double* elapsed_us);
+
+/* Engine geometry and counters. */
+int pk_get_info(pk_engine* e, pk_info* info);
+
+/* Stop the kernel (EXIT, bounded wait) and free everything. NULL is a no-op.
+ * If the kernel does not leave, device memory is deliberately leaked and
+ * PK_ETIMEDOUT returned. */
+int pk_destroy(pk_engine* e);
+
+/* Static string for a status code. */
+const char* pk_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PK_H */

@@ -1,0 +1,421 @@
+// Device building blocks of the Jacobi engine (gfx950, wave64).
+//
+// The update every sweep applies to an interior node, in the element type T:
+//     new = 0.25 * (((W + E) + (S + N)) + b)
+// ("Persistent Kernels: Bridging GPU-CPU Execution", "The problem" and its
+// "Derivation", with the source taken as -Lap(u) = f so b = +h*h*f; the order
+// of the additions is fixed so that every implementation rounds alike).
+// W/E are the neighbours in the same row, S/N the rows i-1 / i+1.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pk_shared.h"
+
+namespace pkd {
+
+// ---------------------------------------------------------------------------
+// 16-byte vectors: four floats or two doubles per lane, so one wave moves
+// 1 KiB of a row per load instruction (global_load_dwordx4).
+// ---------------------------------------------------------------------------
+template <typename T>
+struct VecW {
+    static constexpr int W = 16 / sizeof(T);
+};
+
+template <typename T>
+struct alignas(16) Vec {
+    T v[VecW<T>::W];
+};
+
+template <typename T>
+__device__ __forceinline__ Vec<T> vzero() {
+    Vec<T> r;
+#pragma unroll
+    for (int k = 0; k < VecW<T>::W; ++k) r.v[k] = T(0);
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ Vec<T> vload(const T* p) {
+    return *reinterpret_cast<const Vec<T>*>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ void vstore(T* p, const Vec<T>& x) {
+    *reinterpret_cast<Vec<T>*>(p) = x;
+}
+
+// ---------------------------------------------------------------------------
+// Whole-wave lane shifts (DPP wave_shr:1 / wave_shl:1). Lane l receives the
+// value of lane l-1 (from_lower) or l+1 (from_upper); the lane with no source
+// (0 or 63) keeps `edge`, which the caller loads from memory for exactly that
+// lane. This gives each lane its W/E neighbour across the 16-byte vectors.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int dpp_from_lower_i(int edge, int v) {
+    return __builtin_amdgcn_update_dpp(edge, v, 0x138, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int dpp_from_upper_i(int edge, int v) {
+    return __builtin_amdgcn_update_dpp(edge, v, 0x130, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ float from_lower(float edge, float v) {
+    return __int_as_float(dpp_from_lower_i(__float_as_int(edge), __float_as_int(v)));
+}
+__device__ __forceinline__ float from_upper(float edge, float v) {
+    return __int_as_float(dpp_from_upper_i(__float_as_int(edge), __float_as_int(v)));
+}
+__device__ __forceinline__ double from_lower(double edge, double v) {
+    const long long e = __double_as_longlong(edge), x = __double_as_longlong(v);
+    const int lo = dpp_from_lower_i(static_cast<int>(e), static_cast<int>(x));
+    const int hi = dpp_from_lower_i(static_cast<int>(e >> 32), static_cast<int>(x >> 32));
+    return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                                static_cast<long long>(static_cast<unsigned>(lo)));
+}
+__device__ __forceinline__ double from_upper(double edge, double v) {
+    const long long e = __double_as_longlong(edge), x = __double_as_longlong(v);
+    const int lo = dpp_from_upper_i(static_cast<int>(e), static_cast<int>(x));
+    const int hi = dpp_from_upper_i(static_cast<int>(e >> 32), static_cast<int>(x >> 32));
+    return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                                static_cast<long long>(static_cast<unsigned>(lo)));
+}
+
+// ---------------------------------------------------------------------------
+// The stencil on one lane's vector. `col` is the first column of the vector;
+// columns 0 and nx-1 (the Dirichlet ring) and padding columns >= nx keep
+// their value. `edge` holds, for lane 0, column col-1 and, for lane 63,
+// column col+W of the same row; the other lanes get theirs by DPP.
+// ---------------------------------------------------------------------------
+template <typename T, bool HAS_B>
+__device__ __forceinline__ Vec<T> stencil(const Vec<T>& s, const Vec<T>& m, const Vec<T>& n,
+                                          const Vec<T>& b, T edge, int col, int nx) {
+    constexpr int W = VecW<T>::W;
+    const T west_of_first = from_lower(edge, m.v[W - 1]);
+    const T east_of_last = from_upper(edge, m.v[0]);
+    Vec<T> o;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const T w = (k == 0) ? west_of_first : m.v[k - 1];
+        const T e = (k == W - 1) ? east_of_last : m.v[k + 1];
+        T t = (w + e) + (s.v[k] + n.v[k]);
+        if (HAS_B) t = t + b.v[k];
+        const int c = col + k;
+        const bool ring = (c == 0) || (c >= nx - 1);
+        o.v[k] = ring ? m.v[k] : T(0.25) * t;
+    }
+    return o;
+}
+
+// rho^2 summed over the interior nodes of one vector, in double:
+//     rho = (((W + E) + (S + N)) + b) - 4u.
+template <typename T, bool HAS_B>
+__device__ __forceinline__ double rho2(const Vec<T>& s, const Vec<T>& m, const Vec<T>& n,
+                                       const Vec<T>& b, T edge, int col, int nx) {
+    constexpr int W = VecW<T>::W;
+    const T west_of_first = from_lower(edge, m.v[W - 1]);
+    const T east_of_last = from_upper(edge, m.v[0]);
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const double w = static_cast<double>((k == 0) ? west_of_first : m.v[k - 1]);
+        const double e = static_cast<double>((k == W - 1) ? east_of_last : m.v[k + 1]);
+        double t = (w + e) + (static_cast<double>(s.v[k]) + static_cast<double>(n.v[k]));
+        if (HAS_B) t = t + static_cast<double>(b.v[k]);
+        const double r = t - 4.0 * static_cast<double>(m.v[k]);
+        const int c = col + k;
+        const bool ring = (c == 0) || (c >= nx - 1);
+        acc += ring ? 0.0 : r * r;
+    }
+    return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Grid-wide barrier: an arrival counter plus a generation word
+// ("Grid-Wide Barriers and Persistent Work Queues", "The barrier is a counter
+// and a generation"; the "@persistent" page, "grid_barrier"). The counter only
+// ever grows: generation g completes when it reaches (g+1) * G, so there is no
+// reset and no reset race ("Failure modes that only appear at this scale").
+//   - each thread of the block arrives at a block barrier first;
+//   - lane 0 adds 1 to the counter with release ordering (agent scope), so
+//     the block's stores are visible before it is counted;
+//   - the block that brings the counter to (g+1) * G stores g+1 into the
+//     generation word with release ordering; the others spin on it with
+//     relaxed loads and then issue one acquire fence, so the loads after the
+//     barrier see every block's stores (spin relaxed, acquire once:
+//     "Persistent Kernels", "Reflections and next steps", point 2);
+//   - a final block barrier releases the block's other threads.
+// The grid must be co-resident (cooperative launch). A wait that exceeds
+// `spin_ticks` of the device wall clock marks the engine faulted and stops
+// waiting from then on, so every wave still reaches the end of the kernel.
+// `relaxed` (negative control only, set for the barriers between sweeps and
+// stamp rounds of an engine created with PK_DBG_BROKEN_BARRIER) drops the
+// release/acquire ordering: the same atomics, relaxed, and no fence. Every
+// block still runs the same number of barriers and every wait still ends;
+// only the visibility of other blocks' writes is no longer ordered. The task
+// broadcast and the other barriers always keep their ordering, so all blocks
+// agree on what to run.
+// ---------------------------------------------------------------------------
+struct BarrierCtx {
+    pk_dev_state* st;
+    uint32_t grid;
+    uint32_t epoch;      // generations completed (identical in every block)
+    uint64_t spin_ticks;
+    bool broken;         // engine flag: data barriers run relaxed (negative control)
+    bool faulted;        // thread 0's view; broadcast at task boundaries
+};
+
+__device__ __forceinline__ void grid_barrier(BarrierCtx& bc, bool relaxed = false) {
+    __syncthreads();
+    if (threadIdx.x == 0 && bc.grid > 1) {
+        const uint32_t target = bc.epoch + 1;
+        uint32_t old;
+        if (!relaxed)
+            old = __hip_atomic_fetch_add(&bc.st->bar_count, 1u, __ATOMIC_RELEASE,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        else
+            old = __hip_atomic_fetch_add(&bc.st->bar_count, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        if (old == target * bc.grid - 1u) {
+            if (!relaxed)
+                __hip_atomic_store(&bc.st->bar_gen, target, __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            else
+                __hip_atomic_store(&bc.st->bar_gen, target, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        } else if (!bc.faulted) {
+            const uint64_t t0 = wall_clock64();
+            while (static_cast<int32_t>(__hip_atomic_load(&bc.st->bar_gen, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT) -
+                                        target) < 0) {
+                __builtin_amdgcn_s_sleep(1);
+                if (wall_clock64() - t0 > bc.spin_ticks) {
+                    bc.faulted = true;
+                    __hip_atomic_store(&bc.st->fault, static_cast<uint32_t>(PK_FAULT_BARRIER_TIMEOUT),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+        }
+        if (!relaxed) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    bc.epoch += 1;
+    __syncthreads();
+}
+
+// Hardware dispatch places block b on XCD (b mod 8). With remapping, logical
+// block numbers [x*G/8, (x+1)*G/8) all live on XCD x, so neighbouring work
+// (and the halo rows it shares) stays inside one XCD's L2.
+__device__ __forceinline__ int logical_block(int remap, int grid) {
+    const int b = static_cast<int>(blockIdx.x);
+    if (!remap) return b;
+    const int per = grid >> 3;
+    return (b & 7) * per + (b >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed-order double reductions (bitwise reproducible for a given grid).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sum over the block; the result is valid in thread 0.
+__device__ __forceinline__ double block_sum(double v, double* s_red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_sum(v);
+    if (lane == 0) s_red[wave] = v;
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x == 0) {
+        const int nw = blockDim.x >> 6;
+        for (int w = 0; w < nw; ++w) t += s_red[w];
+    }
+    __syncthreads();
+    return t;
+}
+
+// ---------------------------------------------------------------------------
+// Streaming sweep. A unit is a band of interior rows x one strip of 64 lanes
+// x W columns. The wave walks down its band keeping rows i-1, i, i+1 in
+// registers (the column-march of "Persistent Kernels", "Cache-line aware
+// tiling and iteration", with a 16-byte vector per lane instead of one
+// column per thread) and issues CH rows of loads before computing them.
+// ---------------------------------------------------------------------------
+template <typename T, bool HAS_B, int CH>
+__device__ __forceinline__ void stream_unit(const T* __restrict__ src, T* __restrict__ dst,
+                                            const T* __restrict__ bsrc, int nx, int pitch, int c0,
+                                            int r_begin, int r_end) {
+    constexpr int W = VecW<T>::W;
+    const int lane = threadIdx.x & 63;
+    const int col = c0 + lane * W;
+    const bool act = col < nx;
+    const int hcol = (lane == 0) ? c0 - 1 : c0 + 64 * W;
+    const bool hact = (lane == 0) ? (c0 > 0) : ((lane == 63) && (c0 + 64 * W < nx));
+    const size_t p = static_cast<size_t>(pitch);
+
+    Vec<T> up = act ? vload(src + static_cast<size_t>(r_begin - 1) * p + col) : vzero<T>();
+    Vec<T> mid = act ? vload(src + static_cast<size_t>(r_begin) * p + col) : vzero<T>();
+    T mh = hact ? src[static_cast<size_t>(r_begin) * p + hcol] : T(0);
+
+    for (int r = r_begin; r < r_end; r += CH) {
+        Vec<T> dn[CH];
+        Vec<T> bb[CH];
+        T dh[CH];
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int rl = min(r + k + 1, r_end);  // r_end itself is a valid row
+            dn[k] = act ? vload(src + static_cast<size_t>(rl) * p + col) : vzero<T>();
+            dh[k] = hact ? src[static_cast<size_t>(rl) * p + hcol] : T(0);
+            if (HAS_B) {
+                const int rb = min(r + k, r_end - 1);
+                bb[k] = act ? vload(bsrc + static_cast<size_t>(rb) * p + col) : vzero<T>();
+            } else {
+                bb[k] = vzero<T>();
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const Vec<T> o = stencil<T, HAS_B>(up, mid, dn[k], bb[k], mh, col, nx);
+            if (act && r + k < r_end) vstore(dst + static_cast<size_t>(r + k) * p + col, o);
+            up = mid;
+            mid = dn[k];
+            mh = dh[k];
+        }
+    }
+}
+
+template <typename T, bool HAS_B>
+__device__ __forceinline__ double stream_unit_residual(const T* __restrict__ src,
+                                                       const T* __restrict__ bsrc, int nx,
+                                                       int pitch, int c0, int r_begin, int r_end) {
+    constexpr int W = VecW<T>::W;
+    constexpr int CH = 4;
+    const int lane = threadIdx.x & 63;
+    const int col = c0 + lane * W;
+    const bool act = col < nx;
+    const int hcol = (lane == 0) ? c0 - 1 : c0 + 64 * W;
+    const bool hact = (lane == 0) ? (c0 > 0) : ((lane == 63) && (c0 + 64 * W < nx));
+    const size_t p = static_cast<size_t>(pitch);
+
+    Vec<T> up = act ? vload(src + static_cast<size_t>(r_begin - 1) * p + col) : vzero<T>();
+    Vec<T> mid = act ? vload(src + static_cast<size_t>(r_begin) * p + col) : vzero<T>();
+    T mh = hact ? src[static_cast<size_t>(r_begin) * p + hcol] : T(0);
+    double acc = 0.0;
+    for (int r = r_begin; r < r_end; r += CH) {
+        Vec<T> dn[CH];
+        Vec<T> bb[CH];
+        T dh[CH];
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int rl = min(r + k + 1, r_end);
+            dn[k] = act ? vload(src + static_cast<size_t>(rl) * p + col) : vzero<T>();
+            dh[k] = hact ? src[static_cast<size_t>(rl) * p + hcol] : T(0);
+            if (HAS_B) {
+                const int rb = min(r + k, r_end - 1);
+                bb[k] = act ? vload(bsrc + static_cast<size_t>(rb) * p + col) : vzero<T>();
+            } else {
+                bb[k] = vzero<T>();
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const double q = rho2<T, HAS_B>(up, mid, dn[k], bb[k], mh, col, nx);
+            if (act && r + k < r_end) acc += q;
+            up = mid;
+            mid = dn[k];
+            mh = dh[k];
+        }
+    }
+    return acc;
+}
+
+template <typename T, bool HAS_B>
+__device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restrict__ src,
+                                             T* __restrict__ dst) {
+    constexpr int W = VecW<T>::W;
+    const int wpb = static_cast<int>(blockDim.x) >> 6;
+    const int gw = logical_block(a.xcd_remap, a.grid) * wpb + (static_cast<int>(threadIdx.x) >> 6);
+    const int nw = a.grid * wpb;
+    const int units = a.strips * a.bands;
+    const T* bsrc = static_cast<const T*>(a.b);
+    for (int u = gw; u < units; u += nw) {
+        const int strip = u % a.strips, band = u / a.strips;
+        const int r_begin = 1 + band * a.band_rows;
+        const int r_end = min(a.ny - 1, r_begin + a.band_rows);
+        if (r_begin >= r_end) continue;
+        // rows of loads in flight per wave: fewer when b doubles the traffic
+        constexpr int CH = (HAS_B || sizeof(T) == 8) ? 4 : 8;
+        stream_unit<T, HAS_B, CH>(src, dst, bsrc, a.nx, a.pitch, strip * 64 * W, r_begin, r_end);
+    }
+}
+
+// Per-block sum of rho^2 over the same units; valid in thread 0.
+template <typename T, bool HAS_B>
+__device__ __forceinline__ double stream_residual_block(const pk_kargs& a, const T* __restrict__ src,
+                                                        double* s_red) {
+    constexpr int W = VecW<T>::W;
+    const int wpb = static_cast<int>(blockDim.x) >> 6;
+    const int gw = logical_block(a.xcd_remap, a.grid) * wpb + (static_cast<int>(threadIdx.x) >> 6);
+    const int nw = a.grid * wpb;
+    const int units = a.strips * a.bands;
+    const T* bsrc = static_cast<const T*>(a.b);
+    double acc = 0.0;
+    for (int u = gw; u < units; u += nw) {
+        const int strip = u % a.strips, band = u / a.strips;
+        const int r_begin = 1 + band * a.band_rows;
+        const int r_end = min(a.ny - 1, r_begin + a.band_rows);
+        if (r_begin >= r_end) continue;
+        acc += stream_unit_residual<T, HAS_B>(src, bsrc, a.nx, a.pitch, strip * 64 * W, r_begin,
+                                              r_end);
+    }
+    return block_sum(acc, s_red);
+}
+
+// Fixed-order total of the per-block partials, by the first wave of a block;
+// the result is valid in thread 0.
+__device__ __forceinline__ double sum_partials(const double* partials, int grid) {
+    const int lane = threadIdx.x & 63;
+    double v = 0.0;
+    if (threadIdx.x < 64)
+        for (int k = lane; k < grid; k += 64) v += partials[k];
+    return wave_sum(v);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-resident sweep rows: compute LDS rows [lo, hi) of D from S (both with
+// row stride lp elements, nv = lp / W vectors per row). Consecutive lanes hold
+// consecutive vectors in row-major order, so the DPP shifts give W/E inside a
+// wave; lanes 0 and 63 read their outside neighbour from LDS. Where a lane's
+// shifted-in neighbour belongs to another row it always lands on a ring or
+// padding column, which keeps its value.
+// ---------------------------------------------------------------------------
+template <typename T, bool HAS_B>
+__device__ __forceinline__ void resident_rows(const T* S, T* D, const T* Bt, int lo, int hi, int nv,
+                                              int lp, int nx) {
+    constexpr int W = VecW<T>::W;
+    const int lane = threadIdx.x & 63;
+    const int total = (hi - lo) * nv;
+    for (int base = static_cast<int>(threadIdx.x) - lane; base < total;
+         base += static_cast<int>(blockDim.x)) {
+        const int idx = base + lane;
+        const bool act = idx < total;
+        const int id = act ? idx : total - 1;
+        const int rr = lo + id / nv;
+        const int col = (id % nv) * W;
+        const T* p = S + rr * lp + col;
+        const Vec<T> m = vload(p);
+        const Vec<T> s = vload(p - lp);
+        const Vec<T> n = vload(p + lp);
+        const Vec<T> bb = HAS_B ? vload(Bt + rr * lp + col) : vzero<T>();
+        T edge = T(0);
+        if (lane == 0 && col > 0) edge = p[-1];
+        if (lane == 63 && col + W < lp) edge = p[W];
+        const Vec<T> o = stencil<T, HAS_B>(s, m, n, bb, edge, col, nx);
+        if (act) vstore(D + rr * lp + col, o);
+    }
+}
+
+}  // namespace pkd

@@ -1,0 +1,611 @@
+// Host runtime of the Jacobi engine: argument checks, grid planning from the
+// occupancy query, device buffers, the pinned mailbox, the cooperative launch,
+// task submission and completion, and the launch-per-sweep baseline.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/pk.h"
+#include "pk_launch.h"
+#include "pk_ring.h"
+#include "pk_shared.h"
+
+namespace {
+
+enum EngineState { RUNNING = 0, EXITED = 1, POISONED = 2 };
+
+struct Plan {
+    int layout = PK_LAYOUT_STREAM;
+    int threads = 1024;
+    int grid = 1;
+    int strips = 1, bands = 1, band_rows = 1;
+    int res_band_rows = 0, res_halo = 0, res_ext_rows = 0, lds_pitch = 0;
+    size_t lds_bytes = 0;
+    int xcd_remap = 0;
+    int occ = 0;  // blocks per CU allowed by the occupancy query
+};
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Stream geometry for a given grid: one unit (band x strip) per wave where the
+// field is large enough, never less than `min_rows` rows per band.
+void stream_geometry(Plan& p, int nx, int ny, int esize, int min_rows) {
+    const int W = 16 / esize;
+    p.strips = ceil_div(nx, 64 * W);
+    const int interior = ny - 2;
+    const int nw = p.grid * (p.threads / 64);
+    int bands = std::max(1, nw / p.strips);
+    bands = std::min(bands, std::max(1, interior / std::max(1, min_rows)));
+    p.band_rows = ceil_div(interior, bands);
+    p.bands = ceil_div(interior, p.band_rows);
+}
+
+}  // namespace
+
+struct pk_engine {
+    int nx = 0, ny = 0, dtype = PK_F32, esize = 4, pitch = 0;
+    size_t pitch_bytes = 0;
+    int mode = PK_PERSISTENT;
+    bool has_b = false;
+    double h = 0.0;
+    unsigned flags = 0;
+    Plan plan;
+    int cus = 0;
+    int wclk_khz = 100000;  // device wall clock rate
+    void* d_u[2] = {nullptr, nullptr};
+    void* d_b = nullptr;
+    pk_dev_state* d_st = nullptr;
+    double* d_partials = nullptr;
+    uint32_t* d_stamp = nullptr;
+    pk_mailbox* h_mail = nullptr;
+    pk_mailbox* d_mail = nullptr;
+    void* h_staging = nullptr;
+    void* d_staging = nullptr;
+    double* h_lres = nullptr;  // launch mode: residual results (pinned, mapped)
+    double* d_lres = nullptr;
+    hipStream_t stream = nullptr;
+    bool own_stream = false;
+    hipEvent_t ev_start = nullptr, ev_end = nullptr;
+    hipEvent_t ev_ticket[PK_RING] = {};
+    pk_kargs ka{};
+    int state = RUNNING;
+    bool launched = false;
+    pkr::HostRing ring;
+    // launch mode bookkeeping
+    int cur = 0;
+    int64_t sweeps_done = 0;
+    int64_t launches = 0;
+    double last_batch_ms = 0.0;
+    std::vector<pk_result> lresults;  // by ticket
+};
+
+namespace {
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int map_err(hipError_t e) {
+    if (e == hipSuccess) return PK_OK;
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return PK_ENOMEM;
+    return PK_EDEVICE;
+}
+
+void release(pk_engine* e) {
+    if (!e) return;
+    for (auto& ev : e->ev_ticket)
+        if (ev) (void)hipEventDestroy(ev);
+    if (e->ev_start) (void)hipEventDestroy(e->ev_start);
+    if (e->ev_end) (void)hipEventDestroy(e->ev_end);
+    if (e->d_u[0]) (void)hipFree(e->d_u[0]);
+    if (e->d_u[1]) (void)hipFree(e->d_u[1]);
+    if (e->d_b) (void)hipFree(e->d_b);
+    if (e->d_st) (void)hipFree(e->d_st);
+    if (e->d_partials) (void)hipFree(e->d_partials);
+    if (e->d_stamp) (void)hipFree(e->d_stamp);
+    if (e->h_mail) (void)hipHostFree(e->h_mail);
+    if (e->h_staging) (void)hipHostFree(e->h_staging);
+    if (e->h_lres) (void)hipHostFree(e->h_lres);
+    if (e->own_stream && e->stream) (void)hipStreamDestroy(e->stream);
+    delete e;
+}
+
+// Choose layout, block size and grid. Both modes share the result, so the
+// launch-per-sweep baseline uses the same block count as the persistent kernel
+// ("Persistent Kernels", "Sketching out the experiment").
+int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
+    Plan p;
+    p.threads = o.threads ? o.threads : 1024;
+    const int W = 16 / e->esize;
+    const int interior = e->ny - 2;
+    const size_t lds_max = prop.sharedMemPerBlock > 1024 ? prop.sharedMemPerBlock - 1024 : 0;
+
+    bool resident = false;
+    if (e->mode == PK_PERSISTENT && o.layout != PK_LAYOUT_STREAM) {
+        const int lp = static_cast<int>(round_up(static_cast<size_t>(e->nx), W));
+        const size_t row_bytes = static_cast<size_t>(lp) * e->esize * (e->has_b ? 3 : 2);
+        const int max_rows = static_cast<int>(lds_max / row_bytes);
+        int g = 0, band = 0, m = 0;
+        if (max_rows >= e->ny && (o.max_blocks == 0 || o.max_blocks == 1)) {
+            g = 1;                          // the whole field lives in one block's LDS
+            band = interior;
+            m = 1 << 20;                    // no neighbours: one period per task
+        } else if (max_rows >= 3) {
+            const int gmax = std::min(e->cus, interior);
+            if (o.max_blocks > 0) {
+                g = std::min(o.max_blocks, gmax);
+                band = ceil_div(interior, g);
+                m = o.halo_depth > 0 ? o.halo_depth : 8;
+                m = std::min(m, (max_rows - band) / 2);
+            } else {
+                m = o.halo_depth > 0 ? o.halo_depth : 8;
+                m = std::min(m, max_rows / 3);
+                band = max_rows - 2 * m;
+                g = ceil_div(interior, band);
+                if (g > gmax) { g = 0; }
+            }
+            if (g > 0) {
+                band = ceil_div(interior, g);
+                g = ceil_div(interior, band);
+                const int last = interior - (g - 1) * band;
+                m = std::min({m, band, last});
+                if (band + 2 * m > max_rows || m < 1) g = 0;
+            }
+        }
+        if (g > 0) {
+            p.layout = PK_LAYOUT_RESIDENT;
+            p.grid = g;
+            p.res_band_rows = band;
+            p.res_halo = m;
+            p.res_ext_rows = std::min(e->ny, band + 2 * std::min(m, e->ny));
+            p.lds_pitch = lp;
+            p.lds_bytes = static_cast<size_t>(p.res_ext_rows) * lp * e->esize * (e->has_b ? 3 : 2);
+            resident = true;
+        } else if (o.layout == PK_LAYOUT_RESIDENT) {
+            return PK_EINVAL;  // asked for, but the bands do not fit in LDS
+        }
+    }
+    if (!resident) {
+        p.layout = PK_LAYOUT_STREAM;
+        const int wpb = p.threads / 64;
+        // enough blocks for one wave per unit of >= 4 rows, at most one block per CU
+        const int strips = ceil_div(e->nx, 64 * W);
+        const int units = strips * std::max(1, interior / 4);
+        int g = std::min(e->cus, ceil_div(units, wpb));
+        if (o.max_blocks > 0) g = o.max_blocks;  // an explicit grid, checked below
+        p.grid = std::max(1, g);
+    }
+    p.xcd_remap = (p.grid >= 8 && p.grid % 8 == 0) ? 1 : 0;
+    stream_geometry(p, e->nx, e->ny, e->esize, 4);
+
+    // occupancy of the kernel that will be resident, at its LDS footprint
+    const void* fn = e->mode == PK_PERSISTENT ? pkk_persistent_fn(e->dtype, e->has_b, p.layout)
+                                              : pkk_sweep_fn(e->dtype, e->has_b);
+    if (p.lds_bytes > 0)
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  static_cast<int>(p.lds_bytes));
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, p.threads, p.lds_bytes) != hipSuccess)
+        return PK_EDEVICE;
+    p.occ = occ;
+    if (occ < 1) return PK_ELAUNCH;
+    if (e->mode == PK_PERSISTENT && p.grid > occ * e->cus) return PK_ELAUNCH;
+    e->plan = p;
+    return PK_OK;
+}
+
+void fill_kargs(pk_engine* e) {
+    pk_kargs& a = e->ka;
+    const Plan& p = e->plan;
+    a.u[0] = e->d_u[0];
+    a.u[1] = e->d_u[1];
+    a.b = e->d_b;
+    a.nx = e->nx;
+    a.ny = e->ny;
+    a.pitch = e->pitch;
+    a.cur0 = 0;
+    a.strips = p.strips;
+    a.bands = p.bands;
+    a.band_rows = p.band_rows;
+    a.res_band_rows = p.res_band_rows;
+    a.res_halo = p.res_halo;
+    a.res_ext_rows = p.res_ext_rows;
+    a.lds_pitch = p.lds_pitch;
+    a.layout = p.layout;
+    a.grid = p.grid;
+    a.xcd_remap = p.xcd_remap;
+    a.flags = e->flags;
+    a.st = e->d_st;
+    a.mail = e->d_mail;
+    a.partials = e->d_partials;
+    a.staging = e->d_staging;
+    a.stamp = e->d_stamp;
+}
+
+bool poll_exited(void* ctx) {
+    auto* e = static_cast<pk_engine*>(ctx);
+    return __atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE) != 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+void pk_opts_default(pk_opts* o) {
+    if (!o) return;
+    std::memset(o, 0, sizeof(*o));
+    o->dtype = PK_F32;
+    o->mode = PK_PERSISTENT;
+    o->layout = PK_LAYOUT_AUTO;
+}
+
+const char* pk_strerror(int s) {
+    switch (s) {
+        case PK_OK: return "ok";
+        case PK_EINVAL: return "invalid argument";
+        case PK_ENOMEM: return "out of memory";
+        case PK_ELAUNCH: return "launch failed or grid not co-resident";
+        case PK_EDEVICE: return "device or runtime error";
+        case PK_EBUSY: return "busy: ring full or tasks in flight";
+        case PK_ESTATE: return "not valid in the engine's mode or state";
+        case PK_ETIMEDOUT: return "timed out; engine poisoned";
+        default: return "unknown status";
+    }
+}
+
+int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* opts,
+              pk_engine** out) {
+    if (!out || !bc || nx < 3 || ny < 3) return PK_EINVAL;
+    pk_opts o;
+    if (opts) o = *opts;
+    else pk_opts_default(&o);
+    if (o.dtype != PK_F32 && o.dtype != PK_F64) return PK_EINVAL;
+    if (o.mode != PK_PERSISTENT && o.mode != PK_LAUNCH) return PK_EINVAL;
+    if (o.layout < PK_LAYOUT_AUTO || o.layout > PK_LAYOUT_RESIDENT) return PK_EINVAL;
+    if (o.threads != 0 && (o.threads < 64 || o.threads > 1024 || o.threads % 64 != 0)) return PK_EINVAL;
+    if (o.max_blocks < 0 || o.halo_depth < 0 || o.idle_timeout_s < 0) return PK_EINVAL;
+    if (o.flags & ~PK_DBG_BROKEN_BARRIER) return PK_EINVAL;
+    for (int r : o.reserved)
+        if (r != 0) return PK_EINVAL;
+    double h = o.h;
+    if (h == 0.0) {
+        if (nx != ny) return PK_EINVAL;
+        h = 1.0 / (nx - 1);
+    }
+    if (!(h > 0.0)) return PK_EINVAL;
+    const int esize = o.dtype == PK_F64 ? 8 : 4;
+    if (static_cast<int64_t>(nx) * esize > (int64_t(1) << 30)) return PK_EINVAL;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PK_EDEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PK_EDEVICE;
+
+    pk_engine* e = new (std::nothrow) pk_engine();
+    if (!e) return PK_ENOMEM;
+    e->nx = nx;
+    e->ny = ny;
+    e->dtype = o.dtype;
+    e->esize = esize;
+    e->mode = o.mode;
+    e->has_b = src != nullptr;
+    e->h = h;
+    e->flags = o.flags;
+    e->cus = prop.multiProcessorCount;
+    e->pitch_bytes = round_up(static_cast<size_t>(nx) * esize, 256);
+    e->pitch = static_cast<int>(e->pitch_bytes / esize);
+
+    int rc = plan_engine(e, o, prop);
+    if (rc != PK_OK) { release(e); return rc; }
+
+    hipError_t he;
+    const size_t fbytes = e->pitch_bytes * static_cast<size_t>(ny);
+#define PK_TRY(expr)                                 \
+    do {                                             \
+        he = (expr);                                 \
+        if (he != hipSuccess) {                      \
+            rc = map_err(he);                        \
+            release(e);                              \
+            return rc;                               \
+        }                                            \
+    } while (0)
+
+    if (o.stream) {
+        e->stream = static_cast<hipStream_t>(o.stream);
+    } else {
+        PK_TRY(hipStreamCreateWithFlags(&e->stream, hipStreamNonBlocking));
+        e->own_stream = true;
+    }
+    PK_TRY(hipMalloc(&e->d_u[0], fbytes));
+    PK_TRY(hipMalloc(&e->d_u[1], fbytes));
+    PK_TRY(hipMemsetAsync(e->d_u[0], 0, fbytes, e->stream));
+    PK_TRY(hipMemsetAsync(e->d_u[1], 0, fbytes, e->stream));
+    const size_t hrow = static_cast<size_t>(nx) * esize;
+    PK_TRY(hipMemcpy2DAsync(e->d_u[0], e->pitch_bytes, bc, hrow, hrow, ny, hipMemcpyHostToDevice, e->stream));
+    PK_TRY(hipMemcpy2DAsync(e->d_u[1], e->pitch_bytes, bc, hrow, hrow, ny, hipMemcpyHostToDevice, e->stream));
+    if (src) {
+        void* d_f = nullptr;
+        PK_TRY(hipMalloc(&e->d_b, fbytes));
+        PK_TRY(hipMalloc(&d_f, fbytes));
+        he = hipMemsetAsync(d_f, 0, fbytes, e->stream);
+        if (he == hipSuccess)
+            he = hipMemcpy2DAsync(d_f, e->pitch_bytes, src, hrow, hrow, ny, hipMemcpyHostToDevice, e->stream);
+        if (he == hipSuccess)
+            he = pkk_launch_scale_source(e->dtype, d_f, e->d_b, nx, ny, e->pitch, h * h, e->stream);
+        if (he == hipSuccess) he = hipStreamSynchronize(e->stream);
+        (void)hipFree(d_f);
+        if (he != hipSuccess) { rc = map_err(he); release(e); return rc; }
+    }
+    PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_st), sizeof(pk_dev_state)));
+    PK_TRY(hipMemsetAsync(e->d_st, 0, sizeof(pk_dev_state), e->stream));
+    PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_partials), sizeof(double) * e->plan.grid));
+    PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_stamp), sizeof(uint32_t) * 2 * 64 * e->plan.grid));
+    PK_TRY(hipMemsetAsync(e->d_stamp, 0, sizeof(uint32_t) * 2 * 64 * e->plan.grid, e->stream));
+    PK_TRY(hipHostMalloc(reinterpret_cast<void**>(&e->h_mail), sizeof(pk_mailbox),
+                         hipHostMallocCoherent | hipHostMallocMapped));
+    std::memset(e->h_mail, 0, sizeof(pk_mailbox));
+    PK_TRY(hipHostGetDevicePointer(reinterpret_cast<void**>(&e->d_mail), e->h_mail, 0));
+    PK_TRY(hipEventCreate(&e->ev_start));
+    PK_TRY(hipEventCreate(&e->ev_end));
+    if (e->mode == PK_PERSISTENT) {
+        PK_TRY(hipHostMalloc(&e->h_staging, static_cast<size_t>(nx) * ny * esize,
+                             hipHostMallocCoherent | hipHostMallocMapped));
+        PK_TRY(hipHostGetDevicePointer(&e->d_staging, e->h_staging, 0));
+    } else {
+        PK_TRY(hipHostMalloc(reinterpret_cast<void**>(&e->h_lres), sizeof(double) * PK_RING,
+                             hipHostMallocCoherent | hipHostMallocMapped));
+        PK_TRY(hipHostGetDevicePointer(reinterpret_cast<void**>(&e->d_lres), e->h_lres, 0));
+        for (auto& ev : e->ev_ticket) PK_TRY(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    }
+    fill_kargs(e);
+    int wclk_khz = 0;
+    if (hipDeviceGetAttribute(&wclk_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || wclk_khz <= 0)
+        wclk_khz = 100000;
+    e->wclk_khz = wclk_khz;
+    const double idle_s = o.idle_timeout_s > 0 ? o.idle_timeout_s : 120.0;
+    e->ka.idle_ticks = static_cast<uint64_t>(idle_s * wclk_khz * 1000.0);
+    e->ka.spin_ticks = static_cast<uint64_t>((idle_s + 10.0) * wclk_khz * 1000.0);
+    PK_TRY(hipStreamSynchronize(e->stream));
+    e->ring.attach(e->h_mail);
+
+    if (e->mode == PK_PERSISTENT) {
+        const void* fn = pkk_persistent_fn(e->dtype, e->has_b, e->plan.layout);
+        void* args[] = {&e->ka};
+        PK_TRY(hipEventRecord(e->ev_start, e->stream));
+        he = hipLaunchCooperativeKernel(fn, dim3(e->plan.grid), dim3(e->plan.threads), args,
+                                        static_cast<unsigned>(e->plan.lds_bytes), e->stream);
+        if (he != hipSuccess) {
+            (void)hipStreamSynchronize(e->stream);
+            release(e);
+            return PK_ELAUNCH;
+        }
+        e->launched = true;
+        e->launches = 1;
+        (void)hipEventRecord(e->ev_end, e->stream);
+    }
+#undef PK_TRY
+    *out = e;
+    return PK_OK;
+}
+
+int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket) {
+    if (!e) return PK_EINVAL;
+    if (e->state != RUNNING) return PK_ESTATE;
+    const bool known = t.kind == PK_SWEEP || t.kind == PK_RESIDUAL || t.kind == PK_EXIT ||
+                       t.kind == PK_BARRIER || t.kind == PK_STAMP;
+    if (!known || t.n < 0) return PK_EINVAL;
+    if (e->mode == PK_LAUNCH) {
+        if (t.kind == PK_BARRIER || t.kind == PK_STAMP) return PK_EINVAL;
+        const uint64_t seq = e->lresults.size() + 1;
+        hipEvent_t& ev = e->ev_ticket[seq % PK_RING];
+        if (seq > PK_RING) {  // the slot's previous ticket must be finished
+            const hipError_t q = hipEventQuery(ev);
+            if (q == hipErrorNotReady) return PK_EBUSY;
+            if (q != hipSuccess) return PK_EDEVICE;
+            pk_result& old = e->lresults[seq - PK_RING - 1];
+            if (old.kind == PK_RESIDUAL) old.residual = e->h_lres[(seq - PK_RING) % PK_RING];
+        }
+        pk_result r{};
+        r.kind = t.kind;
+        hipError_t he = hipSuccess;
+        if (t.kind == PK_SWEEP) {
+            for (int s = 0; s < t.n && he == hipSuccess; ++s) {
+                he = pkk_launch_sweep(e->dtype, e->has_b, e->ka, e->plan.threads, e->cur, e->stream);
+                e->cur ^= 1;
+                ++e->launches;
+            }
+            e->sweeps_done += t.n;
+        } else if (t.kind == PK_RESIDUAL) {
+            he = pkk_launch_residual(e->dtype, e->has_b, e->ka, e->plan.threads, e->cur,
+                                     e->d_lres + seq % PK_RING, e->stream);
+            e->launches += 2;
+        } else if (t.kind == PK_EXIT) {
+            e->state = EXITED;
+        }
+        if (he == hipSuccess) he = hipEventRecord(ev, e->stream);
+        if (he != hipSuccess) { e->state = POISONED; return PK_EDEVICE; }
+        r.sweeps_done = e->sweeps_done;
+        e->lresults.push_back(r);
+        if (ticket) *ticket = seq;
+        return PK_OK;
+    }
+    if (__atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE)) {
+        e->state = EXITED;  // the kernel left by itself (idle timeout or fault)
+        return PK_ESTATE;
+    }
+    uint64_t seq = 0;
+    const int rc = e->ring.publish(t.kind, t.n, &seq);
+    if (rc != PK_OK) return rc;
+    if (t.kind == PK_EXIT) e->state = EXITED;
+    if (ticket) *ticket = seq;
+    return PK_OK;
+}
+
+int pk_wait(pk_engine* e, uint64_t ticket, double timeout_s, pk_result* r) {
+    if (!e) return PK_EINVAL;
+    if (e->state == POISONED) return PK_ESTATE;
+    if (timeout_s <= 0) timeout_s = 60.0;
+    if (e->mode == PK_LAUNCH) {
+        if (ticket == 0 || ticket > e->lresults.size()) return PK_EINVAL;
+        const uint64_t latest = e->lresults.size();
+        // events are reused every PK_RING tickets; a later ticket done implies this one
+        const auto t0 = std::chrono::steady_clock::now();
+        if (latest - ticket < PK_RING) {
+            hipEvent_t ev = e->ev_ticket[ticket % PK_RING];
+            for (;;) {
+                const hipError_t q = hipEventQuery(ev);
+                if (q == hipSuccess) break;
+                if (q != hipErrorNotReady) { e->state = POISONED; return PK_EDEVICE; }
+                const double el = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+                if (el > timeout_s) { e->state = POISONED; return PK_ETIMEDOUT; }
+            }
+            pk_result& res = e->lresults[ticket - 1];
+            if (res.kind == PK_RESIDUAL) res.residual = e->h_lres[ticket % PK_RING];
+        }
+        if (r) *r = e->lresults[ticket - 1];
+        return PK_OK;
+    }
+    pkr::DoneInfo d{};
+    const int rc = e->ring.wait(ticket, timeout_s, &d, poll_exited, e);
+    if (rc == PK_ETIMEDOUT) e->state = POISONED;
+    if (rc != PK_OK) return rc;
+    if (r) {
+        r->residual = d.residual;
+        r->sweeps_done = d.sweeps_done;
+        r->errors = d.errors;
+        r->kind = d.kind;
+        r->status = d.status;
+        r->device_us = d.t_end >= d.t_begin ? (d.t_end - d.t_begin) * 1000.0 / e->wclk_khz : 0.0;
+    }
+    return d.status == PK_OK ? PK_OK : d.status;
+}
+
+int pk_readback(pk_engine* e, void* dst, size_t bytes) {
+    if (!e || !dst) return PK_EINVAL;
+    if (e->state == POISONED) return PK_ESTATE;
+    const size_t need = static_cast<size_t>(e->nx) * e->ny * e->esize;
+    if (bytes < need) return PK_EINVAL;
+    const size_t hrow = static_cast<size_t>(e->nx) * e->esize;
+    const bool gone = e->mode == PK_PERSISTENT && __atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE);
+    if (e->mode == PK_PERSISTENT && e->state == RUNNING && !gone) {
+        if (e->ring.in_flight() != 0) return PK_EBUSY;
+        uint64_t seq = 0;
+        int rc = e->ring.publish(PK_TASK_READBACK, 0, &seq);
+        if (rc != PK_OK) return rc;
+        pkr::DoneInfo d{};
+        rc = e->ring.wait(seq, 120.0, &d, poll_exited, e);
+        if (rc == PK_ETIMEDOUT) e->state = POISONED;
+        if (rc != PK_OK) return rc;
+        if (d.status != PK_OK) return d.status;
+        std::memcpy(dst, e->h_staging, need);
+        return PK_OK;
+    }
+    int cur = e->cur;
+    if (e->mode == PK_PERSISTENT) {
+        // the kernel has left: wait for it to drain, then an ordinary copy is safe;
+        // the field is in the buffer the last completed task reported
+        if (hipEventSynchronize(e->ev_end) != hipSuccess) return PK_EDEVICE;
+        e->ring.harvest();
+        cur = e->ring.last_cur();
+    }
+    hipError_t he = hipMemcpy2DAsync(dst, hrow, e->d_u[cur], e->pitch_bytes, hrow, e->ny,
+                                      hipMemcpyDeviceToHost, e->stream);
+    if (he == hipSuccess) he = hipStreamSynchronize(e->stream);
+    return map_err(he);
+}
+
+int pk_run_launch_per_iter(pk_engine* e, int n, int sync_each, double* elapsed_us) {
+    if (!e || n < 0) return PK_EINVAL;
+    if (e->mode != PK_LAUNCH) return PK_ESTATE;
+    if (e->state != RUNNING) return PK_ESTATE;
+    if (hipStreamSynchronize(e->stream) != hipSuccess) return PK_EDEVICE;
+    hipError_t he = hipEventRecord(e->ev_start, e->stream);
+    const auto t0 = std::chrono::steady_clock::now();
+    for (int s = 0; s < n && he == hipSuccess; ++s) {
+        he = pkk_launch_sweep(e->dtype, e->has_b, e->ka, e->plan.threads, e->cur, e->stream);
+        e->cur ^= 1;
+        ++e->launches;
+        if (he == hipSuccess && sync_each) he = hipStreamSynchronize(e->stream);
+    }
+    if (he == hipSuccess) he = hipEventRecord(e->ev_end, e->stream);
+    if (he == hipSuccess) he = hipStreamSynchronize(e->stream);
+    const auto t1 = std::chrono::steady_clock::now();
+    if (he != hipSuccess) { e->state = POISONED; return PK_EDEVICE; }
+    e->sweeps_done += n;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, e->ev_start, e->ev_end) == hipSuccess) e->last_batch_ms = ms;
+    if (elapsed_us) *elapsed_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+    return PK_OK;
+}
+
+int pk_get_info(pk_engine* e, pk_info* info) {
+    if (!e || !info) return PK_EINVAL;
+    std::memset(info, 0, sizeof(*info));
+    info->nx = e->nx;
+    info->ny = e->ny;
+    info->dtype = e->dtype;
+    info->mode = e->mode;
+    info->layout = e->plan.layout;
+    info->pitch = e->pitch;
+    info->grid_blocks = e->plan.grid;
+    info->threads = e->plan.threads;
+    info->blocks_per_cu_max = e->plan.occ;
+    info->cus = e->cus;
+    info->halo_depth = e->plan.layout == PK_LAYOUT_RESIDENT ? e->plan.res_halo : 0;
+    info->band_rows = e->plan.layout == PK_LAYOUT_RESIDENT ? e->plan.res_band_rows : e->plan.band_rows;
+    info->strips = e->plan.strips;
+    info->lds_bytes = e->plan.lds_bytes;
+    info->kernel_launches = e->launches;
+    if (e->mode == PK_PERSISTENT) {
+        info->sweeps_done = e->ring.sweeps_seen();
+        info->tasks_done = static_cast<int64_t>(e->ring.done_seen());
+        if (__atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE) && hipEventQuery(e->ev_end) == hipSuccess) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, e->ev_start, e->ev_end) == hipSuccess) info->kernel_ms = ms;
+        }
+    } else {
+        info->sweeps_done = e->sweeps_done;
+        info->tasks_done = static_cast<int64_t>(e->lresults.size());
+        info->kernel_ms = e->last_batch_ms;
+    }
+    return PK_OK;
+}
+
+int pk_destroy(pk_engine* e) {
+    if (!e) return PK_OK;
+    if (e->mode == PK_PERSISTENT && e->launched) {
+        const bool exited = __atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE) != 0;
+        if (!exited) {
+            if (e->state == RUNNING) {
+                uint64_t seq = 0;
+                // make room, then ask the kernel to leave
+                int rc = e->ring.publish(PK_EXIT, 0, &seq);
+                const auto t0 = std::chrono::steady_clock::now();
+                while (rc == PK_EBUSY) {
+                    e->ring.harvest();
+                    rc = e->ring.publish(PK_EXIT, 0, &seq);
+                    if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(30)) break;
+                }
+                e->state = EXITED;
+            }
+            const auto t0 = std::chrono::steady_clock::now();
+            while (__atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE) == 0) {
+                if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(30)) {
+                    // the kernel may still run: leak its memory rather than free it
+                    return PK_ETIMEDOUT;
+                }
+            }
+        }
+        (void)hipEventSynchronize(e->ev_end);
+    } else if (e->mode == PK_LAUNCH) {
+        (void)hipStreamSynchronize(e->stream);
+    }
+    release(e);
+    return PK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,22 @@
+// Host-side launch wrappers exported by pk_kernels.hip to the runtime.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "pk_shared.h"
+
+// Kernel symbol of the persistent kernel for an element type / source / layout.
+const void* pkk_persistent_fn(int dtype, bool has_b, int layout);
+// Kernel symbol of the one-sweep kernel (for the occupancy query).
+const void* pkk_sweep_fn(int dtype, bool has_b);
+
+// One streaming sweep u[src] -> u[src ^ 1] with a.grid blocks of `threads`.
+hipError_t pkk_launch_sweep(int dtype, bool has_b, const pk_kargs& a, int threads, int src,
+                            hipStream_t s);
+// Residual of u[src]: per-block partials, then one block sums them in a fixed
+// order and stores sqrt(sum) at `out` (device-visible).
+hipError_t pkk_launch_residual(int dtype, bool has_b, const pk_kargs& a, int threads, int src,
+                               double* out, hipStream_t s);
+// b = (T)((h*h) * f) on a pitched ny x pitch array.
+hipError_t pkk_launch_scale_source(int dtype, const void* f, void* b, int nx, int ny, int pitch,
+                                   double hh, hipStream_t s);

@@ -1,0 +1,89 @@
+// Memory layouts shared by the host runtime and the device kernels.
+//
+// Host<->device mailbox (fine-grained, coherent pinned host memory, mapped on
+// the device). The host publishes tasks as sequence-numbered slots and then
+// moves `tail`; one device thread (block 0, lane 0) polls `tail`. The device
+// answers by filling `done[seq % PK_RING]` and then moving `done_seq`. Every
+// word that one side polls sits on its own 128-byte line, so the writer of one
+// flag never invalidates the line of another (the first page's flag-padding
+// point, "Reflections and next steps").
+#pragma once
+
+#include <stdint.h>
+
+#define PK_RING 64u
+#define PK_LINE 128
+
+// Internal task kinds (the public ones are in pk.h).
+#define PK_TASK_READBACK 100
+
+// Device fault codes (pk_dev_state::fault).
+#define PK_FAULT_BARRIER_TIMEOUT 1u
+#define PK_FAULT_IDLE_TIMEOUT 2u
+#define PK_FAULT_BAD_TASK 3u
+
+struct alignas(PK_LINE) pk_slot {
+    uint64_t seq;
+    int32_t kind;
+    int32_t n;
+};
+
+struct alignas(PK_LINE) pk_done_rec {
+    uint64_t seq;
+    int32_t kind;
+    int32_t status;
+    double residual;
+    int64_t sweeps_done;
+    uint64_t t_begin;  // device wall clock ticks
+    uint64_t t_end;
+    int64_t errors;
+    int32_t cur;  // buffer index that holds the whole field after this task
+};
+
+struct pk_mailbox {
+    alignas(PK_LINE) uint64_t tail;      // host writes: last published seq
+    alignas(PK_LINE) uint64_t done_seq;  // device writes: last completed seq
+    alignas(PK_LINE) uint32_t exited;    // device writes 1 when the kernel leaves
+    alignas(PK_LINE) uint32_t fault;     // device writes a PK_FAULT_* code
+    pk_slot slot[PK_RING];
+    pk_done_rec done[PK_RING];
+};
+
+// Device-memory state of one engine; zeroed once before the kernel starts.
+// The barrier's two words live on separate lines: arrivals hammer `count`
+// while waiters poll `gen`.
+struct pk_dev_state {
+    alignas(PK_LINE) uint32_t bar_count;   // arrivals, monotonically increasing
+    alignas(PK_LINE) uint32_t bar_gen;     // completed barrier generations
+    alignas(PK_LINE) uint64_t task_seq;    // task broadcast (written by the leader)
+    int32_t task_kind;
+    int32_t task_n;
+    alignas(PK_LINE) uint32_t fault;       // device-side fault, read by every block
+    alignas(PK_LINE) uint64_t stamp_errors;
+};
+
+// Kernel arguments (passed by value).
+struct pk_kargs {
+    void* u[2];            // the two field buffers (ny rows x pitch elements)
+    const void* b;         // scaled source h*h*f (pitched), or null for Laplace
+    int nx, ny, pitch;     // pitch in elements
+    int cur0;              // buffer index holding the field at launch
+    // stream geometry: unit = (band, strip); strip = 64 lanes x vector width
+    int strips, bands, band_rows;
+    // resident geometry (one band per block)
+    int res_band_rows;     // rows per block band (last band may be shorter)
+    int res_halo;          // sweeps per halo exchange
+    int res_ext_rows;      // LDS rows per buffer
+    int lds_pitch;         // LDS row stride in elements
+    int layout;            // PK_LAYOUT_STREAM or PK_LAYOUT_RESIDENT
+    int grid;              // blocks in the grid
+    int xcd_remap;         // 1: map consecutive logical blocks onto one XCD
+    uint32_t flags;
+    uint64_t idle_ticks;   // wall-clock ticks without a task before leaving
+    uint64_t spin_ticks;   // wall-clock ticks a barrier may wait before faulting
+    pk_dev_state* st;
+    pk_mailbox* mail;      // device-visible address of the host mailbox
+    double* partials;      // one double per block
+    void* staging;         // readback target (pinned host, device-visible)
+    uint32_t* stamp;       // 2 x grid x 64 words for the visibility check
+};

@@ -1,0 +1,231 @@
+"""ctypes binding of the engine's C ABI (``include/pk.h``), same names.
+
+Argument marshalling only: every step of the path runs in the HIP library
+``_libpk.so``. There is no CPU fallback; loading raises if the library is
+missing. Arrays are numpy, row-major ``ny x nx``, float32 or float64.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_libpk.so")
+
+# status codes
+PK_OK, PK_EINVAL, PK_ENOMEM, PK_ELAUNCH, PK_EDEVICE, PK_EBUSY, PK_ESTATE, PK_ETIMEDOUT = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+PK_F32, PK_F64 = 0, 1
+PK_PERSISTENT, PK_LAUNCH = 0, 1
+PK_LAYOUT_AUTO, PK_LAYOUT_STREAM, PK_LAYOUT_RESIDENT = 0, 1, 2
+PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP = 1, 2, 3, 4, 5
+PK_DBG_BROKEN_BARRIER = 0x1
+
+EXPORTED = ["pk_opts_default", "pk_create", "pk_submit", "pk_wait", "pk_readback",
+            "pk_run_launch_per_iter", "pk_get_info", "pk_destroy", "pk_strerror"]
+
+
+class pk_opts(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int), ("h", ctypes.c_double), ("mode", ctypes.c_int),
+                ("layout", ctypes.c_int), ("threads", ctypes.c_int),
+                ("max_blocks", ctypes.c_int), ("halo_depth", ctypes.c_int),
+                ("flags", ctypes.c_uint), ("stream", ctypes.c_void_p),
+                ("idle_timeout_s", ctypes.c_double), ("reserved", ctypes.c_int * 8)]
+
+
+class pk_task(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("n", ctypes.c_int)]
+
+
+class pk_result(ctypes.Structure):
+    _fields_ = [("residual", ctypes.c_double), ("sweeps_done", ctypes.c_int64),
+                ("device_us", ctypes.c_double), ("errors", ctypes.c_int64),
+                ("kind", ctypes.c_int), ("status", ctypes.c_int)]
+
+
+class pk_info(ctypes.Structure):
+    _fields_ = [("nx", ctypes.c_int), ("ny", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("mode", ctypes.c_int), ("layout", ctypes.c_int), ("pitch", ctypes.c_int),
+                ("grid_blocks", ctypes.c_int), ("threads", ctypes.c_int),
+                ("blocks_per_cu_max", ctypes.c_int), ("cus", ctypes.c_int),
+                ("halo_depth", ctypes.c_int), ("band_rows", ctypes.c_int),
+                ("strips", ctypes.c_int), ("lds_bytes", ctypes.c_size_t),
+                ("kernel_ms", ctypes.c_double), ("sweeps_done", ctypes.c_int64),
+                ("tasks_done", ctypes.c_int64), ("kernel_launches", ctypes.c_int64)]
+
+
+class PkError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {pk_strerror(status)} ({status})")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load ``_libpk.so`` (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"engine library not built: {path} (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    vp, ip = ctypes.c_void_p, ctypes.c_int
+    lib.pk_opts_default.restype = None
+    lib.pk_opts_default.argtypes = [ctypes.POINTER(pk_opts)]
+    lib.pk_create.restype = ip
+    lib.pk_create.argtypes = [ip, ip, vp, vp, ctypes.POINTER(pk_opts), ctypes.POINTER(vp)]
+    lib.pk_submit.restype = ip
+    lib.pk_submit.argtypes = [vp, pk_task, ctypes.POINTER(ctypes.c_uint64)]
+    lib.pk_wait.restype = ip
+    lib.pk_wait.argtypes = [vp, ctypes.c_uint64, ctypes.c_double, ctypes.POINTER(pk_result)]
+    lib.pk_readback.restype = ip
+    lib.pk_readback.argtypes = [vp, vp, ctypes.c_size_t]
+    lib.pk_run_launch_per_iter.restype = ip
+    lib.pk_run_launch_per_iter.argtypes = [vp, ip, ip, ctypes.POINTER(ctypes.c_double)]
+    lib.pk_get_info.restype = ip
+    lib.pk_get_info.argtypes = [vp, ctypes.POINTER(pk_info)]
+    lib.pk_destroy.restype = ip
+    lib.pk_destroy.argtypes = [vp]
+    lib.pk_strerror.restype = ctypes.c_char_p
+    lib.pk_strerror.argtypes = [ip]
+    _lib = lib
+    return lib
+
+
+def pk_strerror(status: int) -> str:
+    try:
+        return load().pk_strerror(status).decode()
+    except ImportError:
+        return f"status {status}"
+
+
+def _check(rc: int, where: str):
+    if rc != PK_OK:
+        raise PkError(rc, where)
+
+
+def pk_opts_default(**kw) -> pk_opts:
+    o = pk_opts()
+    load().pk_opts_default(ctypes.byref(o))
+    for k, v in kw.items():
+        if k == "stream" and v is not None and not isinstance(v, int):
+            v = int(v)  # e.g. torch.cuda.Stream().cuda_stream
+        setattr(o, k, v)
+    return o
+
+
+def pk_create(bc: np.ndarray, src: np.ndarray | None = None, opts: pk_opts | None = None,
+              **kw) -> int:
+    """Create an engine; returns the opaque handle. ``kw`` fills ``pk_opts``."""
+    if bc.ndim != 2 or bc.dtype not in (np.float32, np.float64):
+        raise ValueError("bc must be a 2-D float32/float64 array")
+    bc = np.ascontiguousarray(bc)
+    if opts is None:
+        kw.setdefault("dtype", PK_F64 if bc.dtype == np.float64 else PK_F32)
+        opts = pk_opts_default(**kw)
+    if (opts.dtype == PK_F64) != (bc.dtype == np.float64):
+        raise ValueError("bc dtype does not match opts.dtype")
+    if src is not None:
+        src = np.ascontiguousarray(src, dtype=bc.dtype)
+        if src.shape != bc.shape:
+            raise ValueError("src must have the shape of bc")
+    ny, nx = bc.shape
+    h = ctypes.c_void_p()
+    rc = load().pk_create(nx, ny, bc.ctypes.data, None if src is None else src.ctypes.data,
+                          ctypes.byref(opts), ctypes.byref(h))
+    _check(rc, "pk_create")
+    return h.value
+
+
+def pk_submit(eng: int, kind: int, n: int = 0) -> int:
+    t = ctypes.c_uint64()
+    _check(load().pk_submit(eng, pk_task(kind, n), ctypes.byref(t)), "pk_submit")
+    return t.value
+
+
+def pk_submit_status(eng: int, kind: int, n: int = 0):
+    """Like pk_submit but returns (status, ticket) instead of raising."""
+    t = ctypes.c_uint64()
+    rc = load().pk_submit(eng, pk_task(kind, n), ctypes.byref(t))
+    return rc, t.value
+
+
+def pk_wait(eng: int, ticket: int, timeout_s: float = 60.0) -> pk_result:
+    r = pk_result()
+    _check(load().pk_wait(eng, ticket, timeout_s, ctypes.byref(r)), "pk_wait")
+    return r
+
+
+def pk_readback(eng: int, out: np.ndarray) -> np.ndarray:
+    if not out.flags.c_contiguous:
+        raise ValueError("out must be C-contiguous")
+    _check(load().pk_readback(eng, out.ctypes.data, out.nbytes), "pk_readback")
+    return out
+
+
+def pk_run_launch_per_iter(eng: int, n: int, sync_each: bool = False) -> float:
+    us = ctypes.c_double()
+    _check(load().pk_run_launch_per_iter(eng, n, 1 if sync_each else 0, ctypes.byref(us)),
+           "pk_run_launch_per_iter")
+    return us.value
+
+
+def pk_get_info(eng: int) -> pk_info:
+    i = pk_info()
+    _check(load().pk_get_info(eng, ctypes.byref(i)), "pk_get_info")
+    return i
+
+
+def pk_destroy(eng: int) -> None:
+    if eng:
+        _check(load().pk_destroy(eng), "pk_destroy")
+
+
+class Engine:
+    """Owning wrapper: ``with Engine(bc, f, mode=...) as e: e.sweep(100); ...``."""
+
+    def __init__(self, bc: np.ndarray, src: np.ndarray | None = None, **opts):
+        self.shape = bc.shape
+        self.dtype = np.dtype(bc.dtype)
+        self.h = pk_create(bc, src, **opts)
+
+    def submit(self, kind: int, n: int = 0) -> int:
+        return pk_submit(self.h, kind, n)
+
+    def wait(self, ticket: int, timeout_s: float = 60.0) -> pk_result:
+        return pk_wait(self.h, ticket, timeout_s)
+
+    def run(self, kind: int, n: int = 0, timeout_s: float = 60.0) -> pk_result:
+        return self.wait(self.submit(kind, n), timeout_s)
+
+    def sweep(self, n: int) -> pk_result:
+        return self.run(PK_SWEEP, n)
+
+    def residual(self) -> float:
+        return self.run(PK_RESIDUAL).residual
+
+    def readback(self) -> np.ndarray:
+        out = np.empty(self.shape, dtype=self.dtype)
+        return pk_readback(self.h, out)
+
+    def info(self) -> pk_info:
+        return pk_get_info(self.h)
+
+    def launch_per_iter(self, n: int, sync_each: bool = False) -> float:
+        return pk_run_launch_per_iter(self.h, n, sync_each)
+
+    def close(self):
+        if self.h:
+            h, self.h = self.h, None
+            pk_destroy(h)
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

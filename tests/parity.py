@@ -1,0 +1,91 @@
+"""Shared helpers for the GPU parity tests: run a workload's task script on the
+engine and on the CPU oracle, and compare them against the gates.
+
+Gates (field): max |engine - oracle| over every node <= 1e-5 x (max - min of the
+oracle field) in fp32, <= 1e-12 x range in fp64. Residual: fp32
+|dR| <= 1e-5 R_0 + 1e-9 R_k, fp64 |dR| <= 1e-9 R_k (summation order differs).
+"""
+
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+import oracle
+from iterative_stencil_pde_amd import pk
+
+FIELD_TOL = {np.float32: 1e-5, np.float64: 1e-12}
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def field_gate(got: np.ndarray, ref: np.ndarray):
+    """Returns (ok, max_abs_err, tolerance, cells_not_bitwise_equal)."""
+    assert got.shape == ref.shape and got.dtype == ref.dtype
+    rng = float(ref.max()) - float(ref.min())
+    tol = FIELD_TOL[ref.dtype.type] * (rng if rng > 0 else 1.0)
+    err = float(np.max(np.abs(got.astype(np.float64) - ref.astype(np.float64))))
+    ui = np.uint32 if ref.dtype == np.float32 else np.uint64
+    nonbit = int(np.count_nonzero(got.view(ui) != ref.view(ui)))
+    return err <= tol, err, tol, nonbit
+
+
+def residual_gate(got, ref, dtype):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if dtype == np.float32:
+        tol = 1e-5 * ref[0] + 1e-9 * np.abs(ref)
+    else:
+        tol = 1e-9 * np.abs(ref)
+    err = np.abs(got - ref)
+    return bool(np.all(err <= tol)), float(np.max(err / np.maximum(tol, 1e-300)))
+
+
+def run_engine_script(w, timeout_s: float = 120.0, **opts):
+    """Run ``w.script`` on a fresh engine. Returns dict with residuals, readbacks
+    (fields at each readback step), info and per-task results."""
+    out = {"residuals": [], "readbacks": [], "results": []}
+    say(f"[engine] {w.name} {w.nx}x{w.ny} opts={opts}")
+    t0 = time.time()
+    with pk.Engine(w.u0, w.f, h=w.h, **opts) as e:
+        out["info"] = e.info()
+        for step in w.script:
+            if step[0] == "sweep":
+                r = e.run(pk.PK_SWEEP, step[1], timeout_s)
+                out["results"].append(r)
+            elif step[0] == "residual":
+                r = e.run(pk.PK_RESIDUAL, 0, timeout_s)
+                out["residuals"].append(r.residual)
+                out["results"].append(r)
+            elif step[0] == "readback":
+                out["readbacks"].append(e.readback())
+        out["final"] = e.readback()
+        out["info_end"] = e.info()
+    out["seconds"] = time.time() - t0
+    return out
+
+
+def run_oracle_script(w):
+    """The oracle's answer for ``w.script``: residuals and fields at each readback."""
+    say(f"[oracle] {w.name}")
+    res_ck = w.residual_checkpoints
+    rb_ck = w.readback_checkpoints
+    marks = sorted(set(rb_ck) | {w.sweeps})
+    fields, residuals = [], []
+    u, k, first = w.u0, 0, True
+    for mark in marks:
+        # residual checkpoints in (k, mark], plus those at 0 in the first segment
+        ck = [c - k for c in res_ck if (k < c <= mark) or (first and c == 0)]
+        first = False
+        u, r = oracle.jacobi(u, mark - k, f=w.f, h=w.h, checkpoints=ck)
+        residuals.extend(r.tolist())
+        fields.extend(u.copy() for c in rb_ck if c == mark)
+        k = mark
+    assert len(residuals) == len(res_ck)
+    return {"residuals": residuals, "readbacks": fields, "final": u}

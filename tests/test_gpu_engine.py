@@ -1,0 +1,163 @@
+"""GPU tests of the engine's protocol and grid barrier (through the C ABI)."""
+
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from iterative_stencil_pde_amd import inputs, pk
+from parity import field_gate, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_stamp_check_correct_barrier():
+    """After each barrier every block sees the stamps all blocks wrote before it
+    ("Grid-Wide Barriers", "The barrier is a counter and a generation"; the
+    "@persistent" page, "grid_barrier")."""
+    w = inputs.laplace_top_edge(4096, 0)
+    with pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM) as e:
+        info = e.info()
+        say(f"  grid={info.grid_blocks} threads={info.threads}")
+        r = e.run(pk.PK_STAMP, 20000, 120)
+        say(f"  stamp rounds=20000 errors={r.errors} device_us={r.device_us:.0f}")
+        assert r.errors == 0 and r.status == 0
+        # the field is untouched by barrier-only tasks
+        e.run(pk.PK_BARRIER, 1000)
+        assert np.array_equal(e.readback(), w.u0)
+
+
+@pytest.mark.parametrize("blocks", [2, 8, 64, 256])
+def test_barrier_only_tasks(blocks):
+    w = inputs.laplace_random_interior(256, 0)
+    with pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM, max_blocks=blocks, threads=256) as e:
+        r = e.run(pk.PK_BARRIER, 5000)
+        r2 = e.run(pk.PK_STAMP, 2000)
+        say(f"  blocks={e.info().grid_blocks}: barrier {r.device_us / 5000:.3f} us, stamp errors {r2.errors}")
+        assert r2.errors == 0
+
+
+def test_broken_barrier_negative_control():
+    """With the barrier's release/acquire removed (relaxed atomics, no fences:
+    every wait still ends and every access is the same as in the correct run),
+    blocks can read halo rows that other XCDs' blocks have not yet made visible.
+    The field gate is expected to catch that ("Grid-Wide Barriers", "Failure
+    modes that only appear at this scale": a barrier of relaxed atomics orders
+    progress, not memory traffic)."""
+    w = inputs.laplace_random_interior(1024, 0)
+    sweeps = 400
+    ref, _ = oracle.jacobi(w.u0, sweeps)
+    results = {}
+    for label, flags in (("correct", 0), ("broken", pk.PK_DBG_BROKEN_BARRIER)):
+        with pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM, flags=flags) as e:
+            e.run(pk.PK_SWEEP, sweeps)
+            got = e.readback()
+            stamp = e.run(pk.PK_STAMP, 5000).errors
+        ok, err, tol, nonbit = field_gate(got, ref)
+        say(f"  {label}: max_abs={err:.3e} tol={tol:.3e} non_bitwise={nonbit} stamp_errors={stamp}")
+        results[label] = (ok, stamp)
+    assert results["correct"] == (True, 0)
+    assert (not results["broken"][0]) or results["broken"][1] > 0, \
+        "the fence-less barrier produced no visible race on this run"
+
+
+def test_protocol_errors_and_ring():
+    w = inputs.laplace_top_edge(128, 0)
+    per_task = 1000
+    with pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM) as e:
+        h = e.h
+        # persistent engines refuse the launch-per-sweep baseline
+        with pytest.raises(pk.PkError) as ex:
+            pk.pk_run_launch_per_iter(h, 1)
+        assert ex.value.status == pk.PK_ESTATE
+        # unknown task kinds and negative counts
+        assert pk.pk_submit_status(h, 99, 0)[0] == pk.PK_EINVAL
+        assert pk.pk_submit_status(h, pk.PK_SWEEP, -1)[0] == pk.PK_EINVAL
+        # fill the ring: 64 slots, the 65th is refused until the oldest completes
+        tickets = []
+        status = pk.PK_OK
+        for _ in range(64 + 8):
+            status, t = pk.pk_submit_status(h, pk.PK_SWEEP, per_task)
+            if status != pk.PK_OK:
+                break
+            tickets.append(t)
+        say(f"  accepted {len(tickets)} tasks before status {status}")
+        assert status == pk.PK_EBUSY and len(tickets) >= 64
+        # readback refuses while tasks are in flight
+        out = np.empty_like(w.u0)
+        with pytest.raises(pk.PkError) as ex:
+            pk.pk_readback(h, out)
+        assert ex.value.status == pk.PK_EBUSY
+        res = [e.wait(t, 120) for t in tickets]
+        assert [r.sweeps_done for r in res] == [per_task * (k + 1) for k in range(len(tickets))]
+        # waiting on a ticket never issued
+        with pytest.raises(pk.PkError) as ex:
+            e.wait(10 ** 6)
+        assert ex.value.status == pk.PK_EINVAL
+        # readback buffer too small
+        with pytest.raises(pk.PkError):
+            pk.pk_readback(h, np.empty(10, np.float32))
+        t = e.submit(pk.PK_EXIT)
+        assert e.wait(t).kind == pk.PK_EXIT
+        assert pk.pk_submit_status(h, pk.PK_SWEEP, 1)[0] == pk.PK_ESTATE
+        # still readable after EXIT (the kernel has left: an ordinary copy)
+        got = e.readback()
+        ref, _ = oracle.jacobi(w.u0, per_task * len(tickets))
+        assert field_gate(got, ref)[0]
+        info = e.info()
+        assert info.kernel_ms > 0 and info.kernel_launches == 1
+
+
+def test_idle_timeout_ends_the_kernel():
+    """The kernel leaves by itself when no task comes; the host sees a device
+    error, not a hang (forced from the host by simply not submitting)."""
+    w = inputs.laplace_harmonic(64, 0)
+    with pk.Engine(w.u0, None, idle_timeout_s=0.5) as e:
+        e.sweep(10)
+        time.sleep(1.5)
+        status, _ = pk.pk_submit_status(e.h, pk.PK_SWEEP, 1)
+        assert status == pk.PK_ESTATE
+        # the field is still there and holds the 10 sweeps
+        got = e.readback()
+        ref, _ = oracle.jacobi(w.u0, 10)
+        assert np.array_equal(got, ref)
+
+
+def test_grid_that_cannot_be_resident_is_refused():
+    """A cooperative grid larger than the device holds is refused, not run
+    ("Grid-Wide Barriers", "The residency requirement")."""
+    w = inputs.laplace_harmonic(64, 0)
+    with pytest.raises(pk.PkError) as ex:
+        pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM, max_blocks=100000, threads=1024)
+    assert ex.value.status == pk.PK_ELAUNCH
+    # and the device is still usable
+    with pk.Engine(w.u0, None) as e:
+        e.sweep(3)
+
+
+def test_launch_mode_rejects_persistent_only_tasks():
+    w = inputs.laplace_harmonic(64, 0)
+    with pk.Engine(w.u0, None, mode=pk.PK_LAUNCH) as e:
+        assert pk.pk_submit_status(e.h, pk.PK_BARRIER, 1)[0] == pk.PK_EINVAL
+        assert pk.pk_submit_status(e.h, pk.PK_STAMP, 1)[0] == pk.PK_EINVAL
+        us_q = e.launch_per_iter(200, False)
+        us_s = e.launch_per_iter(50, True)
+        say(f"  launch queued {us_q / 200:.2f} us/sweep, synced {us_s / 50:.2f} us/sweep")
+        got = e.readback()
+        ref, _ = oracle.jacobi(w.u0, 250)
+        assert np.array_equal(got, ref)
+
+
+def test_engine_on_a_torch_stream():
+    """PyTorch provides the stream (plumbing only); the engine's kernels run on it."""
+    torch = pytest.importorskip("torch")
+    s = torch.cuda.Stream()
+    w = inputs.poisson_uniform(256, 0)
+    with pk.Engine(w.u0, w.f, h=w.h, mode=pk.PK_LAUNCH, stream=s.cuda_stream) as e:
+        e.sweep(100)
+        r = e.residual()
+        got = e.readback()
+    ref, res = oracle.jacobi(w.u0, 100, f=w.f, h=w.h, checkpoints=[100])
+    assert np.array_equal(got, ref)
+    assert abs(r - res[0]) <= 1e-9 * res[0]

@@ -1,0 +1,221 @@
+"""GPU parity: the HIP engine against the CPU oracle on the same seeded inputs.
+
+Every test goes through the C ABI (``include/pk.h``) via the ctypes binding.
+Whole-array comparisons at sizes the oracle finishes in seconds; at the two
+largest workloads, stored oracle values (tests/golden, written by
+make_golden.py) plus properties that hold at any size.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from iterative_stencil_pde_amd import inputs, pk
+from parity import field_gate, residual_gate, run_engine_script, run_oracle_script, say
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+MODES = {
+    "persistent-auto": dict(mode=pk.PK_PERSISTENT),
+    "persistent-stream": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM),
+    "launch": dict(mode=pk.PK_LAUNCH),
+}
+
+
+def check_against_oracle(w, got, ref, label):
+    for k, (g, r) in enumerate(zip(got["readbacks"], ref["readbacks"])):
+        ok, err, tol, nonbit = field_gate(g, r)
+        say(f"  {label} readback {k}: max_abs={err:.3e} tol={tol:.3e} non_bitwise={nonbit}")
+        assert ok, (label, k, err, tol)
+    ok, err, tol, nonbit = field_gate(got["final"], ref["final"])
+    say(f"  {label} final: max_abs={err:.3e} tol={tol:.3e} non_bitwise={nonbit}")
+    assert ok, (label, err, tol)
+    if ref["residuals"]:
+        ok, worst = residual_gate(got["residuals"], ref["residuals"], w.dtype)
+        say(f"  {label} residuals: n={len(ref['residuals'])} worst/tol={worst:.3e}")
+        assert ok, (label, worst)
+
+
+# ---- the three workloads the oracle finishes in seconds, at full size --------
+@pytest.fixture(scope="module")
+def oracle_cache():
+    return {}
+
+
+def _oracle_for(cache, name):
+    if name not in cache:
+        w = inputs.make(name)
+        cache[name] = (w, run_oracle_script(w))
+    return cache[name]
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("name", ["laplace64", "poisson256", "laplace1024"])
+def test_workload_full_size(name, mode, oracle_cache):
+    w, ref = _oracle_for(oracle_cache, name)
+    got = run_engine_script(w, **MODES[mode])
+    say(f"  layout={got['info'].layout} grid={got['info'].grid_blocks} "
+        f"threads={got['info'].threads} halo={got['info'].halo_depth} ({got['seconds']:.1f}s)")
+    check_against_oracle(w, got, ref, f"{name}/{mode}")
+    if name == "laplace64":
+        # the fixed point is x^2 - y^2 exactly; 1000 sweeps are not yet converged
+        assert np.array_equal(got["final"], -got["final"].T)
+    if name == "laplace1024":
+        # maximum principle and monotone residual at every checkpoint
+        prev_hi, prev_lo = 1.0, 0.0
+        for f in got["readbacks"]:
+            assert f.max() <= prev_hi and f.min() >= prev_lo and f.min() >= 0 and f.max() <= 1
+            prev_hi, prev_lo = f.max(), f.min()
+        r = np.asarray(got["residuals"])
+        assert np.all(r[1:] <= r[:-1] * (1 + 1e-6))
+
+
+# ---- ragged shapes, both element types, Laplace and Poisson ------------------
+SHAPES = [(3, 3), (3, 9), (9, 3), (5, 300), (300, 5), (67, 131), (130, 257), (257, 255),
+          (33, 1030), (17, 4100)]
+
+
+def _random_case(ny, nx, dtype, poisson, seed):
+    u = inputs.uniform(seed, 0, ny * nx, -1, 1).reshape(ny, nx).astype(dtype)
+    f = inputs.uniform(seed, 1, ny * nx, -20, 20).reshape(ny, nx).astype(dtype) if poisson else None
+    return u, f
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("poisson", [False, True], ids=["laplace", "poisson"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_ragged_shapes(shape, dtype, poisson, mode):
+    ny, nx = shape
+    u, f = _random_case(ny, nx, dtype, poisson, seed=ny * 1000 + nx)
+    h = 0.013
+    tasks = [("residual",), ("sweep", 7), ("residual",), ("sweep", 0), ("sweep", 30), ("residual",)]
+    w = inputs.Workload(f"rand{ny}x{nx}", nx, ny, dtype, h, u, f, tasks + [("readback",)], "")
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, **MODES[mode])
+    check_against_oracle(w, got, ref, f"{ny}x{nx}/{np.dtype(dtype).name}/{mode}")
+    assert got["results"][-1].sweeps_done == 37
+
+
+# ---- the LDS-resident layout across block counts and halo depths ----------
+@pytest.mark.parametrize("blocks,halo", [(2, 1), (3, 5), (5, 8), (8, 3), (16, 4), (31, 2), (64, 3)])
+def test_resident_layout_blocks_and_halos(blocks, halo):
+    w = inputs.poisson_uniform(256, 0, 100)
+    # uneven task lengths so periods end part-way
+    w.script = [("residual",), ("sweep", 1), ("sweep", 7), ("residual",), ("sweep", 13),
+                ("sweep", 29), ("residual",), ("readback",)]
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_RESIDENT,
+                            max_blocks=blocks, halo_depth=halo)
+    info = got["info"]
+    say(f"  grid={info.grid_blocks} band={info.band_rows} halo={info.halo_depth} lds={info.lds_bytes}")
+    assert info.layout == pk.PK_LAYOUT_RESIDENT
+    check_against_oracle(w, got, ref, f"resident/{blocks}/{halo}")
+
+
+def test_resident_fp64_wide():
+    u, f = _random_case(130, 1000, np.float64, True, seed=77)
+    w = inputs.Workload("wide64", 1000, 130, np.float64, 0.01, u, f,
+                        [("sweep", 11), ("residual",), ("sweep", 20), ("readback",)], "")
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_RESIDENT, max_blocks=20,
+                            halo_depth=2)
+    check_against_oracle(w, got, ref, "resident/f64")
+
+
+# ---- the two largest workloads ---------------------------------------------
+def _golden(name):
+    path = os.path.join(GOLDEN, f"{name}.json")
+    if not os.path.exists(path):
+        pytest.skip(f"no stored oracle values for {name}")
+    return json.load(open(path))
+
+
+def _check_golden(w, field, residuals, g, tol_rel):
+    assert g["input_sha256"] == w.digest(), "inputs differ from those the stored values came from"
+    ref_min, ref_max = float.fromhex(g["min"]), float.fromhex(g["max"])
+    tol = tol_rel * (ref_max - ref_min)
+    errs = [abs(float(field[i, j]) - float.fromhex(v)) for i, j, v in g["samples"]]
+    if "column" in g:
+        col = np.array([float.fromhex(v) for v in g["column"]])
+        errs.append(float(np.max(np.abs(field[:, g["column_index"]] - col))))
+    if "row" in g:
+        row = np.array([float.fromhex(v) for v in g["row"]])
+        errs.append(float(np.max(np.abs(field[g["row_index"], :] - row))))
+    say(f"  sampled max_abs={max(errs):.3e} tol={tol:.3e}")
+    assert max(errs) <= tol
+    assert abs(float(field.min()) - ref_min) <= tol and abs(float(field.max()) - ref_max) <= tol
+    fs = math.fsum(field.astype(np.float64).ravel().tolist())
+    say(f"  fsum engine={fs!r} oracle={float.fromhex(g['fsum'])!r}")
+    assert abs(fs - float.fromhex(g["fsum"])) <= tol * field.size
+    if g["residuals"]:
+        ok, worst = residual_gate(residuals, [float.fromhex(v) for v in g["residuals"]], w.dtype)
+        say(f"  residuals worst/tol={worst:.3e}")
+        assert ok
+
+
+@pytest.mark.parametrize("mode", ["persistent-auto", "launch"])
+def test_laplace4096_full(mode):
+    w = inputs.make("laplace4096")
+    g = _golden("laplace4096")
+    got = run_engine_script(w, **MODES[mode])
+    f = got["final"]
+    say(f"  grid={got['info'].grid_blocks} layout={got['info'].layout} ({got['seconds']:.1f}s)")
+    _check_golden(w, f, got["residuals"], g, 1e-5)
+    # finite propagation: more than 2000 rows below the top row nothing has moved
+    assert np.all(f[: w.ny - 1 - w.sweeps, :] == 0)
+    # bitwise mirror symmetry in x
+    assert np.array_equal(f, f[:, ::-1])
+
+
+@pytest.mark.parametrize("mode", ["persistent-auto", "launch"])
+def test_poisson8192_full(mode):
+    w = inputs.make("poisson8192")
+    g = _golden("poisson8192")
+    got = run_engine_script(w, timeout_s=300, **MODES[mode])
+    say(f"  grid={got['info'].grid_blocks} layout={got['info'].layout} ({got['seconds']:.1f}s)")
+    _check_golden(w, got["final"], got["residuals"], g, 1e-12)
+
+
+@pytest.mark.parametrize("name,sweeps", [("laplace4096", 40), ("poisson8192", 6)])
+def test_full_size_short_run_whole_array(name, sweeps):
+    """The full-size grids, few enough sweeps that the oracle redoes them here."""
+    w = inputs.make(name)
+    w.script = [("residual",), ("sweep", sweeps // 2), ("residual",), ("sweep", sweeps - sweeps // 2),
+                ("residual",), ("readback",)]
+    ref = run_oracle_script(w)
+    for mode in ("persistent-auto", "launch"):
+        got = run_engine_script(w, **MODES[mode])
+        check_against_oracle(w, got, ref, f"{name}/{mode}")
+
+
+def test_eigenmode_decay_full_size_fp64():
+    """Closed form at any size: u0 = sin(3 pi x) sin(2 pi y) decays by mu per sweep."""
+    n, p, q, K = 8192, 3, 2, 20
+    s_p = inputs.sinpi_samples(n, 1 / (n - 1), p)
+    s_q = inputs.sinpi_samples(n, 1 / (n - 1), q)
+    u0 = s_q[:, None] * s_p[None, :]
+    u0[0, :] = u0[-1, :] = 0
+    u0[:, 0] = u0[:, -1] = 0
+    mu = (np.cos(p * np.pi / (n - 1)) + np.cos(q * np.pi / (n - 1))) / 2
+    with pk.Engine(u0, None) as e:
+        e.sweep(K)
+        got = e.readback()
+    err = float(np.max(np.abs(got - mu ** K * u0)))
+    say(f"  eigenmode 8192^2 fp64: max_abs={err:.3e}")
+    assert err <= 1e-13
+
+
+def test_persistent_and_launch_residuals_bitwise_equal():
+    w = inputs.poisson_uniform(256, 300, 50)
+    w.script = [s for s in w.script if s[0] != "readback"]
+    a = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM)
+    b = run_engine_script(w, mode=pk.PK_LAUNCH)
+    assert a["residuals"] == b["residuals"]
+    assert np.array_equal(a["final"], b["final"])
