@@ -114,6 +114,14 @@ def main():
     ap.add_argument("--launch-steps", type=int, default=0,
                     help="steps for the per-launch comparison (default: same as --steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch-only", action="store_true",
+                    help="only the per-launch baseline (for counter collection)")
+    ap.add_argument("--persistent-only", action="store_true")
+    ap.add_argument("--idle-timeout", type=float, default=0.0,
+                    help="persistent kernel idle timeout in seconds (0 = engine default)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a torch device-to-device copy of MIB MiB (a plain copy "
+                         "kernel of known size, to scale HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -121,13 +129,31 @@ def main():
                           "(the multi-GPU row-band design is described, not built)"}))
         sys.exit(2)
 
+    if args.calibrate_copy:
+        import torch  # before the engine library: one HIP runtime in the process
+        n = args.calibrate_copy * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+        torch.cuda.empty_cache()
+
     w = inputs.make(args.workload)
     layout = {"auto": pk.PK_LAYOUT_AUTO, "stream": pk.PK_LAYOUT_STREAM,
               "resident": pk.PK_LAYOUT_RESIDENT}[args.layout]
     opts = dict(layout=layout, threads=args.threads, max_blocks=args.max_blocks,
-                halo_depth=args.halo)
+                halo_depth=args.halo, idle_timeout_s=args.idle_timeout)
     step_bytes, sweep_bytes = algorithmic_bytes(w)
     cells_per_step = w.interior_cells * w.sweeps
+
+    if args.launch_only:
+        ldt, linfo, _ = measure(w, args.steps, args.warmup, mode=pk.PK_LAUNCH, threads=args.threads,
+                                max_blocks=args.max_blocks)
+        print(json.dumps({"workload": w.name, "mode": "launch", "steps": args.steps,
+                          "us_per_iteration": round(ldt / (w.sweeps * args.steps) * 1e6, 4),
+                          "grid_blocks": linfo.grid_blocks, "threads": linfo.threads}), flush=True)
+        return
 
     # persistent engine
     dt, info, info_end = measure(w, args.steps, args.warmup, mode=pk.PK_PERSISTENT, **opts)
@@ -139,9 +165,12 @@ def main():
 
     # per-launch baseline, same block count as the persistent grid
     lsteps = args.launch_steps or args.steps
-    ldt, linfo, _ = measure(w, lsteps, 1, mode=pk.PK_LAUNCH, threads=info.threads,
-                            max_blocks=info.grid_blocks)
-    lvalue = cells_per_step * lsteps / ldt / 1e9
+    if args.persistent_only:
+        ldt, linfo, lvalue = float("nan"), info, float("nan")
+    else:
+        ldt, linfo, _ = measure(w, lsteps, 1, mode=pk.PK_LAUNCH, threads=info.threads,
+                                max_blocks=info.grid_blocks)
+        lvalue = cells_per_step * lsteps / ldt / 1e9
 
     rec = {
         "metric": METRIC,
@@ -169,7 +198,7 @@ def main():
             "halo_depth": info.halo_depth,
             "band_rows": info.band_rows,
         },
-        "per_launch": {
+        "per_launch": None if args.persistent_only else {
             "value": round(lvalue, 4),
             "us_per_iteration": round(ldt / (w.sweeps * lsteps) * 1e6, 4),
             "steps": lsteps,

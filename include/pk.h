@@ -93,6 +93,17 @@ extern "C" {
  * field is expected to diverge from the oracle. A negative control.          */
 #define PK_DBG_BROKEN_BARRIER 0x1u
 
+/* Grid barrier construction (both are an arrival counter plus a generation
+ * word with release/acquire ordering).
+ * FLAT: every block adds to one counter; the last one bumps the generation.
+ * TWO_LEVEL: blocks add to the counter of their XCD group (block b mod 8);
+ *   the last of each group adds to a top counter; the last of those bumps one
+ *   generation word per group. Arrivals then contend 8 ways instead of G ways.
+ * AUTO: TWO_LEVEL from 16 blocks up, FLAT below.                            */
+#define PK_BARRIER_AUTO 0
+#define PK_BARRIER_FLAT 1
+#define PK_BARRIER_TWO_LEVEL 2
+
 typedef struct pk_opts {
     int dtype;             /* PK_F32 or PK_F64                                       */
     double h;              /* grid spacing; 0 => 1/(nx-1), which requires nx == ny  */
@@ -109,7 +120,8 @@ typedef struct pk_opts {
                            /* sit on a stream that other work waits behind)         */
     double idle_timeout_s; /* the persistent kernel leaves by itself after this     */
                            /* long without a task; 0 => 120 s                       */
-    int reserved[8];       /* must be zero                                           */
+    int barrier;           /* PK_BARRIER_AUTO, PK_BARRIER_FLAT, PK_BARRIER_TWO_LEVEL */
+    int reserved[7];       /* must be zero                                           */
 } pk_opts;
 
 typedef struct pk_task {
@@ -136,6 +148,7 @@ typedef struct pk_info {
     int halo_depth;         /* RESIDENT: sweeps per exchange; 0 otherwise                */
     int band_rows;          /* rows per band (RESIDENT: per block; STREAM: per unit)     */
     int strips;             /* STREAM: column strips                                     */
+    int barrier;            /* PK_BARRIER_FLAT or PK_BARRIER_TWO_LEVEL                   */
     size_t lds_bytes;       /* dynamic LDS per block                                     */
     double kernel_ms;       /* PERSISTENT: launch-to-exit time of the kernel (HIP        */
                             /* events on its stream), valid after EXIT; LAUNCH: total   */

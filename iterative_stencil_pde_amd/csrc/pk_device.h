@@ -162,40 +162,62 @@ struct BarrierCtx {
     uint32_t epoch;      // generations completed (identical in every block)
     uint64_t spin_ticks;
     bool broken;         // engine flag: data barriers run relaxed (negative control)
+    bool two_level;      // per-XCD-group counters under a top counter
     bool faulted;        // thread 0's view; broadcast at task boundaries
 };
+
+// Lane 0 spins until *gen reaches `target` (relaxed loads, bounded in time).
+__device__ __forceinline__ void spin_until(BarrierCtx& bc, uint32_t* gen, uint32_t target) {
+    if (bc.faulted) return;
+    const uint64_t t0 = wall_clock64();
+    while (static_cast<int32_t>(__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                                target) < 0) {
+        __builtin_amdgcn_s_sleep(1);
+        if (wall_clock64() - t0 > bc.spin_ticks) {
+            bc.faulted = true;
+            __hip_atomic_store(&bc.st->fault, static_cast<uint32_t>(PK_FAULT_BARRIER_TIMEOUT),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t arrive(uint32_t* ctr, bool relaxed) {
+    return relaxed ? __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ void grid_barrier(BarrierCtx& bc, bool relaxed = false) {
     __syncthreads();
     if (threadIdx.x == 0 && bc.grid > 1) {
         const uint32_t target = bc.epoch + 1;
-        uint32_t old;
-        if (!relaxed)
-            old = __hip_atomic_fetch_add(&bc.st->bar_count, 1u, __ATOMIC_RELEASE,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-        else
-            old = __hip_atomic_fetch_add(&bc.st->bar_count, 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-        if (old == target * bc.grid - 1u) {
-            if (!relaxed)
-                __hip_atomic_store(&bc.st->bar_gen, target, __ATOMIC_RELEASE,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            else
-                __hip_atomic_store(&bc.st->bar_gen, target, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        } else if (!bc.faulted) {
-            const uint64_t t0 = wall_clock64();
-            while (static_cast<int32_t>(__hip_atomic_load(&bc.st->bar_gen, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT) -
-                                        target) < 0) {
-                __builtin_amdgcn_s_sleep(1);
-                if (wall_clock64() - t0 > bc.spin_ticks) {
-                    bc.faulted = true;
-                    __hip_atomic_store(&bc.st->fault, static_cast<uint32_t>(PK_FAULT_BARRIER_TIMEOUT),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
+        pk_dev_state* st = bc.st;
+        if (!bc.two_level) {
+            const uint32_t old = arrive(&st->bar_count, relaxed);
+            if (old == target * bc.grid - 1u) {
+                if (!relaxed) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+                __hip_atomic_store(&st->bar_gen, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                spin_until(bc, &st->bar_gen, target);
+            }
+        } else {
+            const uint32_t g = blockIdx.x & 7u;
+            const uint32_t members = (bc.grid - g + 7u) >> 3;   // blocks in group g
+            const uint32_t groups = bc.grid < 8u ? bc.grid : 8u;
+            bool released = false;
+            const uint32_t old = arrive(&st->grp_count[g].v, relaxed);
+            if (old == target * members - 1u) {                  // last of its group
+                if (!relaxed) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                const uint32_t old2 = arrive(&st->top_count, relaxed);
+                if (old2 == target * groups - 1u) {              // last of all
+                    if (!relaxed) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+                    for (uint32_t k = 0; k < groups; ++k)
+                        __hip_atomic_store(&st->grp_gen[k].v, target, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    released = true;
                 }
             }
+            if (!released) spin_until(bc, &st->grp_gen[g].v, target);
         }
         if (!relaxed) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }

@@ -6,6 +6,8 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <cstdio>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -28,6 +30,7 @@ struct Plan {
     int res_band_rows = 0, res_halo = 0, res_ext_rows = 0, lds_pitch = 0;
     size_t lds_bytes = 0;
     int xcd_remap = 0;
+    int barrier_kind = PK_BARRIER_FLAT;
     int occ = 0;  // blocks per CU allowed by the occupancy query
 };
 
@@ -88,6 +91,12 @@ struct pk_engine {
 namespace {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Opt-in diagnostics on stderr (environment variable PK_DEBUG set).
+void debug_msg(const char* what, hipError_t e) {
+    static const bool on = std::getenv("PK_DEBUG") != nullptr;
+    if (on) std::fprintf(stderr, "pk: %s: %s\n", what, hipGetErrorString(e));
+}
 
 int map_err(hipError_t e) {
     if (e == hipSuccess) return PK_OK;
@@ -180,6 +189,8 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         p.grid = std::max(1, g);
     }
     p.xcd_remap = (p.grid >= 8 && p.grid % 8 == 0) ? 1 : 0;
+    p.barrier_kind = o.barrier != PK_BARRIER_AUTO ? o.barrier
+                     : (p.grid >= 16 ? PK_BARRIER_TWO_LEVEL : PK_BARRIER_FLAT);
     stream_geometry(p, e->nx, e->ny, e->esize, 4);
 
     // occupancy of the kernel that will be resident, at its LDS footprint
@@ -189,11 +200,18 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   static_cast<int>(p.lds_bytes));
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, p.threads, p.lds_bytes) != hipSuccess)
+    const hipError_t oe = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, p.threads, p.lds_bytes);
+    if (oe != hipSuccess) {
+        debug_msg("occupancy query", oe);
         return PK_EDEVICE;
+    }
     p.occ = occ;
-    if (occ < 1) return PK_ELAUNCH;
-    if (e->mode == PK_PERSISTENT && p.grid > occ * e->cus) return PK_ELAUNCH;
+    if (occ < 1 || (e->mode == PK_PERSISTENT && p.grid > occ * e->cus)) {
+        if (std::getenv("PK_DEBUG"))
+            std::fprintf(stderr, "pk: grid of %d blocks x %d threads (%zu B LDS) not co-resident: "
+                         "%d per CU x %d CUs\n", p.grid, p.threads, p.lds_bytes, occ, e->cus);
+        return PK_ELAUNCH;
+    }
     e->plan = p;
     return PK_OK;
 }
@@ -218,6 +236,7 @@ void fill_kargs(pk_engine* e) {
     a.layout = p.layout;
     a.grid = p.grid;
     a.xcd_remap = p.xcd_remap;
+    a.barrier_kind = p.barrier_kind;
     a.flags = e->flags;
     a.st = e->d_st;
     a.mail = e->d_mail;
@@ -269,6 +288,7 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     if (o.threads != 0 && (o.threads < 64 || o.threads > 1024 || o.threads % 64 != 0)) return PK_EINVAL;
     if (o.max_blocks < 0 || o.halo_depth < 0 || o.idle_timeout_s < 0) return PK_EINVAL;
     if (o.flags & ~PK_DBG_BROKEN_BARRIER) return PK_EINVAL;
+    if (o.barrier < PK_BARRIER_AUTO || o.barrier > PK_BARRIER_TWO_LEVEL) return PK_EINVAL;
     for (int r : o.reserved)
         if (r != 0) return PK_EINVAL;
     double h = o.h;
@@ -379,6 +399,7 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
         he = hipLaunchCooperativeKernel(fn, dim3(e->plan.grid), dim3(e->plan.threads), args,
                                         static_cast<unsigned>(e->plan.lds_bytes), e->stream);
         if (he != hipSuccess) {
+            debug_msg("cooperative launch", he);
             (void)hipStreamSynchronize(e->stream);
             release(e);
             return PK_ELAUNCH;
@@ -559,11 +580,14 @@ int pk_get_info(pk_engine* e, pk_info* info) {
     info->band_rows = e->plan.layout == PK_LAYOUT_RESIDENT ? e->plan.res_band_rows : e->plan.band_rows;
     info->strips = e->plan.strips;
     info->lds_bytes = e->plan.lds_bytes;
+    info->barrier = e->plan.barrier_kind;
     info->kernel_launches = e->launches;
     if (e->mode == PK_PERSISTENT) {
         info->sweeps_done = e->ring.sweeps_seen();
         info->tasks_done = static_cast<int64_t>(e->ring.done_seen());
-        if (__atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE) && hipEventQuery(e->ev_end) == hipSuccess) {
+        // once the kernel has said it is leaving, its end event completes promptly
+        if (__atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE) &&
+            hipEventSynchronize(e->ev_end) == hipSuccess) {
             float ms = 0.f;
             if (hipEventElapsedTime(&ms, e->ev_start, e->ev_end) == hipSuccess) info->kernel_ms = ms;
         }

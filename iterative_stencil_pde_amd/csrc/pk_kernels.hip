@@ -190,6 +190,7 @@ __global__ void __launch_bounds__(1024) pk_persistent(pk_kargs a) {
     bc.epoch = 0;
     bc.spin_ticks = a.spin_ticks;
     bc.broken = (a.flags & PK_DBG_BROKEN_BARRIER) != 0;
+    bc.two_level = a.barrier_kind == PK_BARRIER_TWO_LEVEL;
     bc.faulted = false;
 
     const bool leader = (blockIdx.x == 0) && (threadIdx.x == 0);

@@ -52,9 +52,18 @@ struct pk_mailbox {
 // Device-memory state of one engine; zeroed once before the kernel starts.
 // The barrier's two words live on separate lines: arrivals hammer `count`
 // while waiters poll `gen`.
+struct alignas(256) pk_word256 {
+    uint32_t v;
+};
+
 struct pk_dev_state {
     alignas(PK_LINE) uint32_t bar_count;   // arrivals, monotonically increasing
     alignas(PK_LINE) uint32_t bar_gen;     // completed barrier generations
+    // two-level barrier: one arrival counter and one generation word per XCD
+    // group (block b belongs to group b mod 8), and a top-level counter
+    pk_word256 grp_count[8];
+    pk_word256 grp_gen[8];
+    alignas(256) uint32_t top_count;
     alignas(PK_LINE) uint64_t task_seq;    // task broadcast (written by the leader)
     int32_t task_kind;
     int32_t task_n;
@@ -78,6 +87,7 @@ struct pk_kargs {
     int layout;            // PK_LAYOUT_STREAM or PK_LAYOUT_RESIDENT
     int grid;              // blocks in the grid
     int xcd_remap;         // 1: map consecutive logical blocks onto one XCD
+    int barrier_kind;      // PK_BARRIER_FLAT or PK_BARRIER_TWO_LEVEL
     uint32_t flags;
     uint64_t idle_ticks;   // wall-clock ticks without a task before leaving
     uint64_t spin_ticks;   // wall-clock ticks a barrier may wait before faulting

@@ -12,12 +12,13 @@ from parity import field_gate, say
 pytestmark = pytest.mark.gpu
 
 
-def test_stamp_check_correct_barrier():
+@pytest.mark.parametrize("barrier", [pk.PK_BARRIER_FLAT, pk.PK_BARRIER_TWO_LEVEL], ids=["flat", "two_level"])
+def test_stamp_check_correct_barrier(barrier):
     """After each barrier every block sees the stamps all blocks wrote before it
     ("Grid-Wide Barriers", "The barrier is a counter and a generation"; the
     "@persistent" page, "grid_barrier")."""
     w = inputs.laplace_top_edge(4096, 0)
-    with pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM) as e:
+    with pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM, barrier=barrier) as e:
         info = e.info()
         say(f"  grid={info.grid_blocks} threads={info.threads}")
         r = e.run(pk.PK_STAMP, 20000, 120)
@@ -28,13 +29,21 @@ def test_stamp_check_correct_barrier():
         assert np.array_equal(e.readback(), w.u0)
 
 
-@pytest.mark.parametrize("blocks", [2, 8, 64, 256])
-def test_barrier_only_tasks(blocks):
+@pytest.mark.parametrize("barrier", [pk.PK_BARRIER_FLAT, pk.PK_BARRIER_TWO_LEVEL], ids=["flat", "two_level"])
+@pytest.mark.parametrize("blocks", [2, 7, 8, 64, 256, 1024])
+def test_barrier_only_tasks(blocks, barrier):
     w = inputs.laplace_random_interior(256, 0)
-    with pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM, max_blocks=blocks, threads=256) as e:
+    try:
+        eng = pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM, max_blocks=blocks, threads=256,
+                        barrier=barrier)
+    except pk.PkError as ex:
+        assert ex.status == pk.PK_ELAUNCH
+        pytest.skip(f"{blocks} blocks of 256 threads are not co-resident on this device")
+    with eng as e:
         r = e.run(pk.PK_BARRIER, 5000)
         r2 = e.run(pk.PK_STAMP, 2000)
-        say(f"  blocks={e.info().grid_blocks}: barrier {r.device_us / 5000:.3f} us, stamp errors {r2.errors}")
+        say(f"  blocks={e.info().grid_blocks} barrier_kind={e.info().barrier}: "
+            f"{r.device_us / 5000:.3f} us per barrier, stamp errors {r2.errors}")
         assert r2.errors == 0
 
 
@@ -49,15 +58,17 @@ def test_broken_barrier_negative_control():
     sweeps = 400
     ref, _ = oracle.jacobi(w.u0, sweeps)
     results = {}
-    for label, flags in (("correct", 0), ("broken", pk.PK_DBG_BROKEN_BARRIER)):
-        with pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM, flags=flags) as e:
+    for label, flags, kind in (("correct flat", 0, pk.PK_BARRIER_FLAT),
+                               ("correct two-level", 0, pk.PK_BARRIER_TWO_LEVEL),
+                               ("broken", pk.PK_DBG_BROKEN_BARRIER, pk.PK_BARRIER_AUTO)):
+        with pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM, flags=flags, barrier=kind) as e:
             e.run(pk.PK_SWEEP, sweeps)
             got = e.readback()
             stamp = e.run(pk.PK_STAMP, 5000).errors
         ok, err, tol, nonbit = field_gate(got, ref)
         say(f"  {label}: max_abs={err:.3e} tol={tol:.3e} non_bitwise={nonbit} stamp_errors={stamp}")
         results[label] = (ok, stamp)
-    assert results["correct"] == (True, 0)
+    assert results["correct flat"] == (True, 0) and results["correct two-level"] == (True, 0)
     assert (not results["broken"][0]) or results["broken"][1] > 0, \
         "the fence-less barrier produced no visible race on this run"
 
@@ -147,17 +158,3 @@ def test_launch_mode_rejects_persistent_only_tasks():
         got = e.readback()
         ref, _ = oracle.jacobi(w.u0, 250)
         assert np.array_equal(got, ref)
-
-
-def test_engine_on_a_torch_stream():
-    """PyTorch provides the stream (plumbing only); the engine's kernels run on it."""
-    torch = pytest.importorskip("torch")
-    s = torch.cuda.Stream()
-    w = inputs.poisson_uniform(256, 0)
-    with pk.Engine(w.u0, w.f, h=w.h, mode=pk.PK_LAUNCH, stream=s.cuda_stream) as e:
-        e.sweep(100)
-        r = e.residual()
-        got = e.readback()
-    ref, res = oracle.jacobi(w.u0, 100, f=w.f, h=w.h, checkpoints=[100])
-    assert np.array_equal(got, ref)
-    assert abs(r - res[0]) <= 1e-9 * res[0]

@@ -104,7 +104,8 @@ def test_ragged_shapes(shape, dtype, poisson, mode):
 
 
 # ---- the LDS-resident layout across block counts and halo depths ----------
-@pytest.mark.parametrize("blocks,halo", [(2, 1), (3, 5), (5, 8), (8, 3), (16, 4), (31, 2), (64, 3)])
+@pytest.mark.parametrize("blocks,halo", [(5, 1), (6, 4), (8, 3), (16, 4), (31, 2), (64, 3),
+                                         (127, 2), (254, 1)])
 def test_resident_layout_blocks_and_halos(blocks, halo):
     w = inputs.poisson_uniform(256, 0, 100)
     # uneven task lengths so periods end part-way
@@ -119,13 +120,35 @@ def test_resident_layout_blocks_and_halos(blocks, halo):
     check_against_oracle(w, got, ref, f"resident/{blocks}/{halo}")
 
 
+def test_resident_layout_refused_when_bands_do_not_fit():
+    """Two blocks would each need a 127-row band of 256 fp32 values x 3 arrays
+    (381 KiB) in LDS; the engine refuses instead of running something else."""
+    w = inputs.poisson_uniform(256, 0)
+    with pytest.raises(pk.PkError) as ex:
+        pk.Engine(w.u0, w.f, h=w.h, layout=pk.PK_LAYOUT_RESIDENT, max_blocks=2)
+    assert ex.value.status == pk.PK_EINVAL
+
+
+@pytest.mark.parametrize("barrier", [pk.PK_BARRIER_FLAT, pk.PK_BARRIER_TWO_LEVEL], ids=["flat", "two_level"])
+@pytest.mark.parametrize("layout", [pk.PK_LAYOUT_STREAM, pk.PK_LAYOUT_RESIDENT], ids=["stream", "resident"])
+def test_both_barrier_kinds(barrier, layout):
+    w = inputs.laplace_random_interior(1024, 0)
+    w.script = [("residual",), ("sweep", 37), ("residual",), ("sweep", 100), ("residual",), ("readback",)]
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=layout, barrier=barrier)
+    assert got["info"].barrier == barrier
+    check_against_oracle(w, got, ref, f"barrier{barrier}/layout{layout}")
+
+
 def test_resident_fp64_wide():
     u, f = _random_case(130, 1000, np.float64, True, seed=77)
     w = inputs.Workload("wide64", 1000, 130, np.float64, 0.01, u, f,
                         [("sweep", 11), ("residual",), ("sweep", 20), ("readback",)], "")
     ref = run_oracle_script(w)
-    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_RESIDENT, max_blocks=20,
+    # 1000 doubles x 3 arrays = 24 KB per LDS row: 6 rows per block, so 2-row bands, halo 2
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_RESIDENT, max_blocks=64,
                             halo_depth=2)
+    assert got["info"].band_rows == 2 and got["info"].halo_depth == 2
     check_against_oracle(w, got, ref, "resident/f64")
 
 
