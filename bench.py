@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--threads", type=int, default=0)
     ap.add_argument("--max-blocks", type=int, default=0)
     ap.add_argument("--halo", type=int, default=0)
+    ap.add_argument("--barrier", default="auto", choices=["auto", "flat", "two_level", "xcd"])
+    ap.add_argument("--pass-sweeps", type=int, default=0, help="stream layout: sweeps per pass")
+    ap.add_argument("--band-rows", type=int, default=0, help="stream passes: rows per band")
     ap.add_argument("--launch-steps", type=int, default=0,
                     help="steps for the per-launch comparison (default: same as --steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -142,8 +145,11 @@ def main():
     w = inputs.make(args.workload)
     layout = {"auto": pk.PK_LAYOUT_AUTO, "stream": pk.PK_LAYOUT_STREAM,
               "resident": pk.PK_LAYOUT_RESIDENT}[args.layout]
+    barrier = {"auto": pk.PK_BARRIER_AUTO, "flat": pk.PK_BARRIER_FLAT,
+               "two_level": pk.PK_BARRIER_TWO_LEVEL, "xcd": pk.PK_BARRIER_XCD}[args.barrier]
     opts = dict(layout=layout, threads=args.threads, max_blocks=args.max_blocks,
-                halo_depth=args.halo, idle_timeout_s=args.idle_timeout)
+                halo_depth=args.halo, idle_timeout_s=args.idle_timeout, barrier=barrier,
+                pass_sweeps=args.pass_sweeps, band_rows=args.band_rows)
     step_bytes, sweep_bytes = algorithmic_bytes(w)
     cells_per_step = w.interior_cells * w.sweeps
 
@@ -197,6 +203,8 @@ def main():
             "threads": info.threads,
             "halo_depth": info.halo_depth,
             "band_rows": info.band_rows,
+            "barrier": {1: "flat", 2: "two_level", 3: "xcd"}[info.barrier],
+            "pass_sweeps": info.pass_sweeps,
         },
         "per_launch": None if args.persistent_only else {
             "value": round(lvalue, 4),

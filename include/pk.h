@@ -99,10 +99,16 @@ extern "C" {
  * TWO_LEVEL: blocks add to the counter of their XCD group (block b mod 8);
  *   the last of each group adds to a top counter; the last of those bumps one
  *   generation word per group. Arrivals then contend 8 ways instead of G ways.
+ * XCD: TWO_LEVEL grouped by the XCD each block runs on (read from the
+ *   hardware at launch), with the L2 write-back done once per XCD instead of
+ *   once per block: every wave waits for its own stores before its block
+ *   arrives and the last block of an XCD writes that XCD's L2 back once; each
+ *   block still does its own acquire.
  * AUTO: TWO_LEVEL from 16 blocks up, FLAT below.                            */
 #define PK_BARRIER_AUTO 0
 #define PK_BARRIER_FLAT 1
 #define PK_BARRIER_TWO_LEVEL 2
+#define PK_BARRIER_XCD 3
 
 typedef struct pk_opts {
     int dtype;             /* PK_F32 or PK_F64                                       */
@@ -120,8 +126,14 @@ typedef struct pk_opts {
                            /* sit on a stream that other work waits behind)         */
     double idle_timeout_s; /* the persistent kernel leaves by itself after this     */
                            /* long without a task; 0 => 120 s                       */
-    int barrier;           /* PK_BARRIER_AUTO, PK_BARRIER_FLAT, PK_BARRIER_TWO_LEVEL */
-    int reserved[7];       /* must be zero                                           */
+    int barrier;           /* PK_BARRIER_*                                           */
+    int pass_sweeps;       /* STREAM: sweeps per pass, 1..4: each wave carries k     */
+                           /* levels of its band in registers, so the field crosses */
+                           /* HBM and the grid barrier once per k sweeps; 0 = auto; */
+                           /* at most 3 with a source term (pk_info reports it)     */
+    int band_rows;         /* STREAM passes: rows per band (a unit is a band x one  */
+                           /* strip, one per wave); 0 = automatic                   */
+    int reserved[5];       /* must be zero                                           */
 } pk_opts;
 
 typedef struct pk_task {
@@ -148,7 +160,8 @@ typedef struct pk_info {
     int halo_depth;         /* RESIDENT: sweeps per exchange; 0 otherwise                */
     int band_rows;          /* rows per band (RESIDENT: per block; STREAM: per unit)     */
     int strips;             /* STREAM: column strips                                     */
-    int barrier;            /* PK_BARRIER_FLAT or PK_BARRIER_TWO_LEVEL                   */
+    int barrier;            /* PK_BARRIER_FLAT, _TWO_LEVEL or _XCD                       */
+    int pass_sweeps;        /* STREAM: sweeps per pass                                   */
     size_t lds_bytes;       /* dynamic LDS per block                                     */
     double kernel_ms;       /* PERSISTENT: launch-to-exit time of the kernel (HIP        */
                             /* events on its stream), valid after EXIT; LAUNCH: total   */

@@ -163,7 +163,11 @@ struct BarrierCtx {
     uint64_t spin_ticks;
     bool broken;         // engine flag: data barriers run relaxed (negative control)
     bool two_level;      // per-XCD-group counters under a top counter
+    bool xcd;            // groups by hardware XCD, cache maintenance once per XCD
     bool faulted;        // thread 0's view; broadcast at task boundaries
+    uint32_t xg;         // XCD barrier: this block's XCD
+    uint32_t xmembers;   // XCD barrier: blocks on this XCD
+    uint32_t xgroups;    // XCD barrier: XCDs with at least one block
 };
 
 // Lane 0 spins until *gen reaches `target` (relaxed loads, bounded in time).
@@ -187,7 +191,58 @@ __device__ __forceinline__ uint32_t arrive(uint32_t* ctr, bool relaxed) {
                    : __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wait for this wave's outstanding vector memory operations (vmcnt(0)).
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// XCD-grouped barrier (PK_BARRIER_XCD). A wave's stores are in its XCD's L2
+// once its vmcnt reaches 0 (the vector L1 is write-through), and an agent-scope
+// release fence writes back the whole L2 of the XCD it runs on. So the release
+// can be done once per XCD instead of once per block:
+//   every wave: vmcnt(0) (its stores have reached the XCD's L2);
+//   lane 0: relaxed add to its XCD's counter; the last block of the XCD issues
+//     the release fence (one L2 write-back covering every block of that XCD)
+//     and adds to the top counter; the last XCD stores the top generation and
+//     the generation word of every XCD;
+//   every block then waits for its XCD's generation and issues its own acquire
+//     fence: the L2 invalidate must stay per block, because it is also what
+//     invalidates the block's own CU L1 (a workgroup-scope invalidate does not
+//     touch the L1 outside thread-group-split mode).
+// Blocks are grouped by the XCD they actually run on, read from the hardware
+// at launch, so placement does not affect correctness.
+__device__ __forceinline__ void xcd_barrier(BarrierCtx& bc) {
+    wait_vm();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t target = bc.epoch + 1;
+        pk_dev_state* st = bc.st;
+        const uint32_t g = bc.xg;
+        const uint32_t old = __hip_atomic_fetch_add(&st->xgrp_count[g].v, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        bool released = false;
+        if (old == target * bc.xmembers - 1u) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const uint32_t old2 = __hip_atomic_fetch_add(&st->xtop_count, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            if (old2 == target * bc.xgroups - 1u) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+                for (uint32_t k = 0; k < 8; ++k)
+                    __hip_atomic_store(&st->xgrp_gen[k].v, target, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                released = true;
+            }
+        }
+        if (!released) spin_until(bc, &st->xgrp_gen[g].v, target);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    bc.epoch += 1;
+    __syncthreads();
+}
+
 __device__ __forceinline__ void grid_barrier(BarrierCtx& bc, bool relaxed = false) {
+    if (bc.xcd && !relaxed && bc.grid > 1) {
+        xcd_barrier(bc);
+        return;
+    }
     __syncthreads();
     if (threadIdx.x == 0 && bc.grid > 1) {
         const uint32_t target = bc.epoch + 1;
@@ -233,6 +288,14 @@ __device__ __forceinline__ int logical_block(int remap, int grid) {
     if (!remap) return b;
     const int per = grid >> 3;
     return (b & 7) * per + (b >> 3);
+}
+
+// Global wave number for unit assignment, wave-major across blocks: unit u goes
+// to wave (u / G) of logical block (u mod G), so every block (every CU) gets
+// work even when there are fewer units than waves, and consecutive units sit on
+// consecutive logical blocks, i.e. on one XCD.
+__device__ __forceinline__ int unit_wave(const pk_kargs& a) {
+    return (static_cast<int>(threadIdx.x) >> 6) * a.grid + logical_block(a.xcd_remap, a.grid);
 }
 
 // ---------------------------------------------------------------------------
@@ -358,9 +421,8 @@ template <typename T, bool HAS_B>
 __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restrict__ src,
                                              T* __restrict__ dst) {
     constexpr int W = VecW<T>::W;
-    const int wpb = static_cast<int>(blockDim.x) >> 6;
-    const int gw = logical_block(a.xcd_remap, a.grid) * wpb + (static_cast<int>(threadIdx.x) >> 6);
-    const int nw = a.grid * wpb;
+    const int gw = unit_wave(a);
+    const int nw = a.grid * (static_cast<int>(blockDim.x) >> 6);
     const int units = a.strips * a.bands;
     const T* bsrc = static_cast<const T*>(a.b);
     for (int u = gw; u < units; u += nw) {
@@ -374,14 +436,139 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
     }
 }
 
+// ---------------------------------------------------------------------------
+// K sweeps per pass (temporal blocking in the column march). Level 0 is the
+// field in src; level j row i is the stencil of level j-1 rows i-1, i, i+1.
+// At step t the wave loads level-0 row t and computes level j row t-j for
+// j = 1..K (t+j when marching up), each level keeping its last three rows in
+// registers, and stores level K's row when it lies in the unit's band [r0, r1). The band therefore
+// reads K halo rows above and below, and the field is read and written once
+// per K sweeps. Ring rows keep their value at every level (the middle row of
+// the previous level), ring and padding columns likewise (the stencil's mask).
+//
+// Columns: the strip's lanes 0..ov-1 and 64-ov..63 overlap the neighbouring
+// strips and are never stored. Their outer neighbour is not loaded (zero), so
+// wrong values spread inward one column per level; after K <= ov * W levels
+// they have not reached a stored lane. A strip stores (64 - 2 ov) * W columns
+// starting at c0 + ov * W. Results equal K single sweeps bit for bit: every
+// stored value is the same expression on the same operands.
+// ---------------------------------------------------------------------------
+template <typename T, bool HAS_B, int K>
+__device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* __restrict__ dst,
+                                                 const T* __restrict__ bsrc, int nx, int ny,
+                                                 int pitch, int c0, int ov, int r0, int r1,
+                                                 int dir) {
+    constexpr int W = VecW<T>::W;
+    // rows of loads issued ahead; fewer for deep passes (registers hold K windows)
+    constexpr int CH = (HAS_B || (K >= 3 && sizeof(T) == 8)) ? 2 : 4;
+    const int lane = threadIdx.x & 63;
+    const int col = c0 + lane * W;
+    const bool act = col >= 0 && col < nx;
+    const bool store_lane = act && lane >= ov && lane < 64 - ov;
+    const size_t p = static_cast<size_t>(pitch);
+
+    Vec<T> win[K][3];  // win[j] = level j rows (x-2, x-1, x), x the last row pushed
+    Vec<T> bq[K];      // bq[j] = b row of the level j+1 row computed at step t
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        win[j][0] = win[j][1] = win[j][2] = vzero<T>();
+        bq[j] = vzero<T>();
+    }
+    // dir = +1 marches down from r0 - K, dir = -1 marches up from r1 - 1 + K;
+    // neighbouring bands march in opposite directions, so the halo rows they
+    // share are read at about the same time (and hit in the XCD's L2)
+    const int nsteps = (r1 - r0) + 2 * K;
+    const int t_first = dir > 0 ? r0 - K : r1 - 1 + K;
+    for (int q0 = 0; q0 < nsteps; q0 += CH) {
+        Vec<T> ld[CH];
+        Vec<T> lb[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int t = t_first + dir * (q0 + c);
+            const bool live = q0 + c < nsteps;
+            ld[c] = (act && live && t >= 0 && t < ny) ? vload(src + static_cast<size_t>(t) * p + col)
+                                                      : vzero<T>();
+            if (HAS_B) {
+                const int rb = t - dir;
+                lb[c] = (act && live && rb >= 1 && rb <= ny - 2)
+                            ? vload(bsrc + static_cast<size_t>(rb) * p + col) : vzero<T>();
+            } else {
+                lb[c] = vzero<T>();
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            if (q0 + c >= nsteps) break;  // wave-uniform
+            const int t = t_first + dir * (q0 + c);
+            // level 0 receives row t
+            win[0][0] = win[0][1];
+            win[0][1] = win[0][2];
+            win[0][2] = ld[c];
+#pragma unroll
+            for (int j = K - 1; j > 0; --j) bq[j] = bq[j - 1];
+            bq[0] = lb[c];
+#pragma unroll
+            for (int j = 1; j <= K; ++j) {
+                const int row = t - dir * j;  // level j row computed at this step
+                Vec<T> o = stencil<T, HAS_B>(win[j - 1][0], win[j - 1][1], win[j - 1][2], bq[j - 1],
+                                             T(0), col, nx);
+                if (row <= 0 || row >= ny - 1) o = win[j - 1][1];  // ring rows (and beyond)
+                if (j < K) {
+                    win[j][0] = win[j][1];
+                    win[j][1] = win[j][2];
+                    win[j][2] = o;
+                } else if (store_lane && row >= r0 && row < r1) {
+                    vstore(dst + static_cast<size_t>(row) * p + col, o);
+                }
+            }
+        }
+    }
+}
+
+// One pass of k sweeps (1 <= k <= PK_MAX_PASS) over all units, src -> dst.
+template <typename T, bool HAS_B, int K>
+__device__ __forceinline__ void stream_pass_k(const pk_kargs& a, const T* __restrict__ src,
+                                              T* __restrict__ dst) {
+    constexpr int W = VecW<T>::W;
+    const int ov = (K + W - 1) / W;
+    const int stride = (64 - 2 * ov) * W;  // stored columns per strip
+    const int strips = (a.nx + stride - 1) / stride;
+    const int gw = unit_wave(a);
+    const int nw = a.grid * (static_cast<int>(blockDim.x) >> 6);
+    const int units = strips * a.pbands;
+    const T* bsrc = static_cast<const T*>(a.b);
+    for (int u = gw; u < units; u += nw) {
+        const int strip = u % strips, band = u / strips;
+        const int r0 = 1 + band * a.pband_rows;
+        const int r1 = min(a.ny - 1, r0 + a.pband_rows);
+        if (r0 >= r1) continue;
+        stream_pass_unit<T, HAS_B, K>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W, ov,
+                                      r0, r1, (band & 1) ? -1 : 1);
+    }
+}
+
+template <typename T, bool HAS_B>
+__device__ __forceinline__ void stream_pass(const pk_kargs& a, const T* __restrict__ src,
+                                            T* __restrict__ dst, int k) {
+    // a source term adds a window of b rows: passes of at most 3 sweeps then
+    // (the host caps pass_sweeps accordingly), so the kernel stays within 128 VGPRs
+    switch (k) {
+        case 2: stream_pass_k<T, HAS_B, 2>(a, src, dst); break;
+        case 3: stream_pass_k<T, HAS_B, 3>(a, src, dst); break;
+        case 4:
+            if (!HAS_B) stream_pass_k<T, HAS_B, 4>(a, src, dst);
+            break;
+        default: stream_sweep<T, HAS_B>(a, src, dst); break;
+    }
+}
+
 // Per-block sum of rho^2 over the same units; valid in thread 0.
 template <typename T, bool HAS_B>
 __device__ __forceinline__ double stream_residual_block(const pk_kargs& a, const T* __restrict__ src,
                                                         double* s_red) {
     constexpr int W = VecW<T>::W;
-    const int wpb = static_cast<int>(blockDim.x) >> 6;
-    const int gw = logical_block(a.xcd_remap, a.grid) * wpb + (static_cast<int>(threadIdx.x) >> 6);
-    const int nw = a.grid * wpb;
+    const int gw = unit_wave(a);
+    const int nw = a.grid * (static_cast<int>(blockDim.x) >> 6);
     const int units = a.strips * a.bands;
     const T* bsrc = static_cast<const T*>(a.b);
     double acc = 0.0;

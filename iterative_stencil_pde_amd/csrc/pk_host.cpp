@@ -31,6 +31,8 @@ struct Plan {
     size_t lds_bytes = 0;
     int xcd_remap = 0;
     int barrier_kind = PK_BARRIER_FLAT;
+    int pass_sweeps = 1;
+    int pband_rows = 1, pbands = 1;
     int occ = 0;  // blocks per CU allowed by the occupancy query
 };
 
@@ -190,8 +192,26 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     }
     p.xcd_remap = (p.grid >= 8 && p.grid % 8 == 0) ? 1 : 0;
     p.barrier_kind = o.barrier != PK_BARRIER_AUTO ? o.barrier
-                     : (p.grid >= 16 ? PK_BARRIER_TWO_LEVEL : PK_BARRIER_FLAT);
+                     : (p.grid >= 16 && !(o.flags & PK_DBG_BROKEN_BARRIER) ? PK_BARRIER_XCD
+                        : (p.grid >= 16 ? PK_BARRIER_TWO_LEVEL : PK_BARRIER_FLAT));
     stream_geometry(p, e->nx, e->ny, e->esize, 4);
+    // passes of k sweeps (stream layout, persistent only): about one unit per
+    // wave, bands at least 4 k rows tall (each band re-reads 2 k halo rows)
+    p.pass_sweeps = 1;
+    if (e->mode == PK_PERSISTENT && p.layout == PK_LAYOUT_STREAM)
+        p.pass_sweeps = o.pass_sweeps > 0 ? o.pass_sweeps : 2;
+    // with a source term the kernel carries a window of b rows too: at most 3
+    if (e->has_b && p.pass_sweeps > 3) p.pass_sweeps = 3;
+    {
+        const int k = p.pass_sweeps;
+        const int ov = (k + W - 1) / W;
+        const int strips_k = ceil_div(e->nx, (64 - 2 * ov) * W);
+        const int nw = p.grid * (p.threads / 64);
+        int bands = std::max(1, nw / strips_k);
+        bands = std::min(bands, std::max(1, interior / (4 * k)));
+        p.pband_rows = o.band_rows > 0 ? std::min(o.band_rows, interior) : ceil_div(interior, bands);
+        p.pbands = ceil_div(interior, p.pband_rows);
+    }
 
     // occupancy of the kernel that will be resident, at its LDS footprint
     const void* fn = e->mode == PK_PERSISTENT ? pkk_persistent_fn(e->dtype, e->has_b, p.layout)
@@ -237,6 +257,9 @@ void fill_kargs(pk_engine* e) {
     a.grid = p.grid;
     a.xcd_remap = p.xcd_remap;
     a.barrier_kind = p.barrier_kind;
+    a.pass_sweeps = p.pass_sweeps;
+    a.pband_rows = p.pband_rows;
+    a.pbands = p.pbands;
     a.flags = e->flags;
     a.st = e->d_st;
     a.mail = e->d_mail;
@@ -287,8 +310,12 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     if (o.layout < PK_LAYOUT_AUTO || o.layout > PK_LAYOUT_RESIDENT) return PK_EINVAL;
     if (o.threads != 0 && (o.threads < 64 || o.threads > 1024 || o.threads % 64 != 0)) return PK_EINVAL;
     if (o.max_blocks < 0 || o.halo_depth < 0 || o.idle_timeout_s < 0) return PK_EINVAL;
+    if (o.pass_sweeps < 0 || o.pass_sweeps > PK_MAX_PASS || o.band_rows < 0) return PK_EINVAL;
     if (o.flags & ~PK_DBG_BROKEN_BARRIER) return PK_EINVAL;
-    if (o.barrier < PK_BARRIER_AUTO || o.barrier > PK_BARRIER_TWO_LEVEL) return PK_EINVAL;
+    if (o.barrier < PK_BARRIER_AUTO || o.barrier > PK_BARRIER_XCD) return PK_EINVAL;
+    // the negative control relaxes the flat/two-level barriers; the XCD barrier keeps
+    // separate counters, so the two are not combined
+    if ((o.flags & PK_DBG_BROKEN_BARRIER) && o.barrier == PK_BARRIER_XCD) return PK_EINVAL;
     for (int r : o.reserved)
         if (r != 0) return PK_EINVAL;
     double h = o.h;
@@ -577,10 +604,12 @@ int pk_get_info(pk_engine* e, pk_info* info) {
     info->blocks_per_cu_max = e->plan.occ;
     info->cus = e->cus;
     info->halo_depth = e->plan.layout == PK_LAYOUT_RESIDENT ? e->plan.res_halo : 0;
-    info->band_rows = e->plan.layout == PK_LAYOUT_RESIDENT ? e->plan.res_band_rows : e->plan.band_rows;
+    info->band_rows = e->plan.layout == PK_LAYOUT_RESIDENT ? e->plan.res_band_rows
+                      : (e->plan.pass_sweeps > 1 ? e->plan.pband_rows : e->plan.band_rows);
     info->strips = e->plan.strips;
     info->lds_bytes = e->plan.lds_bytes;
     info->barrier = e->plan.barrier_kind;
+    info->pass_sweeps = e->plan.pass_sweeps;
     info->kernel_launches = e->launches;
     if (e->mode == PK_PERSISTENT) {
         info->sweeps_done = e->ring.sweeps_seen();

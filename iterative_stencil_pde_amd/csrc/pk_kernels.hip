@@ -191,7 +191,29 @@ __global__ void __launch_bounds__(1024) pk_persistent(pk_kargs a) {
     bc.spin_ticks = a.spin_ticks;
     bc.broken = (a.flags & PK_DBG_BROKEN_BARRIER) != 0;
     bc.two_level = a.barrier_kind == PK_BARRIER_TWO_LEVEL;
+    bc.xcd = false;
     bc.faulted = false;
+    bc.xg = 0;
+    bc.xmembers = 1;
+    bc.xgroups = 1;
+    if (a.barrier_kind == PK_BARRIER_XCD && a.grid > 1 && !bc.broken) {
+        // count the blocks on each XCD (one flat barrier, generation 1), then
+        // switch to the XCD barrier, whose counters start from zero
+        if (threadIdx.x == 0) {
+            bc.xg = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7u;  // hwreg(HW_REG_XCC_ID, 0, 4)
+            __hip_atomic_fetch_add(&a.st->xmembers[bc.xg].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        grid_barrier(bc);
+        if (threadIdx.x == 0) {
+            bc.xmembers = __hip_atomic_load(&a.st->xmembers[bc.xg].v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            bc.xgroups = 0;
+            for (int k = 0; k < 8; ++k)
+                bc.xgroups += __hip_atomic_load(&a.st->xmembers[k].v, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) > 0u ? 1u : 0u;
+        }
+        bc.epoch = 0;
+        bc.xcd = true;
+    }
 
     const bool leader = (blockIdx.x == 0) && (threadIdx.x == 0);
     int cur = a.cur0;
@@ -276,13 +298,15 @@ __global__ void __launch_bounds__(1024) pk_persistent(pk_kargs a) {
         int64_t errs = 0;
         int status = PK_OK;
         if (kind == PK_SWEEP) {
-            if (LAYOUT == PK_LAYOUT_RESIDENT) {
+            if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
                 resident_sweep_task<T, HAS_B>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
             } else {
-                for (int s = 0; s < n; ++s) {
-                    stream_sweep<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), static_cast<T*>(a.u[cur ^ 1]));
+                for (int s = 0; s < n;) {
+                    const int k = min(a.pass_sweeps, n - s);
+                    stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), static_cast<T*>(a.u[cur ^ 1]), k);
                     grid_barrier(bc, bc.broken);
                     cur ^= 1;
+                    s += k;
                 }
             }
             sweeps += n;

@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #define PK_RING 64u
+#define PK_MAX_PASS 4
 #define PK_LINE 128
 
 // Internal task kinds (the public ones are in pk.h).
@@ -64,6 +65,13 @@ struct pk_dev_state {
     pk_word256 grp_count[8];
     pk_word256 grp_gen[8];
     alignas(256) uint32_t top_count;
+    // XCD barrier: groups are the XCDs the blocks actually run on (hardware
+    // XCC id), with one L2 write-back and one L2 invalidate per XCD
+    pk_word256 xmembers[8];
+    pk_word256 xgrp_count[8];
+    pk_word256 xgrp_gen[8];
+    alignas(256) uint32_t xtop_count;
+    alignas(256) uint32_t xtop_gen;
     alignas(PK_LINE) uint64_t task_seq;    // task broadcast (written by the leader)
     int32_t task_kind;
     int32_t task_n;
@@ -79,6 +87,9 @@ struct pk_kargs {
     int cur0;              // buffer index holding the field at launch
     // stream geometry: unit = (band, strip); strip = 64 lanes x vector width
     int strips, bands, band_rows;
+    // passes of several sweeps: rows per band and bands (strips depend on k)
+    int pass_sweeps;       // sweeps per pass in the stream layout (1 = one per barrier)
+    int pband_rows, pbands;
     // resident geometry (one band per block)
     int res_band_rows;     // rows per block band (last band may be shorter)
     int res_halo;          // sweeps per halo exchange

@@ -12,7 +12,8 @@ from parity import field_gate, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("barrier", [pk.PK_BARRIER_FLAT, pk.PK_BARRIER_TWO_LEVEL], ids=["flat", "two_level"])
+@pytest.mark.parametrize("barrier", [pk.PK_BARRIER_FLAT, pk.PK_BARRIER_TWO_LEVEL, pk.PK_BARRIER_XCD],
+                         ids=["flat", "two_level", "xcd"])
 def test_stamp_check_correct_barrier(barrier):
     """After each barrier every block sees the stamps all blocks wrote before it
     ("Grid-Wide Barriers", "The barrier is a counter and a generation"; the
@@ -29,7 +30,8 @@ def test_stamp_check_correct_barrier(barrier):
         assert np.array_equal(e.readback(), w.u0)
 
 
-@pytest.mark.parametrize("barrier", [pk.PK_BARRIER_FLAT, pk.PK_BARRIER_TWO_LEVEL], ids=["flat", "two_level"])
+@pytest.mark.parametrize("barrier", [pk.PK_BARRIER_FLAT, pk.PK_BARRIER_TWO_LEVEL, pk.PK_BARRIER_XCD],
+                         ids=["flat", "two_level", "xcd"])
 @pytest.mark.parametrize("blocks", [2, 7, 8, 64, 256, 1024])
 def test_barrier_only_tasks(blocks, barrier):
     w = inputs.laplace_random_interior(256, 0)
@@ -60,6 +62,7 @@ def test_broken_barrier_negative_control():
     results = {}
     for label, flags, kind in (("correct flat", 0, pk.PK_BARRIER_FLAT),
                                ("correct two-level", 0, pk.PK_BARRIER_TWO_LEVEL),
+                               ("correct xcd", 0, pk.PK_BARRIER_XCD),
                                ("broken", pk.PK_DBG_BROKEN_BARRIER, pk.PK_BARRIER_AUTO)):
         with pk.Engine(w.u0, None, layout=pk.PK_LAYOUT_STREAM, flags=flags, barrier=kind) as e:
             e.run(pk.PK_SWEEP, sweeps)
@@ -68,7 +71,8 @@ def test_broken_barrier_negative_control():
         ok, err, tol, nonbit = field_gate(got, ref)
         say(f"  {label}: max_abs={err:.3e} tol={tol:.3e} non_bitwise={nonbit} stamp_errors={stamp}")
         results[label] = (ok, stamp)
-    assert results["correct flat"] == (True, 0) and results["correct two-level"] == (True, 0)
+    for label in ("correct flat", "correct two-level", "correct xcd"):
+        assert results[label] == (True, 0), label
     assert (not results["broken"][0]) or results["broken"][1] > 0, \
         "the fence-less barrier produced no visible race on this run"
 

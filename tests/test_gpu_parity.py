@@ -129,7 +129,8 @@ def test_resident_layout_refused_when_bands_do_not_fit():
     assert ex.value.status == pk.PK_EINVAL
 
 
-@pytest.mark.parametrize("barrier", [pk.PK_BARRIER_FLAT, pk.PK_BARRIER_TWO_LEVEL], ids=["flat", "two_level"])
+@pytest.mark.parametrize("barrier", [pk.PK_BARRIER_FLAT, pk.PK_BARRIER_TWO_LEVEL, pk.PK_BARRIER_XCD],
+                         ids=["flat", "two_level", "xcd"])
 @pytest.mark.parametrize("layout", [pk.PK_LAYOUT_STREAM, pk.PK_LAYOUT_RESIDENT], ids=["stream", "resident"])
 def test_both_barrier_kinds(barrier, layout):
     w = inputs.laplace_random_interior(1024, 0)
@@ -138,6 +139,46 @@ def test_both_barrier_kinds(barrier, layout):
     got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=layout, barrier=barrier)
     assert got["info"].barrier == barrier
     check_against_oracle(w, got, ref, f"barrier{barrier}/layout{layout}")
+
+
+@pytest.mark.parametrize("name,sweeps", [("laplace4096", 30), ("poisson8192", 4)])
+def test_xcd_barrier_full_size(name, sweeps):
+    w = inputs.make(name)
+    w.script = [("sweep", sweeps), ("residual",), ("readback",)]
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, barrier=pk.PK_BARRIER_XCD)
+    assert got["info"].barrier == pk.PK_BARRIER_XCD and got["info"].grid_blocks == 256
+    check_against_oracle(w, got, ref, f"{name}/xcd")
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+@pytest.mark.parametrize("poisson", [False, True], ids=["laplace", "poisson"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("shape", [(3, 3), (5, 300), (300, 5), (67, 131), (130, 257), (33, 1030),
+                                   (17, 4100)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_stream_passes_of_k_sweeps(shape, dtype, poisson, k):
+    """k sweeps per pass (k levels in registers, overlapping strips, k halo rows)
+    must equal k single sweeps exactly; task lengths are not multiples of k."""
+    ny, nx = shape
+    u, f = _random_case(ny, nx, dtype, poisson, seed=7 * ny + nx)
+    w = inputs.Workload(f"pass{ny}x{nx}", nx, ny, dtype, 0.013, u, f,
+                        [("sweep", 7), ("residual",), ("sweep", 13), ("sweep", 1), ("residual",),
+                         ("readback",)], "")
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=k)
+    assert got["info"].pass_sweeps == (min(k, 3) if poisson else k)
+    check_against_oracle(w, got, ref, f"pass{k}/{ny}x{nx}/{np.dtype(dtype).name}")
+
+
+@pytest.mark.parametrize("name,sweeps,k", [("laplace4096", 41, 4), ("laplace4096", 23, 3),
+                                           ("poisson8192", 5, 2), ("poisson8192", 7, 3)])
+def test_stream_passes_full_size(name, sweeps, k):
+    w = inputs.make(name)
+    w.script = [("sweep", sweeps), ("residual",), ("readback",)]
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, pass_sweeps=k)
+    assert got["info"].pass_sweeps == k
+    check_against_oracle(w, got, ref, f"{name}/pass{k}")
 
 
 def test_resident_fp64_wide():
