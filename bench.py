@@ -107,16 +107,20 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="poisson256", choices=sorted(inputs.WORKLOADS))
-    ap.add_argument("--layout", default="auto", choices=["auto", "stream", "resident"])
+    ap.add_argument("--layout", default="auto", choices=["auto", "stream", "resident", "register"])
     ap.add_argument("--threads", type=int, default=0)
     ap.add_argument("--max-blocks", type=int, default=0)
     ap.add_argument("--halo", type=int, default=0)
     ap.add_argument("--barrier", default="auto", choices=["auto", "flat", "two_level", "xcd"])
+    ap.add_argument("--exchange", default="auto", choices=["auto", "barrier", "neighbor"],
+                    help="resident layout: halo exchange by grid barrier or neighbour flags")
     ap.add_argument("--pass-sweeps", type=int, default=0, help="stream layout: sweeps per pass")
     ap.add_argument("--band-rows", type=int, default=0, help="stream passes: rows per band")
     ap.add_argument("--launch-steps", type=int, default=0,
                     help="steps for the per-launch comparison (default: same as --steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweeps-only", action="store_true",
+                    help="a step is one SWEEP task of the workload's sweep count (no residuals)")
     ap.add_argument("--launch-only", action="store_true",
                     help="only the per-launch baseline (for counter collection)")
     ap.add_argument("--persistent-only", action="store_true")
@@ -143,13 +147,17 @@ def main():
         torch.cuda.empty_cache()
 
     w = inputs.make(args.workload)
+    if args.sweeps_only:
+        w.script = [("sweep", w.sweeps)]
     layout = {"auto": pk.PK_LAYOUT_AUTO, "stream": pk.PK_LAYOUT_STREAM,
-              "resident": pk.PK_LAYOUT_RESIDENT}[args.layout]
+              "resident": pk.PK_LAYOUT_RESIDENT, "register": pk.PK_LAYOUT_REGISTER}[args.layout]
     barrier = {"auto": pk.PK_BARRIER_AUTO, "flat": pk.PK_BARRIER_FLAT,
                "two_level": pk.PK_BARRIER_TWO_LEVEL, "xcd": pk.PK_BARRIER_XCD}[args.barrier]
+    exchange = {"auto": pk.PK_EXCHANGE_AUTO, "barrier": pk.PK_EXCHANGE_BARRIER,
+                "neighbor": pk.PK_EXCHANGE_NEIGHBOR}[args.exchange]
     opts = dict(layout=layout, threads=args.threads, max_blocks=args.max_blocks,
                 halo_depth=args.halo, idle_timeout_s=args.idle_timeout, barrier=barrier,
-                pass_sweeps=args.pass_sweeps, band_rows=args.band_rows)
+                pass_sweeps=args.pass_sweeps, band_rows=args.band_rows, exchange=exchange)
     step_bytes, sweep_bytes = algorithmic_bytes(w)
     cells_per_step = w.interior_cells * w.sweeps
 
@@ -198,12 +206,13 @@ def main():
             "sweeps_per_step": w.sweeps,
             "residuals_per_step": sum(1 for s in step_tasks(w) if s[0] == "residual"),
             "mode": "persistent",
-            "layout": {1: "stream", 2: "resident"}[info.layout],
+            "layout": {1: "stream", 2: "resident", 3: "register"}[info.layout],
             "grid_blocks": info.grid_blocks,
             "threads": info.threads,
             "halo_depth": info.halo_depth,
             "band_rows": info.band_rows,
             "barrier": {1: "flat", 2: "two_level", 3: "xcd"}[info.barrier],
+            "exchange": {0: None, 1: "barrier", 2: "neighbor"}[info.exchange],
             "pass_sweeps": info.pass_sweeps,
         },
         "per_launch": None if args.persistent_only else {

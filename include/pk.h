@@ -70,10 +70,14 @@ extern "C" {
  *   whole task; only the halo rows go through HBM, once every halo_depth sweeps
  *   (the wider-halo scheme of "Persistent Kernels", "Reflections and next
  *   steps", "Fewer handshakes", with exact Jacobi semantics).
- * AUTO: RESIDENT when the field's bands fit in LDS, else STREAM.            */
+ * REGISTER: as RESIDENT, but each block's rows live in VGPRs (one 16-byte
+ *   vector per lane per row); only wave-boundary rows and columns go through
+ *   LDS. For fields whose bands fit in a block's registers.
+ * AUTO: REGISTER, else RESIDENT, when the bands fit, else STREAM.           */
 #define PK_LAYOUT_AUTO 0
 #define PK_LAYOUT_STREAM 1
 #define PK_LAYOUT_RESIDENT 2
+#define PK_LAYOUT_REGISTER 3
 
 /* ---- tasks -------------------------------------------------------------- */
 #define PK_SWEEP 1    /* n Jacobi sweeps (n >= 0)                                   */
@@ -104,11 +108,31 @@ extern "C" {
  *   once per block: every wave waits for its own stores before its block
  *   arrives and the last block of an XCD writes that XCD's L2 back once; each
  *   block still does its own acquire.
- * AUTO: TWO_LEVEL from 16 blocks up, FLAT below.                            */
+ * AUTO: XCD from 16 blocks up (TWO_LEVEL under PK_DBG_BROKEN_BARRIER),
+ *   FLAT below.                                                              */
 #define PK_BARRIER_AUTO 0
 #define PK_BARRIER_FLAT 1
 #define PK_BARRIER_TWO_LEVEL 2
 #define PK_BARRIER_XCD 3
+
+/* Halo exchange of the RESIDENT layout between the sweeps of one task
+ * (after every halo_depth sweeps, each block publishes its edge rows to device
+ * memory and reloads its neighbours').
+ * BARRIER: a grid barrier between publish and reload.
+ * NEIGHBOR: point-to-point. Each block release-stores its exchange count to a
+ *   flag of its own (one 128-B line per block) and acquires the flags of the
+ *   two blocks whose bands border its own: blocks wait for their neighbours
+ *   only, never for the slowest block of the grid ("Persistent Kernels",
+ *   "Reflections and next steps", GPU-side scheduling on neighbour step
+ *   counters; "Grid-Wide Barriers and Persistent Work Queues", "What the
+ *   barrier buys", on every block waiting for the slowest). A block is at most
+ *   one exchange ahead of a neighbour, which the two device buffers allow.
+ *   The last exchange of every task is still a grid barrier, so a task ends
+ *   with the whole field in device memory.
+ * AUTO: NEIGHBOR, or BARRIER under PK_DBG_BROKEN_BARRIER.                     */
+#define PK_EXCHANGE_AUTO 0
+#define PK_EXCHANGE_BARRIER 1
+#define PK_EXCHANGE_NEIGHBOR 2
 
 typedef struct pk_opts {
     int dtype;             /* PK_F32 or PK_F64                                       */
@@ -129,11 +153,12 @@ typedef struct pk_opts {
     int barrier;           /* PK_BARRIER_*                                           */
     int pass_sweeps;       /* STREAM: sweeps per pass, 1..4: each wave carries k     */
                            /* levels of its band in registers, so the field crosses */
-                           /* HBM and the grid barrier once per k sweeps; 0 = auto; */
+                           /* HBM and the grid barrier once per k sweeps; 0 = 4,   */
                            /* at most 3 with a source term (pk_info reports it)     */
     int band_rows;         /* STREAM passes: rows per band (a unit is a band x one  */
                            /* strip, one per wave); 0 = automatic                   */
-    int reserved[5];       /* must be zero                                           */
+    int exchange;          /* RESIDENT: PK_EXCHANGE_*                                */
+    int reserved[4];       /* must be zero                                           */
 } pk_opts;
 
 typedef struct pk_task {
@@ -162,6 +187,7 @@ typedef struct pk_info {
     int strips;             /* STREAM: column strips                                     */
     int barrier;            /* PK_BARRIER_FLAT, _TWO_LEVEL or _XCD                       */
     int pass_sweeps;        /* STREAM: sweeps per pass                                   */
+    int exchange;           /* RESIDENT: PK_EXCHANGE_BARRIER or _NEIGHBOR; 0 otherwise   */
     size_t lds_bytes;       /* dynamic LDS per block                                     */
     double kernel_ms;       /* PERSISTENT: launch-to-exit time of the kernel (HIP        */
                             /* events on its stream), valid after EXIT; LAUNCH: total   */

@@ -84,15 +84,15 @@ __device__ __forceinline__ double from_upper(double edge, double v) {
 // ---------------------------------------------------------------------------
 // The stencil on one lane's vector. `col` is the first column of the vector;
 // columns 0 and nx-1 (the Dirichlet ring) and padding columns >= nx keep
-// their value. `edge` holds, for lane 0, column col-1 and, for lane 63,
-// column col+W of the same row; the other lanes get theirs by DPP.
+// their value. west_of_first / east_of_last are columns col-1 and col+W of
+// the same row. In stencil(), `edge` holds, for lane 0, column col-1 and, for
+// lane 63, column col+W; the other lanes get theirs by DPP.
 // ---------------------------------------------------------------------------
 template <typename T, bool HAS_B>
-__device__ __forceinline__ Vec<T> stencil(const Vec<T>& s, const Vec<T>& m, const Vec<T>& n,
-                                          const Vec<T>& b, T edge, int col, int nx) {
+__device__ __forceinline__ Vec<T> stencil_we(const Vec<T>& s, const Vec<T>& m, const Vec<T>& n,
+                                             const Vec<T>& b, T west_of_first, T east_of_last,
+                                             int col, int nx) {
     constexpr int W = VecW<T>::W;
-    const T west_of_first = from_lower(edge, m.v[W - 1]);
-    const T east_of_last = from_upper(edge, m.v[0]);
     Vec<T> o;
 #pragma unroll
     for (int k = 0; k < W; ++k) {
@@ -105,6 +105,16 @@ __device__ __forceinline__ Vec<T> stencil(const Vec<T>& s, const Vec<T>& m, cons
         o.v[k] = ring ? m.v[k] : T(0.25) * t;
     }
     return o;
+}
+
+// W/E neighbours of the end elements passed in (stencil_we) or taken by DPP
+// from the adjacent lanes (stencil).
+template <typename T, bool HAS_B>
+__device__ __forceinline__ Vec<T> stencil(const Vec<T>& s, const Vec<T>& m, const Vec<T>& n,
+                                          const Vec<T>& b, T edge, int col, int nx) {
+    constexpr int W = VecW<T>::W;
+    return stencil_we<T, HAS_B>(s, m, n, b, from_lower(edge, m.v[W - 1]), from_upper(edge, m.v[0]),
+                                col, nx);
 }
 
 // rho^2 summed over the interior nodes of one vector, in double:
@@ -168,6 +178,7 @@ struct BarrierCtx {
     uint32_t xg;         // XCD barrier: this block's XCD
     uint32_t xmembers;   // XCD barrier: blocks on this XCD
     uint32_t xgroups;    // XCD barrier: XCDs with at least one block
+    uint32_t nbr_epoch;  // neighbour exchanges completed (identical in every block)
 };
 
 // Lane 0 spins until *gen reaches `target` (relaxed loads, bounded in time).
@@ -238,6 +249,28 @@ __device__ __forceinline__ void xcd_barrier(BarrierCtx& bc) {
     __syncthreads();
 }
 
+// Point-to-point halo sync between the blocks of neighbouring bands. Every
+// wave waits for its own stores (the edge rows just published), the block
+// meets, and thread 0 publishes the new exchange count on the block's flag
+// with agent-scope release, then acquires the flags of logical blocks lb-1 and
+// lb+1 (bounded spin). Blocks meet only their neighbours ("Persistent
+// Kernels", "Reflections and next steps", GPU-side scheduling).
+__device__ __forceinline__ void neighbor_sync(BarrierCtx& bc, uint32_t* nbr, int lb) {
+    wait_vm();
+    __syncthreads();
+    const uint32_t target = bc.nbr_epoch + 1;
+    if (threadIdx.x == 0 && !bc.faulted) {
+        __hip_atomic_store(nbr + static_cast<size_t>(lb) * PK_NBR_WORDS, target, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (lb > 0) spin_until(bc, nbr + static_cast<size_t>(lb - 1) * PK_NBR_WORDS, target);
+        if (lb + 1 < static_cast<int>(bc.grid))
+            spin_until(bc, nbr + static_cast<size_t>(lb + 1) * PK_NBR_WORDS, target);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    bc.nbr_epoch = target;
+    __syncthreads();
+}
+
 __device__ __forceinline__ void grid_barrier(BarrierCtx& bc, bool relaxed = false) {
     if (bc.xcd && !relaxed && bc.grid > 1) {
         xcd_barrier(bc);
@@ -283,6 +316,13 @@ __device__ __forceinline__ void grid_barrier(BarrierCtx& bc, bool relaxed = fals
 // Hardware dispatch places block b on XCD (b mod 8). With remapping, logical
 // block numbers [x*G/8, (x+1)*G/8) all live on XCD x, so neighbouring work
 // (and the halo rows it shares) stays inside one XCD's L2.
+// Wave index in the block, in a scalar register: the compiler's divergence
+// analysis treats threadIdx.x >> 6 as per-lane, which would put every loop
+// driven by it into vector registers under exec masks.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+}
+
 __device__ __forceinline__ int logical_block(int remap, int grid) {
     const int b = static_cast<int>(blockIdx.x);
     if (!remap) return b;
@@ -295,7 +335,7 @@ __device__ __forceinline__ int logical_block(int remap, int grid) {
 // work even when there are fewer units than waves, and consecutive units sit on
 // consecutive logical blocks, i.e. on one XCD.
 __device__ __forceinline__ int unit_wave(const pk_kargs& a) {
-    return (static_cast<int>(threadIdx.x) >> 6) * a.grid + logical_block(a.xcd_remap, a.grid);
+    return wave_id() * a.grid + logical_block(a.xcd_remap, a.grid);
 }
 
 // ---------------------------------------------------------------------------
@@ -453,14 +493,14 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
 // starting at c0 + ov * W. Results equal K single sweeps bit for bit: every
 // stored value is the same expression on the same operands.
 // ---------------------------------------------------------------------------
-template <typename T, bool HAS_B, int K>
+template <typename T, bool HAS_B, int K, int DIR>
 __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* __restrict__ dst,
                                                  const T* __restrict__ bsrc, int nx, int ny,
-                                                 int pitch, int c0, int ov, int r0, int r1,
-                                                 int dir) {
+                                                 int pitch, int c0, int ov, int r0, int r1) {
+    constexpr int dir = DIR;
     constexpr int W = VecW<T>::W;
     // rows of loads issued ahead; fewer for deep passes (registers hold K windows)
-    constexpr int CH = (HAS_B || (K >= 3 && sizeof(T) == 8)) ? 2 : 4;
+    constexpr int CH = (HAS_B || K >= 3) ? 2 : 4;
     const int lane = threadIdx.x & 63;
     const int col = c0 + lane * W;
     const bool act = col >= 0 && col < nx;
@@ -542,8 +582,12 @@ __device__ __forceinline__ void stream_pass_k(const pk_kargs& a, const T* __rest
         const int r0 = 1 + band * a.pband_rows;
         const int r1 = min(a.ny - 1, r0 + a.pband_rows);
         if (r0 >= r1) continue;
-        stream_pass_unit<T, HAS_B, K>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W, ov,
-                                      r0, r1, (band & 1) ? -1 : 1);
+        if (band & 1)
+            stream_pass_unit<T, HAS_B, K, -1>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W,
+                                              ov, r0, r1);
+        else
+            stream_pass_unit<T, HAS_B, K, 1>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W,
+                                             ov, r0, r1);
     }
 }
 
@@ -594,36 +638,107 @@ __device__ __forceinline__ double sum_partials(const double* partials, int grid)
 }
 
 // ---------------------------------------------------------------------------
-// LDS-resident sweep rows: compute LDS rows [lo, hi) of D from S (both with
-// row stride lp elements, nv = lp / W vectors per row). Consecutive lanes hold
-// consecutive vectors in row-major order, so the DPP shifts give W/E inside a
-// wave; lanes 0 and 63 read their outside neighbour from LDS. Where a lane's
-// shifted-in neighbour belongs to another row it always lands on a ring or
-// padding column, which keeps its value.
+// LDS-resident sweep rows.
+//
+// A row of the tile holds nv = lp / W vectors. Work goes out per wave in items
+// of 64 lanes: a row narrower than 64 vectors shares an item with 64 / sw - 1
+// others (sw = the power of two >= nv), a wider row is cut into segs segments
+// of 64 vectors. Each wave keeps one segment for the whole task (segs <= waves
+// per block) and walks the row groups with a stride, so a lane's column, its
+// ring mask and whether it reads an edge neighbour from LDS are fixed per task.
+//
+// All of this is set up once per task (TileMap): the CU's scalar unit is
+// shared by all its waves, so scalar set-up repeated per sub-sweep by every
+// wave costs as much as the stencil itself on small tiles.
 // ---------------------------------------------------------------------------
+template <typename T>
+struct TileMap {
+    static constexpr int W = VecW<T>::W;
+    int nv, lp, nx;
+    int lsw;       // log2 of the lanes per row within an item (<= 6)
+    int lrpi;      // log2 of the rows per item (6 - lsw)
+    int segs;      // segments per row
+    int seg0;      // this wave's first segment
+    int seg_step;  // next segment of this wave (more segments than waves only)
+    int g0, g_step;  // this wave's first row group and group stride
+    bool active;   // the wave has work
+    int sub;       // this lane's row within an item
+    int lsub;      // this lane's vector within its row segment
+};
+
+template <typename T>
+__device__ __forceinline__ TileMap<T> tile_map(int nv, int lp, int nx) {
+    TileMap<T> t;
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int wave = wave_id();
+    const int nwv = static_cast<int>(blockDim.x) >> 6;
+    int lsw = 0;
+    while ((1 << lsw) < nv && lsw < 6) ++lsw;
+    t.nv = nv;
+    t.lp = lp;
+    t.nx = nx;
+    t.lsw = lsw;
+    t.lrpi = 6 - lsw;
+    t.segs = (nv + (1 << lsw) - 1) >> lsw;
+    const int per = t.segs < nwv ? t.segs : nwv;  // segments handled at once
+    const int wps = nwv / per;                    // waves per segment
+    t.active = wave < wps * per;
+    t.seg0 = wave % t.segs;
+    t.seg_step = per;
+    t.g0 = wave / t.segs;
+    t.g_step = wps;
+    t.sub = lane >> lsw;
+    t.lsub = lane & ((1 << lsw) - 1);
+    return t;
+}
+
+// Rows [lo, hi) of D from S (LDS row stride lp elements; Bt holds b).
 template <typename T, bool HAS_B>
-__device__ __forceinline__ void resident_rows(const T* S, T* D, const T* Bt, int lo, int hi, int nv,
-                                              int lp, int nx) {
+__device__ __forceinline__ void resident_rows(const T* S, T* D, const T* Bt, int lo, int hi,
+                                              const TileMap<T>& t) {
     constexpr int W = VecW<T>::W;
-    const int lane = threadIdx.x & 63;
-    const int total = (hi - lo) * nv;
-    for (int base = static_cast<int>(threadIdx.x) - lane; base < total;
-         base += static_cast<int>(blockDim.x)) {
-        const int idx = base + lane;
-        const bool act = idx < total;
-        const int id = act ? idx : total - 1;
-        const int rr = lo + id / nv;
-        const int col = (id % nv) * W;
-        const T* p = S + rr * lp + col;
-        const Vec<T> m = vload(p);
-        const Vec<T> s = vload(p - lp);
-        const Vec<T> n = vload(p + lp);
-        const Vec<T> bb = HAS_B ? vload(Bt + rr * lp + col) : vzero<T>();
-        T edge = T(0);
-        if (lane == 0 && col > 0) edge = p[-1];
-        if (lane == 63 && col + W < lp) edge = p[W];
-        const Vec<T> o = stencil<T, HAS_B>(s, m, n, bb, edge, col, nx);
-        if (act) vstore(D + rr * lp + col, o);
+    if (!t.active) return;
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int lp = t.lp;
+    const int groups = (hi - lo + (1 << t.lrpi) - 1) >> t.lrpi;
+    for (int seg = t.seg0; seg < t.segs; seg += t.seg_step) {
+        const int v = (seg << t.lsw) + t.lsub;
+        const bool vact = v < t.nv;
+        const int col = (vact ? v : (seg << t.lsw)) * W;
+        // a lane's W/E neighbour comes by DPP from the adjacent lane; the lanes
+        // at the ends of a 64-wide segment read it from LDS unless it can only
+        // reach a ring or padding column (rows of one segment never need it)
+        const bool need_w = lane == 0 && col > 0;
+        const bool need_e = lane == 63 && col + W < lp;
+        bool keep[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) keep[k] = (col + k == 0) || (col + k >= t.nx - 1);
+        for (int g = t.g0; g < groups; g += t.g_step) {
+            const int r = lo + (g << t.lrpi) + t.sub;
+            const bool act = vact && r < hi;
+            const int rr = r < hi ? r : hi - 1;
+            const int o0 = rr * lp + col;
+            const T* p = S + o0;
+            const Vec<T> m = vload(p);
+            const Vec<T> s = vload(p - lp);
+            const Vec<T> n = vload(p + lp);
+            const Vec<T> bb = HAS_B ? vload(Bt + o0) : vzero<T>();
+            T ew = T(0), ee = T(0);
+            if (need_w) ew = p[-1];
+            if (need_e) ee = p[W];
+            const T west = from_lower(ew, m.v[W - 1]);
+            const T east = from_upper(ee, m.v[0]);
+            Vec<T> o;
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                const T w = (k == 0) ? west : m.v[k - 1];
+                const T e = (k == W - 1) ? east : m.v[k + 1];
+                T x = (w + e) + (s.v[k] + n.v[k]);
+                if (HAS_B) x = x + bb.v[k];
+                o.v[k] = keep[k] ? m.v[k] : T(0.25) * x;
+            }
+            if (act) vstore(D + o0, o);
+        }
     }
 }
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <chrono>
 #include <cstdio>
@@ -27,10 +28,12 @@ struct Plan {
     int threads = 1024;
     int grid = 1;
     int strips = 1, bands = 1, band_rows = 1;
-    int res_band_rows = 0, res_halo = 0, res_ext_rows = 0, lds_pitch = 0;
+    int res_q = 0, res_rem = 0, res_halo = 0, res_ext_rows = 0, lds_pitch = 0;
+    int reg_cw = 1, reg_rows = 0;
     size_t lds_bytes = 0;
     int xcd_remap = 0;
     int barrier_kind = PK_BARRIER_FLAT;
+    int exchange = 0;  // RESIDENT: PK_EXCHANGE_BARRIER or PK_EXCHANGE_NEIGHBOR
     int pass_sweeps = 1;
     int pband_rows = 1, pbands = 1;
     int occ = 0;  // blocks per CU allowed by the occupancy query
@@ -68,6 +71,7 @@ struct pk_engine {
     pk_dev_state* d_st = nullptr;
     double* d_partials = nullptr;
     uint32_t* d_stamp = nullptr;
+    uint32_t* d_nbr = nullptr;
     pk_mailbox* h_mail = nullptr;
     pk_mailbox* d_mail = nullptr;
     void* h_staging = nullptr;
@@ -118,11 +122,148 @@ void release(pk_engine* e) {
     if (e->d_st) (void)hipFree(e->d_st);
     if (e->d_partials) (void)hipFree(e->d_partials);
     if (e->d_stamp) (void)hipFree(e->d_stamp);
+    if (e->d_nbr) (void)hipFree(e->d_nbr);
     if (e->h_mail) (void)hipHostFree(e->h_mail);
     if (e->h_staging) (void)hipHostFree(e->h_staging);
     if (e->h_lres) (void)hipHostFree(e->h_lres);
     if (e->own_stream && e->stream) (void)hipStreamDestroy(e->stream);
     delete e;
+}
+
+// ---------------------------------------------------------------------------
+// Planning of the tile layouts (RESIDENT in LDS, REGISTER in VGPRs): one band of
+// interior rows per block, bands of q or q+1 rows, halo depth m <= q (a block's
+// halo rows come from its neighbours' bands), tile height ext = band + 2m.
+// Estimated time per sweep = sub-sweep + exchange / m, with costs fitted to
+// measurements on MI355X (one block of 16 waves per CU):
+//   LDS sub-sweep: 0.37 us + 0.19 us per work item (a 64-lane row segment)
+//     per wave, over the rows of an average sub-sweep (band + m - 1);
+//   exchange with the grid barrier:   2.5 us + 0.046 us per KB published + 0.0064 us per block;
+//   exchange with neighbour flags:    1.4 us + 0.069 us per KB published + 0.015 us per block
+//     (every block writes its XCD's L2 back on its own, so this grows faster with blocks).
+// The register tile keeps its own rough estimate (~25 ns per register row).
+// ---------------------------------------------------------------------------
+struct TilePlan {
+    int g = 0, q = 0, rem = 0, m = 0, ext = 0, rows = 0, cw = 1;
+    int exchange = PK_EXCHANGE_BARRIER;
+    size_t lds = 0;
+    double cost = 1e30;
+};
+
+double barrier_estimate_us(int g) {
+    if (g <= 1) return 0.2;
+    if (g < 16) return 1.4;
+    return 1.6 + 0.0078 * g;
+}
+
+double exchange_estimate_us(int exchange, int g, double kb) {
+    return exchange == PK_EXCHANGE_NEIGHBOR ? 1.4 + 0.069 * kb + 0.015 * g
+                                            : 2.5 + 0.046 * kb + 0.0064 * g;
+}
+
+constexpr int kRegRows = 8;  // rows per wave held in registers (PK_REG_RMAX)
+constexpr int kRegThreads = 512;  // block size of the register-tile kernel
+
+// One candidate block count g for the LDS (register == false) or register tile.
+// `exchanges` lists the exchange kinds to consider (LDS tile only).
+TilePlan tile_candidate(int nx, int ny, int esize, bool has_b, int nwv, size_t lds_max, int g,
+                        int want_m, bool register_tile, int exchanges) {
+    TilePlan t;
+    const int W = 16 / esize;
+    const int interior = ny - 2;
+    if (g < 1 || g > interior) return t;
+    const int q = interior / g, rem = interior % g;
+    const int band_max = q + (rem ? 1 : 0);
+    const int nvec = (nx + W - 1) / W;
+    const int lp = nvec * W;
+    int m_hi = g == 1 ? (1 << 20) : q;
+    if (want_m > 0) m_hi = std::min(m_hi, want_m);
+    auto ext_of = [&](int m) { return g == 1 ? ny : std::min(ny, band_max + 2 * m); };
+    t.g = g;
+    t.q = q;
+    t.rem = rem;
+    if (register_tile) {
+        int m = 0, rows = 0;
+        const int cw = (nvec + 63) / 64;
+        if (cw > nwv) return TilePlan{};
+        const int rw = nwv / cw;
+        // deepest halo whose tile fits in kRegRows rows per wave; the kernel holds
+        // a power of two of rows per wave (2, 4 or 8)
+        for (int mm = std::min(m_hi, ny); mm >= 1; --mm) {
+            const int r = (ext_of(mm) + rw - 1) / rw;
+            if (r <= kRegRows) {
+                m = mm;
+                rows = 2;
+                while (rows < r) rows *= 2;
+                break;
+            }
+        }
+        if (m == 0) return TilePlan{};
+        if (g == 1) m = 1 << 20;
+        size_t lds = static_cast<size_t>(2) * nwv * (2 * 64 * W + 2 * kRegRows) * esize;
+        if (has_b) lds += static_cast<size_t>(ext_of(m == (1 << 20) ? ny : m)) * lp * esize;
+        if (lds > lds_max) return TilePlan{};
+        t.m = m;
+        t.ext = ext_of(m);
+        t.rows = rows;
+        t.cw = cw;
+        t.lds = lds;
+        const double exchange = barrier_estimate_us(g) + (g > 1 ? 1.0 : 0.0);
+        t.cost = (g == 1 ? 0.0 : exchange / m) + 0.10 + 0.025 * rows;
+        return t;
+    }
+    const size_t row_bytes = static_cast<size_t>(lp) * esize * (has_b ? 3 : 2);
+    const int max_rows = static_cast<int>(lds_max / row_bytes);
+    if (ext_of(1) > max_rows && !(g == 1 && ny <= max_rows)) return TilePlan{};
+    // work items per row: rows narrower than 64 vectors share a wave
+    int sw = 1;
+    while (sw < nvec && sw < 64) sw *= 2;
+    const int rpi = 64 / sw;
+    const int segs = (nvec + sw - 1) / sw;
+    auto sub_us = [&](double rows) {
+        const double items = std::ceil(rows / rpi) * segs;
+        return 0.37 + 0.19 * items / nwv;
+    };
+    if (g == 1) {
+        if (ny > max_rows) return TilePlan{};
+        t.m = 1 << 20;
+        t.ext = ny;
+        t.lds = static_cast<size_t>(ny) * row_bytes;
+        t.cost = sub_us(interior);
+        return t;
+    }
+    for (int m = 1; m <= std::min(m_hi, ny); ++m) {
+        if (ext_of(m) > max_rows) break;
+        const double kb = 2.0 * m * lp * esize / 1024.0;
+        for (int x = PK_EXCHANGE_BARRIER; x <= PK_EXCHANGE_NEIGHBOR; ++x) {
+            if (!(exchanges & (1 << x))) continue;
+            const double c = sub_us(band_max + m - 1.0) + exchange_estimate_us(x, g, kb) / m;
+            if (c < t.cost) {
+                t.cost = c;
+                t.m = m;
+                t.exchange = x;
+            }
+        }
+    }
+    if (t.m == 0) return TilePlan{};
+    t.ext = ext_of(t.m);
+    t.lds = static_cast<size_t>(t.ext) * row_bytes;
+    return t;
+}
+
+// Best tile plan over block counts (or the given one).
+TilePlan best_tile(int nx, int ny, int esize, bool has_b, int nwv, size_t lds_max, int cus,
+                   int want_g, int want_m, bool register_tile, int exchanges) {
+    TilePlan best;
+    const int interior = ny - 2;
+    const int lo = want_g > 0 ? want_g : 1;
+    const int hi = want_g > 0 ? want_g : std::min(cus, interior);
+    for (int g = lo; g <= hi; ++g) {
+        const TilePlan t = tile_candidate(nx, ny, esize, has_b, nwv, lds_max, g, want_m, register_tile,
+                                          exchanges);
+        if (t.g && t.cost < best.cost) best = t;
+    }
+    return best;
 }
 
 // Choose layout, block size and grid. Both modes share the result, so the
@@ -134,53 +275,45 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     const int W = 16 / e->esize;
     const int interior = e->ny - 2;
     const size_t lds_max = prop.sharedMemPerBlock > 1024 ? prop.sharedMemPerBlock - 1024 : 0;
+    const int nwv = p.threads / 64;
 
-    bool resident = false;
+    bool tiled = false;
     if (e->mode == PK_PERSISTENT && o.layout != PK_LAYOUT_STREAM) {
-        const int lp = static_cast<int>(round_up(static_cast<size_t>(e->nx), W));
-        const size_t row_bytes = static_cast<size_t>(lp) * e->esize * (e->has_b ? 3 : 2);
-        const int max_rows = static_cast<int>(lds_max / row_bytes);
-        int g = 0, band = 0, m = 0;
-        if (max_rows >= e->ny && (o.max_blocks == 0 || o.max_blocks == 1)) {
-            g = 1;                          // the whole field lives in one block's LDS
-            band = interior;
-            m = 1 << 20;                    // no neighbours: one period per task
-        } else if (max_rows >= 3) {
-            const int gmax = std::min(e->cus, interior);
-            if (o.max_blocks > 0) {
-                g = std::min(o.max_blocks, gmax);
-                band = ceil_div(interior, g);
-                m = o.halo_depth > 0 ? o.halo_depth : 8;
-                m = std::min(m, (max_rows - band) / 2);
-            } else {
-                m = o.halo_depth > 0 ? o.halo_depth : 8;
-                m = std::min(m, max_rows / 3);
-                band = max_rows - 2 * m;
-                g = ceil_div(interior, band);
-                if (g > gmax) { g = 0; }
-            }
-            if (g > 0) {
-                band = ceil_div(interior, g);
-                g = ceil_div(interior, band);
-                const int last = interior - (g - 1) * band;
-                m = std::min({m, band, last});
-                if (band + 2 * m > max_rows || m < 1) g = 0;
-            }
-        }
-        if (g > 0) {
-            p.layout = PK_LAYOUT_RESIDENT;
-            p.grid = g;
-            p.res_band_rows = band;
-            p.res_halo = m;
-            p.res_ext_rows = std::min(e->ny, band + 2 * std::min(m, e->ny));
-            p.lds_pitch = lp;
-            p.lds_bytes = static_cast<size_t>(p.res_ext_rows) * lp * e->esize * (e->has_b ? 3 : 2);
-            resident = true;
-        } else if (o.layout == PK_LAYOUT_RESIDENT) {
-            return PK_EINVAL;  // asked for, but the bands do not fit in LDS
+        TilePlan reg, lds;
+        // exchange kinds the LDS tile may use (bit per PK_EXCHANGE_* value)
+        const int exchanges = o.exchange != PK_EXCHANGE_AUTO ? (1 << o.exchange)
+                              : (o.flags & PK_DBG_BROKEN_BARRIER) ? (1 << PK_EXCHANGE_BARRIER)
+                              : ((1 << PK_EXCHANGE_BARRIER) | (1 << PK_EXCHANGE_NEIGHBOR));
+        const int reg_threads = std::min(p.threads, kRegThreads);
+        // the register tile is taken only on request: on MI355X it has not beaten
+        // the LDS tile at any measured size
+        if (o.layout == PK_LAYOUT_REGISTER)
+            reg = best_tile(e->nx, e->ny, e->esize, e->has_b, reg_threads / 64, lds_max, e->cus,
+                            o.max_blocks, o.halo_depth, true, 0);
+        if (o.layout == PK_LAYOUT_AUTO || o.layout == PK_LAYOUT_RESIDENT)
+            lds = best_tile(e->nx, e->ny, e->esize, e->has_b, nwv, lds_max, e->cus, o.max_blocks,
+                            o.halo_depth, false, exchanges);
+        const bool use_reg = reg.g && (!lds.g || reg.cost <= lds.cost);
+        const TilePlan& t = use_reg ? reg : lds;
+        if (t.g) {
+            p.layout = use_reg ? PK_LAYOUT_REGISTER : PK_LAYOUT_RESIDENT;
+            if (use_reg) p.threads = reg_threads;
+            p.grid = t.g;
+            p.res_q = t.q;
+            p.res_rem = t.rem;
+            p.res_halo = t.m;
+            p.res_ext_rows = t.ext;
+            p.reg_cw = t.cw;
+            p.reg_rows = t.rows;
+            p.lds_pitch = static_cast<int>(round_up(static_cast<size_t>(e->nx), W));
+            p.lds_bytes = t.lds;
+            p.exchange = use_reg ? 0 : t.exchange;
+            tiled = true;
+        } else if (o.layout == PK_LAYOUT_RESIDENT || o.layout == PK_LAYOUT_REGISTER) {
+            return PK_EINVAL;  // asked for, but the bands do not fit
         }
     }
-    if (!resident) {
+    if (!tiled) {
         p.layout = PK_LAYOUT_STREAM;
         const int wpb = p.threads / 64;
         // enough blocks for one wave per unit of >= 4 rows, at most one block per CU
@@ -197,9 +330,11 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     stream_geometry(p, e->nx, e->ny, e->esize, 4);
     // passes of k sweeps (stream layout, persistent only): about one unit per
     // wave, bands at least 4 k rows tall (each band re-reads 2 k halo rows)
+    // default: the deepest pass the kernel carries (4 levels, 3 with a source
+    // term); measured fastest on 4096^2 fp32 and 8192^2 fp64
     p.pass_sweeps = 1;
     if (e->mode == PK_PERSISTENT && p.layout == PK_LAYOUT_STREAM)
-        p.pass_sweeps = o.pass_sweeps > 0 ? o.pass_sweeps : 2;
+        p.pass_sweeps = o.pass_sweeps > 0 ? o.pass_sweeps : PK_MAX_PASS;
     // with a source term the kernel carries a window of b rows too: at most 3
     if (e->has_b && p.pass_sweeps > 3) p.pass_sweeps = 3;
     {
@@ -249,7 +384,10 @@ void fill_kargs(pk_engine* e) {
     a.strips = p.strips;
     a.bands = p.bands;
     a.band_rows = p.band_rows;
-    a.res_band_rows = p.res_band_rows;
+    a.res_q = p.res_q;
+    a.res_rem = p.res_rem;
+    a.reg_cw = p.reg_cw;
+    a.reg_rows = p.reg_rows;
     a.res_halo = p.res_halo;
     a.res_ext_rows = p.res_ext_rows;
     a.lds_pitch = p.lds_pitch;
@@ -266,6 +404,8 @@ void fill_kargs(pk_engine* e) {
     a.partials = e->d_partials;
     a.staging = e->d_staging;
     a.stamp = e->d_stamp;
+    a.nbr = e->d_nbr;
+    a.exchange = p.exchange;
 }
 
 bool poll_exited(void* ctx) {
@@ -307,7 +447,7 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     else pk_opts_default(&o);
     if (o.dtype != PK_F32 && o.dtype != PK_F64) return PK_EINVAL;
     if (o.mode != PK_PERSISTENT && o.mode != PK_LAUNCH) return PK_EINVAL;
-    if (o.layout < PK_LAYOUT_AUTO || o.layout > PK_LAYOUT_RESIDENT) return PK_EINVAL;
+    if (o.layout < PK_LAYOUT_AUTO || o.layout > PK_LAYOUT_REGISTER) return PK_EINVAL;
     if (o.threads != 0 && (o.threads < 64 || o.threads > 1024 || o.threads % 64 != 0)) return PK_EINVAL;
     if (o.max_blocks < 0 || o.halo_depth < 0 || o.idle_timeout_s < 0) return PK_EINVAL;
     if (o.pass_sweeps < 0 || o.pass_sweeps > PK_MAX_PASS || o.band_rows < 0) return PK_EINVAL;
@@ -316,6 +456,9 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     // the negative control relaxes the flat/two-level barriers; the XCD barrier keeps
     // separate counters, so the two are not combined
     if ((o.flags & PK_DBG_BROKEN_BARRIER) && o.barrier == PK_BARRIER_XCD) return PK_EINVAL;
+    if (o.exchange < PK_EXCHANGE_AUTO || o.exchange > PK_EXCHANGE_NEIGHBOR) return PK_EINVAL;
+    // the negative control weakens the grid barrier only
+    if ((o.flags & PK_DBG_BROKEN_BARRIER) && o.exchange == PK_EXCHANGE_NEIGHBOR) return PK_EINVAL;
     for (int r : o.reserved)
         if (r != 0) return PK_EINVAL;
     double h = o.h;
@@ -392,6 +535,9 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_partials), sizeof(double) * e->plan.grid));
     PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_stamp), sizeof(uint32_t) * 2 * 64 * e->plan.grid));
     PK_TRY(hipMemsetAsync(e->d_stamp, 0, sizeof(uint32_t) * 2 * 64 * e->plan.grid, e->stream));
+    const size_t nbr_bytes = sizeof(uint32_t) * PK_NBR_WORDS * e->plan.grid;
+    PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_nbr), nbr_bytes));
+    PK_TRY(hipMemsetAsync(e->d_nbr, 0, nbr_bytes, e->stream));
     PK_TRY(hipHostMalloc(reinterpret_cast<void**>(&e->h_mail), sizeof(pk_mailbox),
                          hipHostMallocCoherent | hipHostMallocMapped));
     std::memset(e->h_mail, 0, sizeof(pk_mailbox));
@@ -603,13 +749,15 @@ int pk_get_info(pk_engine* e, pk_info* info) {
     info->threads = e->plan.threads;
     info->blocks_per_cu_max = e->plan.occ;
     info->cus = e->cus;
-    info->halo_depth = e->plan.layout == PK_LAYOUT_RESIDENT ? e->plan.res_halo : 0;
-    info->band_rows = e->plan.layout == PK_LAYOUT_RESIDENT ? e->plan.res_band_rows
+    const bool tiled = e->plan.layout == PK_LAYOUT_RESIDENT || e->plan.layout == PK_LAYOUT_REGISTER;
+    info->halo_depth = tiled ? e->plan.res_halo : 0;
+    info->band_rows = tiled ? e->plan.res_q + (e->plan.res_rem ? 1 : 0)
                       : (e->plan.pass_sweeps > 1 ? e->plan.pband_rows : e->plan.band_rows);
     info->strips = e->plan.strips;
     info->lds_bytes = e->plan.lds_bytes;
     info->barrier = e->plan.barrier_kind;
     info->pass_sweeps = e->plan.pass_sweeps;
+    info->exchange = e->plan.exchange;
     info->kernel_launches = e->launches;
     if (e->mode == PK_PERSISTENT) {
         info->sweeps_done = e->ring.sweeps_seen();

@@ -13,6 +13,169 @@ using namespace pkd;
 
 namespace {
 
+// Interior rows of band L when the interior is split into `grid` bands of
+// q or q+1 rows (the first `rem` bands get the extra row).
+__device__ __forceinline__ int band_begin(const pk_kargs& a, int L) {
+    return 1 + L * a.res_q + min(L, a.res_rem);
+}
+
+// ---------------------------------------------------------------------------
+// Register-tile SWEEP task (PK_LAYOUT_REGISTER). Same band / halo / publish /
+// barrier protocol as the LDS-resident task below, but each block keeps its
+// rows [r0 - m, r1 + m) in VGPRs: the waves form cw column groups (64 lanes x
+// W columns each) times rw row groups, and a lane holds one 16-byte vector for
+// each of its R rows. A sub-sweep updates those rows in place in registers;
+// W/E come from DPP lane shifts, and only what crosses a wave boundary goes
+// through LDS: each wave's first and last row, and its first and last column.
+// Every row of the tile is recomputed each sub-sweep; values that depend on
+// the zero fill beyond the tile spread one row per sub-sweep and never reach
+// the owned rows within a period of m <= (halo) sub-sweeps. Ring rows and
+// columns keep their values.
+// ---------------------------------------------------------------------------
+constexpr int PK_REG_RMAX = 8;  // rows per wave; the layout runs 512-thread blocks
+
+// Exchange slot of one wave for one sub-sweep parity: its first row, its last
+// row, its first column (element 0 of lane 0, one per row) and its last column
+// (element W-1 of lane 63). Columns are stored contiguously so a consumer lane
+// reads them with 16-byte LDS loads.
+template <typename T>
+struct RegSlot {
+    static constexpr int W = VecW<T>::W;
+    static constexpr int size = 2 * 64 * W + 2 * PK_REG_RMAX;
+    static constexpr int top = 0, bottom = 64 * W, first_col = 2 * 64 * W,
+                         last_col = 2 * 64 * W + PK_REG_RMAX;
+};
+
+template <typename T, bool HAS_B, int RT>
+__device__ void reg_sweep_rows(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
+    constexpr int W = VecW<T>::W;
+    using S = RegSlot<T>;
+    const int lb = logical_block(a.xcd_remap, a.grid);
+    const int ny = a.ny, nx = a.nx;
+    const int r0 = band_begin(a, lb), r1 = band_begin(a, lb + 1);
+    const int m = a.res_halo;
+    const int e0 = max(0, r0 - m), e1 = min(ny, r1 + m);
+    const int nwv = static_cast<int>(blockDim.x) >> 6;
+    const int wave = wave_id(), lane = static_cast<int>(threadIdx.x) & 63;
+    const int cw = a.reg_cw;
+    const int rw = nwv / cw;
+    const int cg = wave % cw, rg = wave / cw;
+    const bool wave_live = rg < rw;  // wave-uniform
+    const int col = (cg * 64 + lane) * W;
+    const bool lane_live = wave_live && col < nx;
+    const int row_base = e0 + rg * RT;
+    const size_t p = static_cast<size_t>(a.pitch);
+    const int lp = a.lds_pitch;
+    T* lds_b = lds + static_cast<size_t>(2 * nwv) * S::size;
+    const bool has_left = cg > 0, has_right = cg + 1 < cw;  // wave-uniform
+
+    Vec<T> u[RT];
+    {
+        const T* g = static_cast<const T*>(a.u[cur]);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int row = row_base + r;
+            u[r] = (lane_live && row < e1) ? vload(g + static_cast<size_t>(row) * p + col) : vzero<T>();
+        }
+        if (HAS_B) {
+            const T* gb = static_cast<const T*>(a.b);
+            const int nv = lp / W;
+            const int tot = (e1 - e0) * nv;
+            for (int idx = static_cast<int>(threadIdx.x); idx < tot; idx += static_cast<int>(blockDim.x)) {
+                const int rr = idx / nv, c = (idx % nv) * W;
+                vstore(lds_b + rr * lp + c, vload(gb + static_cast<size_t>(e0 + rr) * p + c));
+            }
+        }
+    }
+    int par = 0;
+    int remaining = n;
+    while (remaining > 0) {
+        const int sc = min(m, remaining);
+        for (int s = 0; s < sc; ++s) {
+            T* base = lds + static_cast<size_t>(par * nwv) * S::size;
+            T* mine = base + static_cast<size_t>(wave) * S::size;
+            if (wave_live) {
+                vstore(mine + S::top + lane * W, u[0]);
+                vstore(mine + S::bottom + lane * W, u[RT - 1]);
+                if (lane == 0) {
+#pragma unroll
+                    for (int r = 0; r < RT; ++r) mine[S::first_col + r] = u[r].v[0];
+                }
+                if (lane == 63) {
+#pragma unroll
+                    for (int r = 0; r < RT; ++r) mine[S::last_col + r] = u[r].v[W - 1];
+                }
+            }
+            __syncthreads();
+            if (wave_live) {
+                const Vec<T> above = rg > 0 ? vload(base + static_cast<size_t>(wave - cw) * S::size + S::bottom + lane * W)
+                                            : vzero<T>();
+                const Vec<T> below = rg + 1 < rw ? vload(base + static_cast<size_t>(wave + cw) * S::size + S::top + lane * W)
+                                                 : vzero<T>();
+                // outside neighbours of lanes 0 and 63 for every row
+                T edge[RT];
+#pragma unroll
+                for (int r = 0; r < RT; ++r) edge[r] = T(0);
+                if (lane == 0 && has_left) {
+                    const T* src = base + static_cast<size_t>(wave - 1) * S::size + S::last_col;
+#pragma unroll
+                    for (int r = 0; r < RT; ++r) edge[r] = src[r];
+                } else if (lane == 63 && has_right) {
+                    const T* src = base + static_cast<size_t>(wave + 1) * S::size + S::first_col;
+#pragma unroll
+                    for (int r = 0; r < RT; ++r) edge[r] = src[r];
+                }
+                Vec<T> prev = above;
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    const Vec<T> nxt = (r + 1 < RT) ? u[r + 1 < RT ? r + 1 : r] : below;
+                    const int row = row_base + r;
+                    Vec<T> bb = vzero<T>();
+                    if (HAS_B && row < e1) bb = vload(lds_b + (row - e0) * lp + col);
+                    const Vec<T> o = stencil<T, HAS_B>(prev, u[r], nxt, bb, edge[r], col, nx);
+                    prev = u[r];
+                    const bool keep = row <= 0 || row >= ny - 1 || row >= e1;  // wave-uniform
+                    if (!keep) u[r] = o;
+                }
+            }
+            par ^= 1;
+        }
+        remaining -= sc;
+        const int mn = min(m, remaining);
+        {   // publish edge rows for the neighbours, or every owned row at the end
+            T* g = static_cast<T*>(a.u[cur ^ 1]);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int row = row_base + r;
+                const bool own = row >= r0 && row < r1;
+                const bool need = remaining == 0 || (r0 > 1 && row < r0 + mn) || (r1 < ny - 1 && row >= r1 - mn);
+                if (lane_live && own && need) vstore(g + static_cast<size_t>(row) * p + col, u[r]);
+            }
+        }
+        grid_barrier(bc, bc.broken);
+        cur ^= 1;
+        if (remaining > 0) {  // the neighbours' edge rows become this block's halo
+            const T* g = static_cast<const T*>(a.u[cur]);
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int row = row_base + r;
+                const bool halo = (r0 > 1 && row >= r0 - mn && row < r0) || (r1 < ny - 1 && row >= r1 && row < r1 + mn);
+                if (lane_live && row < e1 && halo) u[r] = vload(g + static_cast<size_t>(row) * p + col);
+            }
+        }
+    }
+}
+
+// Rows per wave are a compile-time count (2, 4 or 8), chosen per engine.
+template <typename T, bool HAS_B>
+__device__ void reg_sweep_task(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
+    switch (a.reg_rows) {
+        case 2: reg_sweep_rows<T, HAS_B, 2>(a, n, cur, bc, lds); break;
+        case 4: reg_sweep_rows<T, HAS_B, 4>(a, n, cur, bc, lds); break;
+        default: reg_sweep_rows<T, HAS_B, 8>(a, n, cur, bc, lds); break;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // LDS-resident SWEEP task. Block (logical) L owns interior rows [r0, r1) and
 // keeps rows [r0 - m, r1 + m) in LDS (two ping-pong buffers, plus b). Each
@@ -31,8 +194,8 @@ __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierC
     constexpr int W = VecW<T>::W;
     const int lb = logical_block(a.xcd_remap, a.grid);
     const int ny = a.ny;
-    const int r0 = 1 + lb * a.res_band_rows;
-    const int r1 = min(ny - 1, r0 + a.res_band_rows);
+    const int r0 = band_begin(a, lb);
+    const int r1 = band_begin(a, lb + 1);
     const int m = a.res_halo;
     const int e0 = max(0, r0 - m);
     const int e1 = min(ny, r1 + m);
@@ -48,26 +211,43 @@ __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierC
         const T* g = static_cast<const T*>(a.u[cur]);
         const T* gb = static_cast<const T*>(a.b);
         const int tot = (e1 - e0) * nv;
-        for (int idx = tid; idx < tot; idx += nt) {
-            const int rr = idx / nv, col = (idx % nv) * W;
-            const size_t go = static_cast<size_t>(e0 + rr) * p + col;
-            const Vec<T> x = vload(g + go);
-            vstore(A + rr * lp + col, x);
-            vstore(B + rr * lp + col, x);
-            if (HAS_B) vstore(Bt + rr * lp + col, vload(gb + go));
+        constexpr int U = 4;  // loads in flight per thread
+        for (int base = tid; base < tot; base += U * nt) {
+            Vec<T> x[U], xb[U];
+            int dst[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int idx = base + u * nt;
+                dst[u] = -1;
+                if (idx < tot) {
+                    const int rr = idx / nv, col = (idx % nv) * W;
+                    const size_t go = static_cast<size_t>(e0 + rr) * p + col;
+                    x[u] = vload(g + go);
+                    if (HAS_B) xb[u] = vload(gb + go);
+                    dst[u] = rr * lp + col;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (dst[u] < 0) continue;
+                vstore(A + dst[u], x[u]);
+                vstore(B + dst[u], x[u]);
+                if (HAS_B) vstore(Bt + dst[u], xb[u]);
+            }
         }
     }
     __syncthreads();
 
     T* S = A;
     T* D = B;
+    const TileMap<T> tm = tile_map<T>(nv, lp, a.nx);
     int remaining = n;
     while (remaining > 0) {
         const int sc = min(m, remaining);
         for (int s = 1; s <= sc; ++s) {
             const int lo = (r0 == 1) ? 1 : r0 - (sc - s);
             const int hi = (r1 == ny - 1) ? ny - 1 : r1 + (sc - s);
-            resident_rows<T, HAS_B>(S, D, Bt, lo - e0, hi - e0, nv, lp, a.nx);
+            resident_rows<T, HAS_B>(S, D, Bt, lo - e0, hi - e0, tm);
             __syncthreads();
             T* t = S;
             S = D;
@@ -94,17 +274,37 @@ __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierC
                 vstore(g + static_cast<size_t>(rr) * p + col, vload(S + (rr - e0) * lp + col));
             }
         }
-        grid_barrier(bc, bc.broken);
+        if (remaining > 0 && a.exchange == PK_EXCHANGE_NEIGHBOR)
+            neighbor_sync(bc, a.nbr, lb);
+        else
+            grid_barrier(bc, bc.broken);
         cur ^= 1;
         if (remaining > 0) {  // the neighbours' edge rows become this block's halo
             const T* g = static_cast<const T*>(a.u[cur]);
             const int above = (r0 > 1) ? mn : 0;
             const int below = (r1 < ny - 1) ? mn : 0;
             const int tot = (above + below) * nv;
-            for (int idx = tid; idx < tot; idx += nt) {
-                const int k = idx / nv, col = (idx % nv) * W;
-                const int rr = (k < above) ? r0 - above + k : r1 + (k - above);
-                vstore(S + (rr - e0) * lp + col, vload(g + static_cast<size_t>(rr) * p + col));
+            // several loads in flight per thread before the LDS stores: each
+            // one is a trip to memory (the release/acquire pair of the
+            // barrier leaves these rows in no cache)
+            constexpr int U = 4;
+            for (int base = tid; base < tot; base += U * nt) {
+                Vec<T> x[U];
+                int dst[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int idx = base + u * nt;
+                    dst[u] = -1;
+                    if (idx < tot) {
+                        const int k = idx / nv, col = (idx % nv) * W;
+                        const int rr = (k < above) ? r0 - above + k : r1 + (k - above);
+                        x[u] = vload(g + static_cast<size_t>(rr) * p + col);
+                        dst[u] = (rr - e0) * lp + col;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (dst[u] >= 0) vstore(S + dst[u], x[u]);
             }
             __syncthreads();
         }
@@ -118,7 +318,7 @@ __device__ void readback_task(const pk_kargs& a, int cur) {
     T* h = static_cast<T*>(a.staging);
     const int lane = threadIdx.x & 63;
     const int wpb = static_cast<int>(blockDim.x) >> 6;
-    const int gw = static_cast<int>(blockIdx.x) * wpb + (static_cast<int>(threadIdx.x) >> 6);
+    const int gw = static_cast<int>(blockIdx.x) * wpb + wave_id();
     const int nw = a.grid * wpb;
     for (int r = gw; r < a.ny; r += nw) {
         const T* src = g + static_cast<size_t>(r) * a.pitch;
@@ -177,8 +377,15 @@ __device__ int64_t stamp_task(const pk_kargs& a, int n, uint32_t& round, Barrier
 // after the task's last barrier and released before `done_seq` moves, so the
 // host never sees "done" ahead of the work ("Reflections", point 3).
 // ---------------------------------------------------------------------------
+// Blocks of up to 1024 threads (128 VGPRs per lane); the register-tile layout
+// uses 512 so that each lane can hold 16 rows of u and b (256 VGPRs per lane).
+template <int LAYOUT>
+struct PkMaxThreads {
+    static constexpr int value = LAYOUT == PK_LAYOUT_REGISTER ? 512 : 1024;
+};
+
 template <typename T, bool HAS_B, int LAYOUT>
-__global__ void __launch_bounds__(1024) pk_persistent(pk_kargs a) {
+__global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_kargs a) {
     extern __shared__ __align__(16) unsigned char pk_lds[];
     __shared__ double s_red[16];
     __shared__ int s_kind, s_n, s_exit;
@@ -196,6 +403,7 @@ __global__ void __launch_bounds__(1024) pk_persistent(pk_kargs a) {
     bc.xg = 0;
     bc.xmembers = 1;
     bc.xgroups = 1;
+    bc.nbr_epoch = 0;
     if (a.barrier_kind == PK_BARRIER_XCD && a.grid > 1 && !bc.broken) {
         // count the blocks on each XCD (one flat barrier, generation 1), then
         // switch to the XCD barrier, whose counters start from zero
@@ -300,6 +508,8 @@ __global__ void __launch_bounds__(1024) pk_persistent(pk_kargs a) {
         if (kind == PK_SWEEP) {
             if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
                 resident_sweep_task<T, HAS_B>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
+            } else if constexpr (LAYOUT == PK_LAYOUT_REGISTER) {
+                reg_sweep_task<T, HAS_B>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
             } else {
                 for (int s = 0; s < n;) {
                     const int k = min(a.pass_sweeps, n - s);
@@ -378,6 +588,9 @@ __global__ void __launch_bounds__(256) pk_scale_source(const T* f, T* b, int nx,
 
 template <typename T>
 const void* persistent_fn(bool has_b, int layout) {
+    if (layout == PK_LAYOUT_REGISTER)
+        return has_b ? reinterpret_cast<const void*>(&pk_persistent<T, true, PK_LAYOUT_REGISTER>)
+                     : reinterpret_cast<const void*>(&pk_persistent<T, false, PK_LAYOUT_REGISTER>);
     if (layout == PK_LAYOUT_RESIDENT)
         return has_b ? reinterpret_cast<const void*>(&pk_persistent<T, true, PK_LAYOUT_RESIDENT>)
                      : reinterpret_cast<const void*>(&pk_persistent<T, false, PK_LAYOUT_RESIDENT>);

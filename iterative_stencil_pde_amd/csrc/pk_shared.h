@@ -80,6 +80,10 @@ struct pk_dev_state {
 };
 
 // Kernel arguments (passed by value).
+// Words per neighbour-exchange flag: one 128-byte line per block, so a
+// block's store does not touch the line its neighbours poll.
+#define PK_NBR_WORDS 32
+
 struct pk_kargs {
     void* u[2];            // the two field buffers (ny rows x pitch elements)
     const void* b;         // scaled source h*h*f (pitched), or null for Laplace
@@ -90,8 +94,10 @@ struct pk_kargs {
     // passes of several sweeps: rows per band and bands (strips depend on k)
     int pass_sweeps;       // sweeps per pass in the stream layout (1 = one per barrier)
     int pband_rows, pbands;
-    // resident geometry (one band per block)
-    int res_band_rows;     // rows per block band (last band may be shorter)
+    // resident and register geometry: one band per block, the interior split
+    // into bands of res_q or res_q + 1 rows (the first res_rem bands are longer)
+    int res_q, res_rem;
+    int reg_cw, reg_rows;  // register layout: column waves, rows per wave
     int res_halo;          // sweeps per halo exchange
     int res_ext_rows;      // LDS rows per buffer
     int lds_pitch;         // LDS row stride in elements
@@ -107,4 +113,6 @@ struct pk_kargs {
     double* partials;      // one double per block
     void* staging;         // readback target (pinned host, device-visible)
     uint32_t* stamp;       // 2 x grid x 64 words for the visibility check
+    uint32_t* nbr;         // neighbour exchange flags, PK_NBR_WORDS words per block
+    int exchange;          // PK_EXCHANGE_BARRIER or PK_EXCHANGE_NEIGHBOR (resident)
 };

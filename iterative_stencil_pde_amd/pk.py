@@ -25,10 +25,11 @@ PK_OK, PK_EINVAL, PK_ENOMEM, PK_ELAUNCH, PK_EDEVICE, PK_EBUSY, PK_ESTATE, PK_ETI
     0, -1, -2, -3, -4, -5, -6, -7)
 PK_F32, PK_F64 = 0, 1
 PK_PERSISTENT, PK_LAUNCH = 0, 1
-PK_LAYOUT_AUTO, PK_LAYOUT_STREAM, PK_LAYOUT_RESIDENT = 0, 1, 2
+PK_LAYOUT_AUTO, PK_LAYOUT_STREAM, PK_LAYOUT_RESIDENT, PK_LAYOUT_REGISTER = 0, 1, 2, 3
 PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP = 1, 2, 3, 4, 5
 PK_DBG_BROKEN_BARRIER = 0x1
 PK_BARRIER_AUTO, PK_BARRIER_FLAT, PK_BARRIER_TWO_LEVEL, PK_BARRIER_XCD = 0, 1, 2, 3
+PK_EXCHANGE_AUTO, PK_EXCHANGE_BARRIER, PK_EXCHANGE_NEIGHBOR = 0, 1, 2
 
 EXPORTED = ["pk_opts_default", "pk_create", "pk_submit", "pk_wait", "pk_readback",
             "pk_run_launch_per_iter", "pk_get_info", "pk_destroy", "pk_strerror"]
@@ -41,7 +42,7 @@ class pk_opts(ctypes.Structure):
                 ("flags", ctypes.c_uint), ("stream", ctypes.c_void_p),
                 ("idle_timeout_s", ctypes.c_double), ("barrier", ctypes.c_int),
                 ("pass_sweeps", ctypes.c_int), ("band_rows", ctypes.c_int),
-                ("reserved", ctypes.c_int * 5)]
+                ("exchange", ctypes.c_int), ("reserved", ctypes.c_int * 4)]
 
 
 class pk_task(ctypes.Structure):
@@ -61,7 +62,7 @@ class pk_info(ctypes.Structure):
                 ("blocks_per_cu_max", ctypes.c_int), ("cus", ctypes.c_int),
                 ("halo_depth", ctypes.c_int), ("band_rows", ctypes.c_int),
                 ("strips", ctypes.c_int), ("barrier", ctypes.c_int), ("pass_sweeps", ctypes.c_int),
-                ("lds_bytes", ctypes.c_size_t),
+                ("exchange", ctypes.c_int), ("lds_bytes", ctypes.c_size_t),
                 ("kernel_ms", ctypes.c_double), ("sweeps_done", ctypes.c_int64),
                 ("tasks_done", ctypes.c_int64), ("kernel_launches", ctypes.c_int64)]
 

@@ -53,9 +53,10 @@ def test_struct_layouts_match_header(tmp_path):
 int main(void) {
   printf("pk_opts %zu\\npk_task %zu\\npk_result %zu\\npk_info %zu\\n",
          sizeof(pk_opts), sizeof(pk_task), sizeof(pk_result), sizeof(pk_info));
-  P(pk_opts, h); P(pk_opts, flags); P(pk_opts, stream); P(pk_opts, idle_timeout_s); P(pk_opts, reserved);
+  P(pk_opts, h); P(pk_opts, flags); P(pk_opts, stream); P(pk_opts, idle_timeout_s); P(pk_opts, exchange);
+  P(pk_opts, reserved);
   P(pk_result, residual); P(pk_result, errors); P(pk_result, status);
-  P(pk_info, lds_bytes); P(pk_info, kernel_ms); P(pk_info, kernel_launches);
+  P(pk_info, exchange); P(pk_info, lds_bytes); P(pk_info, kernel_ms); P(pk_info, kernel_launches);
   return 0;
 }
 """)
@@ -94,6 +95,10 @@ def test_create_rejects_bad_arguments_before_touching_a_device(lib):
     bad = pk.pk_opts_default(dtype=7)
     assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
     bad = pk.pk_opts_default(threads=100)
+    assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
+    bad = pk.pk_opts_default(exchange=3)
+    assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
+    bad = pk.pk_opts_default(exchange=pk.PK_EXCHANGE_NEIGHBOR, flags=pk.PK_DBG_BROKEN_BARRIER)
     assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
     bad = pk.pk_opts_default()
     bad.reserved[3] = 1

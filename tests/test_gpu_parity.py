@@ -181,6 +181,87 @@ def test_stream_passes_full_size(name, sweeps, k):
     check_against_oracle(w, got, ref, f"{name}/pass{k}")
 
 
+@pytest.mark.parametrize("layout", [pk.PK_LAYOUT_REGISTER, pk.PK_LAYOUT_RESIDENT], ids=["register", "lds"])
+@pytest.mark.parametrize("blocks,halo", [(1, 0), (2, 5), (7, 9), (16, 15), (32, 7), (64, 3), (127, 2)])
+def test_tile_layouts_poisson256(layout, blocks, halo):
+    w = inputs.poisson_uniform(256, 0, 100)
+    w.script = [("residual",), ("sweep", 1), ("sweep", 7), ("residual",), ("sweep", 13),
+                ("sweep", 29), ("sweep", 40), ("residual",), ("readback",)]
+    ref = run_oracle_script(w)
+    try:
+        got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=layout, max_blocks=blocks,
+                                halo_depth=halo)
+    except pk.PkError as ex:
+        assert ex.status == pk.PK_EINVAL
+        pytest.skip(f"{blocks} blocks do not fit this layout")
+    info = got["info"]
+    say(f"  layout={info.layout} grid={info.grid_blocks} threads={info.threads} band={info.band_rows} "
+        f"halo={info.halo_depth} lds={info.lds_bytes}")
+    assert info.layout == layout and info.grid_blocks == blocks
+    check_against_oracle(w, got, ref, f"tile{layout}/{blocks}/{halo}")
+
+
+@pytest.mark.parametrize("poisson", [False, True], ids=["laplace", "poisson"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("shape,blocks", [((3, 3), 1), ((64, 64), 1), ((67, 131), 4), ((130, 257), 8),
+                                          ((200, 1030), 50), ((41, 2048), 39), ((300, 5), 12)],
+                         ids=lambda v: str(v))
+def test_register_layout_shapes(shape, blocks, dtype, poisson):
+    ny, nx = shape
+    u, f = _random_case(ny, nx, dtype, poisson, seed=11 * ny + nx)
+    w = inputs.Workload(f"reg{ny}x{nx}", nx, ny, dtype, 0.013, u, f,
+                        [("sweep", 5), ("residual",), ("sweep", 12), ("residual",), ("readback",)], "")
+    ref = run_oracle_script(w)
+    try:
+        got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_REGISTER, max_blocks=blocks)
+    except pk.PkError as ex:
+        assert ex.status == pk.PK_EINVAL
+        pytest.skip("does not fit the register layout")
+    say(f"  grid={got['info'].grid_blocks} halo={got['info'].halo_depth}")
+    check_against_oracle(w, got, ref, f"register/{ny}x{nx}/{np.dtype(dtype).name}")
+
+
+@pytest.mark.parametrize("exchange", [pk.PK_EXCHANGE_BARRIER, pk.PK_EXCHANGE_NEIGHBOR],
+                         ids=["barrier", "neighbor"])
+@pytest.mark.parametrize("blocks,halo", [(2, 5), (5, 3), (32, 7), (127, 2)])
+def test_resident_exchange_kinds(exchange, blocks, halo):
+    """Halo exchange by grid barrier or by neighbour flags: same field, same
+    residuals. Task lengths are not multiples of the halo depth."""
+    w = inputs.poisson_uniform(256, 0, 100)
+    w.script = [("residual",), ("sweep", 1), ("sweep", 11), ("residual",), ("sweep", 23),
+                ("sweep", 40), ("residual",), ("readback",)]
+    ref = run_oracle_script(w)
+    try:
+        got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_RESIDENT,
+                                max_blocks=blocks, halo_depth=halo, exchange=exchange)
+    except pk.PkError as ex:
+        assert ex.status == pk.PK_EINVAL
+        pytest.skip(f"{blocks} blocks do not fit")
+    assert got["info"].exchange == exchange
+    check_against_oracle(w, got, ref, f"exchange{exchange}/{blocks}/{halo}")
+
+
+@pytest.mark.parametrize("shape,dtype,poisson,threads,blocks,halo", [
+    ((20, 4100), np.float32, False, 1024, 9, 1),  # 1025 vectors a row: more segments than waves
+    ((40, 1030), np.float32, True, 256, 12, 1),   # 258 vectors, 4 waves: segments taken in turn
+    ((70, 1000), np.float64, True, 1024, 34, 1),  # 500 vectors: 8 segments of 2 waves each
+    ((66, 37), np.float32, True, 1024, 1, 0),     # 10 vectors: 4 rows share a wave
+    ((130, 127), np.float32, True, 512, 16, 4),   # 32 vectors: 2 rows share a wave
+], ids=["4100f32", "1030f32t256", "1000f64", "37f32", "127f32t512"])
+def test_resident_row_mappings(shape, dtype, poisson, threads, blocks, halo):
+    ny, nx = shape
+    u, f = _random_case(ny, nx, dtype, poisson, seed=5 * ny + nx)
+    w = inputs.Workload(f"map{ny}x{nx}", nx, ny, dtype, 0.02, u, f,
+                        [("sweep", 6), ("residual",), ("sweep", 9), ("residual",), ("readback",)], "")
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_RESIDENT, threads=threads,
+                            max_blocks=blocks, halo_depth=halo)
+    info = got["info"]
+    say(f"  grid={info.grid_blocks} threads={info.threads} band={info.band_rows} halo={info.halo_depth}")
+    assert info.layout == pk.PK_LAYOUT_RESIDENT and info.threads == threads
+    check_against_oracle(w, got, ref, f"rowmap/{ny}x{nx}")
+
+
 def test_resident_fp64_wide():
     u, f = _random_case(130, 1000, np.float64, True, seed=77)
     w = inputs.Workload("wide64", 1000, 130, np.float64, 0.01, u, f,
