@@ -17,6 +17,9 @@ from __future__ import annotations
 
 import argparse
 import collections
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +32,8 @@ sys.path.insert(0, ROOT)
 
 from iterative_stencil_pde_amd import inputs, pk  # noqa: E402
 
+PROFILES = os.path.join(ROOT, "profiles")
+DEVICE_SOURCES = ["pk_device.h", "pk_kernels.hip", "pk_shared.h"]
 METRIC = ("µs/iteration + Gcell-updates/s (persistent vs per-launch); "
           "HBM GB/s % of peak")
 HBM_PEAK_GBS = 8000.0
@@ -84,6 +89,115 @@ def measure(w, steps, warmup, **opts):
     return t1 - t0, info0, info1
 
 
+def sweep_only(w, steps, warmup, **opts):
+    """Variant (i): the same sweeps as one SWEEP task per step, no residuals."""
+    import copy
+    w1 = copy.copy(w)
+    w1.script = [("sweep", w.sweeps)]
+    dt, _, _ = measure(w1, steps, warmup, **opts)
+    return dt / (w.sweeps * steps) * 1e6
+
+
+def overheads(w, opts, n_barrier=20000, n_handshake=2000):
+    """Fixed costs of the persistent engine with the same plan: create + launch,
+    one task round trip (SWEEP 0), and one grid barrier (a BARRIER task)."""
+    t0 = time.perf_counter()
+    e = pk.Engine(w.u0, w.f, h=w.h, mode=pk.PK_PERSISTENT, **opts)
+    create_ms = (time.perf_counter() - t0) * 1e3
+    with e:
+        for _ in range(50):
+            e.run(pk.PK_SWEEP, 0)
+        t0 = time.perf_counter()
+        for _ in range(n_handshake):
+            e.run(pk.PK_SWEEP, 0)
+        handshake_us = (time.perf_counter() - t0) / n_handshake * 1e6
+        e.run(pk.PK_BARRIER, 100)
+        r = e.run(pk.PK_BARRIER, n_barrier)
+        barrier_us = r.device_us / n_barrier
+    return {"create_launch_ms": round(create_ms, 3), "handshake_us": round(handshake_us, 3),
+            "barrier_us": round(barrier_us, 4)}
+
+
+def launch_synced(w, n, threads, blocks):
+    """Per-launch baseline with a host synchronization after every launch."""
+    with pk.Engine(w.u0, w.f, h=w.h, mode=pk.PK_LAUNCH, threads=threads, max_blocks=blocks) as e:
+        e.launch_per_iter(min(n, 50), True)
+        return e.launch_per_iter(n, True) / n
+
+
+def device_source_sha() -> str:
+    """Hash of the device code: stored counter traffic is valid for this hash only."""
+    h = hashlib.sha256()
+    for name in DEVICE_SOURCES:
+        with open(os.path.join(ROOT, "iterative_stencil_pde_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"pk_persistent_{workload}_traffic.json")
+
+
+def stored_traffic(workload: str, steps_in_launch: int):
+    """HBM-side bytes of one persistent launch from stored rocprofv3 counters
+    (FETCH_SIZE and WRITE_SIZE, calibrated on a copy of known size), scaled to
+    this launch's step count; None when absent or taken on other device code."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("device_source_sha") != device_source_sha():
+        return None
+    return rec["bytes_per_step"] * steps_in_launch
+
+
+def _counter_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def fold_traffic(fetch_dir, write_dir, workload, steps_in_launch, copy_mib):
+    """Turn two counter runs (each: a copy of copy_mib MiB, then the persistent
+    launch of steps_in_launch steps) into the stored traffic record."""
+    def per_kernel(d, counter):
+        out = collections.defaultdict(list)
+        rows = sorted(_counter_rows(d), key=lambda r: int(r.get("Dispatch_Id", 0) or 0))
+        for r in rows:
+            if r["Counter_Name"] == counter:
+                out[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return out
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    copy_bytes = copy_mib * (1 << 20)
+
+    def one(table, pattern, what):
+        keys = [k for k in table if pattern in k and "Rect" not in k]
+        if not keys or not table[keys[0]]:
+            raise SystemExit(f"no {what} dispatch ({pattern}) in the counters")
+        return table[keys[0]][0]  # the first dispatch: the calibration copy / the timed launch
+
+    copy_key = "copyBuffer"  # the runtime's device-to-device copy kernel
+    f_scale = copy_bytes / (one(fetch, copy_key, "copy") * 1024.0)
+    w_scale = copy_bytes / (one(write, copy_key, "copy") * 1024.0)
+    f_kib = one(fetch, "pk_persistent", "persistent")
+    w_kib = one(write, "pk_persistent", "persistent")
+    total = f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale
+    rec = {"workload": workload, "device_source_sha": device_source_sha(),
+           "steps_in_profiled_launch": steps_in_launch,
+           "fetch_kib": f_kib, "write_kib": w_kib, "fetch_scale": round(f_scale, 4),
+           "write_scale": round(w_scale, 4), "bytes_per_launch": total,
+           "bytes_per_step": total / steps_in_launch,
+           "note": "FETCH_SIZE and WRITE_SIZE of the first pk_persistent dispatch, each scaled by "
+                   "known bytes / counter of a device copy of the same run; MALL hits count"}
+    with open(traffic_file(workload), "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(w, budget_s: float = 10.0):
     import oracle
     ck = w.residual_checkpoints
@@ -126,6 +240,11 @@ def main():
     ap.add_argument("--persistent-only", action="store_true")
     ap.add_argument("--idle-timeout", type=float, default=0.0,
                     help="persistent kernel idle timeout in seconds (0 = engine default)")
+    ap.add_argument("--main-only", action="store_true",
+                    help="only the timed persistent launch (for counter collection)")
+    ap.add_argument("--fold-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="store the traffic of two rocprofv3 counter runs of this workload "
+                         "(made with --main-only --calibrate-copy MIB) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a torch device-to-device copy of MIB MiB (a plain copy "
                          "kernel of known size, to scale HBM byte counters)")
@@ -135,6 +254,11 @@ def main():
         print(json.dumps({"error": "this engine runs on one GPU; --gpus must be 1 "
                           "(the multi-GPU row-band design is described, not built)"}))
         sys.exit(2)
+
+    if args.fold_traffic:
+        fold_traffic(args.fold_traffic[0], args.fold_traffic[1], args.workload,
+                     args.steps + args.warmup, args.calibrate_copy or 1024)
+        return
 
     if args.calibrate_copy:
         import torch  # before the engine library: one HIP runtime in the process
@@ -177,14 +301,25 @@ def main():
     launch_bytes = step_bytes * (args.steps + args.warmup)
     achieved = launch_bytes / kernel_s / 1e9 if kernel_s > 0 else None
 
+    if args.main_only:
+        print(json.dumps({"workload": w.name, "us_per_iteration": round(us_iter, 4),
+                          "kernel_ms": info_end.kernel_ms, "steps_in_launch": args.steps + args.warmup}),
+              flush=True)
+        return
+    us_sweep_only = None
+    if not args.sweeps_only and sum(1 for t in step_tasks(w) if t[0] == "residual"):
+        us_sweep_only = sweep_only(w, args.steps, args.warmup, mode=pk.PK_PERSISTENT, **opts)
+    fixed = overheads(w, opts)
+
     # per-launch baseline, same block count as the persistent grid
     lsteps = args.launch_steps or args.steps
     if args.persistent_only:
-        ldt, linfo, lvalue = float("nan"), info, float("nan")
+        ldt, linfo, lvalue, lsync = float("nan"), info, float("nan"), None
     else:
         ldt, linfo, _ = measure(w, lsteps, 1, mode=pk.PK_LAUNCH, threads=info.threads,
                                 max_blocks=info.grid_blocks)
         lvalue = cells_per_step * lsteps / ldt / 1e9
+        lsync = launch_synced(w, min(w.sweeps, 2000), info.threads, info.grid_blocks)
 
     rec = {
         "metric": METRIC,
@@ -195,6 +330,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(dt / args.steps * 1e3, 4),
         "us_per_iteration": round(us_iter, 4),
+        "us_per_iteration_sweep_task": round(us_sweep_only, 4) if us_sweep_only else round(us_iter, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -218,18 +354,20 @@ def main():
         "per_launch": None if args.persistent_only else {
             "value": round(lvalue, 4),
             "us_per_iteration": round(ldt / (w.sweeps * lsteps) * 1e6, 4),
+            "us_per_iteration_synced": round(lsync, 4),
             "steps": lsteps,
             "grid_blocks": linfo.grid_blocks,
             "kernel_launches_per_step": w.sweeps + 2 * sum(1 for s in step_tasks(w) if s[0] == "residual"),
             "speedup_persistent": round(value / lvalue, 3),
         },
+        "overheads": fixed,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2) if achieved else None,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 5) if achieved else None,
-            "traffic": None,
+            "traffic": stored_traffic(args.workload, args.steps + args.warmup),
             "kernel": "pk_persistent",
             "kernel_ms": round(info_end.kernel_ms, 3),
             "algorithmic_bytes_per_launch": launch_bytes,

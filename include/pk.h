@@ -161,6 +161,8 @@ typedef struct pk_opts {
     int reserved[4];       /* must be zero                                           */
 } pk_opts;
 
+#define PK_TASK_N_MAX 0x0FFFFFFF /* largest n of one task */
+
 typedef struct pk_task {
     int kind; /* PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP */
     int n;    /* count for SWEEP, BARRIER and STAMP; ignored otherwise */
@@ -215,9 +217,11 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* o,
               pk_engine** out);
 
 /* Queue a task; tasks run in FIFO order. *ticket (may be NULL) receives the
- * task's sequence number (1, 2, ...). Does not block.
- * Errors: PK_EINVAL (unknown kind, n < 0, persistent-only kind in PK_LAUNCH
- * mode), PK_EBUSY (ring full: wait on an older ticket first), PK_ESTATE
+ * task's sequence number (1, 2, ...). Does not block. A task travels to the
+ * device as one 64-bit word, so n is at most PK_TASK_N_MAX (2^28 - 1): split
+ * longer runs into several SWEEP tasks.
+ * Errors: PK_EINVAL (unknown kind, n < 0 or > PK_TASK_N_MAX, persistent-only
+ * kind in PK_LAUNCH mode), PK_EBUSY (ring full: wait on an older ticket first), PK_ESTATE
  * (after EXIT, or on a poisoned engine). */
 int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket);
 

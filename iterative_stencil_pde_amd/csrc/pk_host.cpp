@@ -591,7 +591,7 @@ int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket) {
     if (e->state != RUNNING) return PK_ESTATE;
     const bool known = t.kind == PK_SWEEP || t.kind == PK_RESIDUAL || t.kind == PK_EXIT ||
                        t.kind == PK_BARRIER || t.kind == PK_STAMP;
-    if (!known || t.n < 0) return PK_EINVAL;
+    if (!known || t.n < 0 || t.n > PK_TASK_N_MAX) return PK_EINVAL;
     if (e->mode == PK_LAUNCH) {
         if (t.kind == PK_BARRIER || t.kind == PK_STAMP) return PK_EINVAL;
         const uint64_t seq = e->lresults.size() + 1;

@@ -437,8 +437,13 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
             if (!bc.faulted && fault == 0) {
                 const uint64_t t0 = wall_clock64();
                 bool idle = false;
-                while (__hip_atomic_load(&mail->tail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) <
-                       next_seq) {
+                // the slot word carries the whole task: poll it until its
+                // sequence half is the one expected (one bus read per poll)
+                const uint64_t* slot = &mail->slot[next_seq % PK_RING].word;
+                uint64_t w = 0;
+                for (;;) {
+                    w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    if (static_cast<uint32_t>(w >> 32) == static_cast<uint32_t>(next_seq)) break;
                     __builtin_amdgcn_s_sleep(1);
                     if (wall_clock64() - t0 > a.idle_ticks) {
                         idle = true;
@@ -449,17 +454,8 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
                     __hip_atomic_store(&a.st->fault, static_cast<uint32_t>(PK_FAULT_IDLE_TIMEOUT),
                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 } else {
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");  // the slot the host released
-                    const pk_slot* sl = &mail->slot[next_seq % PK_RING];
-                    const uint64_t sseq =
-                        __hip_atomic_load(&sl->seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    kind = __hip_atomic_load(&sl->kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    nn = __hip_atomic_load(&sl->n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    if (sseq != next_seq) {
-                        kind = PK_EXIT;
-                        __hip_atomic_store(&a.st->fault, static_cast<uint32_t>(PK_FAULT_BAD_TASK),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
+                    kind = static_cast<int>((w >> 28) & 0xF);
+                    nn = static_cast<int>(w & PK_TASK_N_MAX);
                 }
             }
             a.st->task_seq = next_seq;

@@ -3,9 +3,9 @@
 // be exercised on the CPU against a thread that plays the device.
 //
 // Protocol (see pk_shared.h for the layout):
-//   host:   write slot[s % RING] = {seq s, kind, n}; release-store tail = s.
-//   device: poll tail >= s (relaxed), acquire, read the slot, run the task,
-//           write done[s % RING], release-store done_seq = s.
+//   host:   store slot[s % RING] = pack(s, kind, n) (one 64-bit word).
+//   device: poll slot[s % RING] until its sequence half equals s, run the
+//           task, write done[s % RING], release-store done_seq = s.
 // A slot is reused only after its previous task's record has been harvested,
 // so neither side ever overwrites something the other still needs. Sequence
 // numbers replace IDLE/DONE toggles, so there is no early acknowledgement
@@ -53,11 +53,8 @@ public:
     int publish(int kind, int n, uint64_t* seq) {
         harvest();
         if (next_ - 1 - harvested_ >= PK_RING) return PK_EBUSY;
-        pk_slot& s = m_->slot[next_ % PK_RING];
-        s.kind = kind;
-        s.n = n;
-        s.seq = next_;
-        __atomic_store_n(&m_->tail, next_, __ATOMIC_RELEASE);
+        __atomic_store_n(&m_->slot[next_ % PK_RING].word, pk_slot_pack(next_, kind, n),
+                         __ATOMIC_RELEASE);
         if (seq) *seq = next_;
         ++next_;
         return PK_OK;

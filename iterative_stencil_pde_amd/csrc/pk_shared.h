@@ -1,9 +1,11 @@
 // Memory layouts shared by the host runtime and the device kernels.
 //
 // Host<->device mailbox (fine-grained, coherent pinned host memory, mapped on
-// the device). The host publishes tasks as sequence-numbered slots and then
-// moves `tail`; one device thread (block 0, lane 0) polls `tail`. The device
-// answers by filling `done[seq % PK_RING]` and then moving `done_seq`. Every
+// the device). The host publishes a task as one 64-bit slot word (sequence
+// number, kind and count together, one atomic store); one device thread
+// (block 0, lane 0) polls the next slot's word, so a single read over the bus
+// both notices the task and delivers it. The device answers by filling
+// `done[seq % PK_RING]` and then moving `done_seq`. Every
 // word that one side polls sits on its own 128-byte line, so the writer of one
 // flag never invalidates the line of another (the first page's flag-padding
 // point, "Reflections and next steps").
@@ -15,19 +17,30 @@
 #define PK_MAX_PASS 4
 #define PK_LINE 128
 
-// Internal task kinds (the public ones are in pk.h).
-#define PK_TASK_READBACK 100
+// Internal task kinds (the public ones are in pk.h); kinds fit in 4 bits.
+#define PK_TASK_READBACK 15
 
 // Device fault codes (pk_dev_state::fault).
 #define PK_FAULT_BARRIER_TIMEOUT 1u
 #define PK_FAULT_IDLE_TIMEOUT 2u
-#define PK_FAULT_BAD_TASK 3u
+
+// Slot word: bits 63..32 the low half of the sequence number, 31..28 the
+// kind, 27..0 the count (PK_TASK_N_MAX, from pk.h, is the largest count).
+#ifndef PK_TASK_N_MAX
+#define PK_TASK_N_MAX 0x0FFFFFFF
+#endif
 
 struct alignas(PK_LINE) pk_slot {
-    uint64_t seq;
-    int32_t kind;
-    int32_t n;
+    uint64_t word;
 };
+
+static inline uint64_t pk_slot_pack(uint64_t seq, int kind, int n) {
+    return ((seq & 0xFFFFFFFFull) << 32) | (static_cast<uint64_t>(kind & 0xF) << 28) |
+           static_cast<uint64_t>(n & PK_TASK_N_MAX);
+}
+static inline uint32_t pk_slot_seq(uint64_t w) { return static_cast<uint32_t>(w >> 32); }
+static inline int pk_slot_kind(uint64_t w) { return static_cast<int>((w >> 28) & 0xF); }
+static inline int pk_slot_n(uint64_t w) { return static_cast<int>(w & PK_TASK_N_MAX); }
 
 struct alignas(PK_LINE) pk_done_rec {
     uint64_t seq;
@@ -42,7 +55,6 @@ struct alignas(PK_LINE) pk_done_rec {
 };
 
 struct pk_mailbox {
-    alignas(PK_LINE) uint64_t tail;      // host writes: last published seq
     alignas(PK_LINE) uint64_t done_seq;  // device writes: last completed seq
     alignas(PK_LINE) uint32_t exited;    // device writes 1 when the kernel leaves
     alignas(PK_LINE) uint32_t fault;     // device writes a PK_FAULT_* code

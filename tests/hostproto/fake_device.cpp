@@ -37,7 +37,8 @@ struct FakeDevice {
         uint64_t next = 1;
         int handled = 0;
         while (!stop.load(std::memory_order_relaxed)) {
-            if (__atomic_load_n(&m->tail, __ATOMIC_ACQUIRE) < next) {
+            const uint64_t w = __atomic_load_n(&m->slot[next % PK_RING].word, __ATOMIC_ACQUIRE);
+            if (pk_slot_seq(w) != static_cast<uint32_t>(next)) {
                 std::this_thread::yield();
                 continue;
             }
@@ -49,14 +50,13 @@ struct FakeDevice {
                 __atomic_store_n(&m->exited, 1u, __ATOMIC_RELEASE);
                 return;
             }
-            const pk_slot& s = m->slot[next % PK_RING];
-            const uint64_t seq = s.seq;
-            const int kind = s.kind, n = s.n;
+            const uint64_t seq = next;
+            const int kind = pk_slot_kind(w), n = pk_slot_n(w);
             if (delay_us) std::this_thread::sleep_for(std::chrono::microseconds(delay_us));
             pk_done_rec& d = m->done[next % PK_RING];
             if (kind == PK_SWEEP) sweeps += n;
             d.kind = kind;
-            d.status = (seq == next) ? PK_OK : PK_EDEVICE;
+            d.status = PK_OK;
             d.residual = kind == PK_RESIDUAL ? 1.0 / static_cast<double>(seq) : 0.0;
             d.sweeps_done = sweeps;
             d.errors = 0;

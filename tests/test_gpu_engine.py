@@ -89,6 +89,7 @@ def test_protocol_errors_and_ring():
         # unknown task kinds and negative counts
         assert pk.pk_submit_status(h, 99, 0)[0] == pk.PK_EINVAL
         assert pk.pk_submit_status(h, pk.PK_SWEEP, -1)[0] == pk.PK_EINVAL
+        assert pk.pk_submit_status(h, pk.PK_SWEEP, pk.PK_TASK_N_MAX + 1)[0] == pk.PK_EINVAL
         # fill the ring: 64 slots, the 65th is refused until the oldest completes
         tickets = []
         status = pk.PK_OK
