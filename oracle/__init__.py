@@ -1,4 +1,5 @@
-"""CPU oracle for the 5-point Jacobi iteration (test infrastructure only).
+"""CPU oracle for the 5-point Jacobi and red-black Gauss-Seidel iterations
+(test infrastructure only).
 
 Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The HIP engine never imports, links or
@@ -44,7 +45,7 @@ class Oracle:
     def __init__(self, path: str):
         lib = ctypes.CDLL(path)
         dp = ctypes.c_void_p
-        for name in ("oracle_jacobi_f32", "oracle_jacobi_f64"):
+        for name in ("oracle_jacobi_f32", "oracle_jacobi_f64", "oracle_rbgs_f32", "oracle_rbgs_f64"):
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, dp, dp, ctypes.c_int64,
@@ -77,6 +78,25 @@ class Oracle:
         out = np.empty_like(u0)
         fn = self.lib.oracle_jacobi_f32 if u0.dtype == np.float32 else self.lib.oracle_jacobi_f64
         rc = fn(nx, ny, float(h), _ptr(u0), _ptr(f), int(sweeps), _ptr(ck) if len(ck) else None,
+                len(ck), _ptr(out), _ptr(res) if len(ck) else None)
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return out, res
+
+    def rbgs(self, u0: np.ndarray, iterations: int, f: np.ndarray | None = None,
+             h: float | None = None, checkpoints=()):
+        """Run ``iterations`` red-black Gauss-Seidel iterations from ``u0`` in place
+        (red = interior nodes with i + j even, updated first; then black). Arguments
+        and result as for :meth:`jacobi`, with checkpoints counted in iterations."""
+        u0, f = _check_field(u0, f)
+        ny, nx = u0.shape
+        if h is None:
+            h = 1.0 / (nx - 1)
+        ck = np.ascontiguousarray(np.asarray(checkpoints, dtype=np.int64))
+        res = np.zeros(len(ck), dtype=np.float64)
+        out = np.empty_like(u0)
+        fn = self.lib.oracle_rbgs_f32 if u0.dtype == np.float32 else self.lib.oracle_rbgs_f64
+        rc = fn(nx, ny, float(h), _ptr(u0), _ptr(f), int(iterations), _ptr(ck) if len(ck) else None,
                 len(ck), _ptr(out), _ptr(res) if len(ck) else None)
         if rc != 0:
             raise ValueError("oracle rejected its arguments")
@@ -138,6 +158,10 @@ def default() -> Oracle:
 
 def jacobi(u0, sweeps, f=None, h=None, checkpoints=()):
     return default().jacobi(u0, sweeps, f=f, h=h, checkpoints=checkpoints)
+
+
+def rbgs(u0, iterations, f=None, h=None, checkpoints=()):
+    return default().rbgs(u0, iterations, f=f, h=h, checkpoints=checkpoints)
 
 
 def residual(u, f=None, h=None):

@@ -1,4 +1,5 @@
-// Jacobi oracle for the 5-point Poisson/Laplace iteration.
+// Jacobi and red-black Gauss-Seidel oracle for the 5-point Poisson/Laplace
+// iteration.
 //
 // TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call
 // this file: only the tests, the smoke check and the CPU-baseline leg of the
@@ -32,6 +33,13 @@
 //     every operand widened to double first and the sum accumulated in double,
 //     in row-major order.
 //   * Dirichlet only: the outer ring of the grid is never written.
+//
+// Red-black Gauss-Seidel (the iteration that page measures, same section and
+// its Figure 3): in place, one iteration = first every interior node whose
+// indices i and j have the same parity (red), then every interior node whose
+// parities differ (black). Each node's update is the same formula as above; its
+// four neighbours have the other colour, so within one half the order of the
+// updates does not matter.
 //
 // Plain nested loops, single thread, no blocking, fusion or reordering.
 
@@ -90,6 +98,24 @@ double residual(int nx, int ny, const T* A, const T* b) {
     return std::sqrt(acc);
 }
 
+// One half of a red-black iteration, in place: every interior node of colour
+// `parity` ((i + j) mod 2) from the current values of its neighbours.
+template <typename T>
+void rb_half(int nx, int ny, T* U, const T* b, int parity) {
+    for (int i = 1; i <= ny - 2; ++i) {
+        for (int j = 1; j <= nx - 2; ++j) {
+            if (((i + j) & 1) != parity) continue;
+            const T west = U[at(nx, i, j - 1)];
+            const T east = U[at(nx, i, j + 1)];
+            const T south = U[at(nx, i - 1, j)];
+            const T north = U[at(nx, i + 1, j)];
+            T t = (west + east) + (south + north);
+            if (b) t = t + b[at(nx, i, j)];
+            U[at(nx, i, j)] = T(0.25) * t;
+        }
+    }
+}
+
 // K sweeps from U0. Before sweep k (k = 0..K) the residual is recorded once for
 // every checkpoint entry equal to k (so a checkpoint of K is the final state).
 // Checkpoints must be non-decreasing and lie in [0, K].
@@ -120,6 +146,34 @@ int jacobi(int nx, int ny, double h, const T* U0, const T* F, int64_t K,
     return 0;
 }
 
+// K red-black iterations from U0 (red half, then black half, in one array);
+// checkpoints as for jacobi(), counted in iterations.
+template <typename T>
+int rbgs(int nx, int ny, double h, const T* U0, const T* F, int64_t K,
+         const int64_t* ckpt, int nckpt, T* out, double* res_out) {
+    if (nx < 3 || ny < 3 || K < 0 || !U0 || !out) return -1;
+    if (nckpt < 0 || (nckpt > 0 && (!ckpt || !res_out))) return -1;
+    for (int c = 0; c < nckpt; ++c) {
+        if (ckpt[c] < 0 || ckpt[c] > K) return -1;
+        if (c > 0 && ckpt[c] < ckpt[c - 1]) return -1;
+    }
+    if (F && !(h > 0.0)) return -1;
+    const std::size_t cells = static_cast<std::size_t>(nx) * ny;
+    std::vector<T> U(U0, U0 + cells);
+    std::vector<T> b;
+    if (F) scaled_source<T>(nx, ny, h, F, b);
+    const T* bp = F ? b.data() : nullptr;
+    int c = 0;
+    for (int64_t k = 0;; ++k) {
+        while (c < nckpt && ckpt[c] == k) res_out[c++] = residual<T>(nx, ny, U.data(), bp);
+        if (k == K) break;
+        rb_half<T>(nx, ny, U.data(), bp, 0);  // red: i + j even
+        rb_half<T>(nx, ny, U.data(), bp, 1);  // black: i + j odd
+    }
+    std::memcpy(out, U.data(), cells * sizeof(T));
+    return 0;
+}
+
 template <typename T>
 int residual_of(int nx, int ny, double h, const T* U, const T* F, double* r) {
     if (nx < 3 || ny < 3 || !U || !r) return -1;
@@ -142,6 +196,16 @@ int oracle_jacobi_f32(int nx, int ny, double h, const float* U0, const float* F,
 int oracle_jacobi_f64(int nx, int ny, double h, const double* U0, const double* F, int64_t K,
                       const int64_t* ckpt, int nckpt, double* out, double* res_out) {
     return jacobi<double>(nx, ny, h, U0, F, K, ckpt, nckpt, out, res_out);
+}
+
+int oracle_rbgs_f32(int nx, int ny, double h, const float* U0, const float* F, int64_t K,
+                    const int64_t* ckpt, int nckpt, float* out, double* res_out) {
+    return rbgs<float>(nx, ny, h, U0, F, K, ckpt, nckpt, out, res_out);
+}
+
+int oracle_rbgs_f64(int nx, int ny, double h, const double* U0, const double* F, int64_t K,
+                    const int64_t* ckpt, int nckpt, double* out, double* res_out) {
+    return rbgs<double>(nx, ny, h, U0, F, K, ckpt, nckpt, out, res_out);
 }
 
 int oracle_residual_f32(int nx, int ny, double h, const float* U, const float* F, double* r) {

@@ -10,7 +10,7 @@ requires that every mistake trips at least one pin.
 Pages: "Persistent Kernels: Bridging GPU-CPU Execution" (P1), section "The
 problem" and its "Derivation" (5-point update, grid, spacing 1/(N-1)), and
 section "Implementation details and correctness" (Jacobi into a separate
-matrix); "Grid-Wide Barriers and Persistent Work Queues", "What the barrier
+matrix; red-black Gauss-Seidel in place, same-parity nodes first, Figure 3); "Grid-Wide Barriers and Persistent Work Queues", "What the barrier
 buys" (convergence check as a grid reduction).
 """
 
@@ -275,6 +275,156 @@ def pin_checkpoint_semantics(orc):
         assert res[c] == orc.residual(uk, f=f)
 
 
+# --- red-black Gauss-Seidel ---------------------------------------------------
+def pin_rb_top_row_4x4(orc):
+    """4x4 grid, top row (i = 3) = 1. Interior nodes: (1,1) and (2,2) red, (1,2)
+    and (2,1) black. With s = the sum of the two black values, one iteration gives
+    (1,1) = s/4, (2,2) = (s + 1)/4, then (1,2) = (2s + 1)/16, (2,1) = (2s + 5)/16,
+    so s' = (2s + 3)/8 and from zero s_k = 1/2 - (1/2) 4^-k (the rate 1/4 is the
+    square of the Jacobi rate 1/2 of this grid). Exact dyadics: exact in floating
+    point while they fit the mantissa. The first two iterations were also worked
+    by hand: (0, .0625; .3125, .25) and (.09375, .109375; .359375, .34375)."""
+    by_hand = {1: (0.0, 0.0625, 0.3125, 0.25), 2: (0.09375, 0.109375, 0.359375, 0.34375)}
+    for dtype, kmax in ((np.float32, 10), (np.float64, 24)):
+        u0 = np.zeros((4, 4), dtype=dtype)
+        u0[3, :] = 1
+        for k in sorted({1, 2, 3, 6, kmax}):
+            out, _ = orc.rbgs(u0, k)
+            s = Fraction(1, 2) - Fraction(1, 2) * Fraction(1, 4) ** (k - 1)  # s_{k-1}
+            want = np.zeros((4, 4), dtype=dtype)
+            want[3, :] = 1
+            want[1, 1] = float(s / 4)
+            want[2, 2] = float((s + 1) / 4)
+            want[1, 2] = float((2 * s + 1) / 16)
+            want[2, 1] = float((2 * s + 5) / 16)
+            assert np.array_equal(out, want), (dtype, k, out)
+            if k in by_hand:
+                assert (out[1, 1], out[1, 2], out[2, 1], out[2, 2]) == by_hand[k]
+
+
+def pin_rb_halves_are_one_colour_jacobi(orc):
+    """Red nodes read only black neighbours, so after the red half every red node
+    equals one Jacobi sweep of the input, and every black node is unchanged; the
+    black half is then one Jacobi sweep of that intermediate state, black nodes
+    only. Checked bitwise against the (separately pinned) Jacobi oracle, on
+    non-square grids whose corner parities differ."""
+    rng = np.random.default_rng(77)
+    for (ny, nx) in ((7, 9), (8, 5), (6, 6)):
+        for dtype in (np.float32, np.float64):
+            u = rng.uniform(-1, 1, (ny, nx)).astype(dtype)
+            f = rng.uniform(-3, 3, (ny, nx)).astype(dtype)
+            for src in (None, f):
+                ii, jj = np.indices((ny, nx))
+                interior = (ii > 0) & (ii < ny - 1) & (jj > 0) & (jj < nx - 1)
+                red = interior & ((ii + jj) % 2 == 0)
+                black = interior & ((ii + jj) % 2 == 1)
+                cur = u
+                for _ in range(3):
+                    j1, _ = orc.jacobi(cur, 1, f=src, h=0.3)
+                    mid = cur.copy()
+                    mid[red] = j1[red]
+                    j2, _ = orc.jacobi(mid, 1, f=src, h=0.3)
+                    want = mid.copy()
+                    want[black] = j2[black]
+                    got, _ = orc.rbgs(cur, 1, f=src, h=0.3)
+                    assert np.array_equal(got, want), (ny, nx, dtype)
+                    cur = got
+            # several iterations in one call equal the same number of single calls
+            one = u
+            for _ in range(4):
+                one, _ = orc.rbgs(one, 1)
+            four, _ = orc.rbgs(u, 4)
+            assert np.array_equal(one, four)
+
+
+def _exact_rb_iteration(u, f, h):
+    ny, nx = u.shape
+    U = [[Fraction(float(v)) for v in row] for row in u]
+    hh = Fraction(h) * Fraction(h)
+    for parity in (0, 1):
+        for i in range(1, ny - 1):
+            for j in range(1, nx - 1):
+                if (i + j) % 2 != parity:
+                    continue
+                s = U[i][j - 1] + U[i][j + 1] + U[i - 1][j] + U[i + 1][j]
+                if f is not None:
+                    s += hh * Fraction(float(f[i, j]))
+                U[i][j] = s / 4
+    return U
+
+
+def pin_rb_exact_rational_small(orc):
+    """One fp64 red-black iteration on random 5x7 and 6x5 grids against the same
+    iteration in exact rational arithmetic: red nodes within one rounding of the
+    5-term sum, black nodes within that plus the red rounding they read."""
+    rng = np.random.default_rng(4321)
+    for (ny, nx) in ((5, 7), (6, 5)):
+        u = rng.uniform(-1, 1, (ny, nx))
+        f = rng.uniform(-4, 4, (ny, nx))
+        h = 0.41
+        for src in (None, f):
+            got, _ = orc.rbgs(u, 1, f=src, h=h)
+            ex = _exact_rb_iteration(u, src, h)
+            for i in range(ny):
+                for j in range(nx):
+                    if i in (0, ny - 1) or j in (0, nx - 1):
+                        assert got[i, j] == u[i, j]
+                        continue
+                    bound = 16 * F64_EPS * (4 + (h * h * 4 if src is not None else 0))
+                    assert abs(Fraction(float(got[i, j])) - ex[i][j]) <= Fraction(bound), (i, j)
+
+
+def pin_rb_harmonic_fixed_point(orc):
+    """x^2 - y^2 has zero 5-point Laplacian: started at it, red-black stays there
+    up to rounding."""
+    n = 33
+    x = np.linspace(0.0, 1.0, n)
+    full = (x[None, :] ** 2 - x[:, None] ** 2)
+    out, _ = orc.rbgs(full, 200)
+    assert np.max(np.abs(out - full)) < 1e-13
+    out32, _ = orc.rbgs(full.astype(np.float32), 200)
+    assert np.max(np.abs(out32 - full.astype(np.float32))) < 2e-6
+
+
+def pin_rb_rate(orc):
+    """Red-black Gauss-Seidel on the model problem contracts the slowest error mode
+    by cos(pi h)^2 per iteration, the square of the Jacobi rate cos(pi h): after
+    many iterations the residual ratio per iteration approaches cos(pi h)^2."""
+    n = 17
+    h = 1.0 / (n - 1)
+    u0 = np.zeros((n, n))
+    u0[1:-1, 1:-1] = inputs.uniform(31, 0, (n - 2) ** 2, 0, 1).reshape(n - 2, n - 2)
+    _, res = orc.rbgs(u0, 400, checkpoints=[399, 400])
+    ratio = res[1] / res[0]
+    assert abs(ratio - np.cos(np.pi * h) ** 2) < 1e-6, ratio
+    _, rj = orc.jacobi(u0, 800, checkpoints=[799, 800])
+    assert abs(rj[1] / rj[0] - np.cos(np.pi * h)) < 1e-6
+
+
+def pin_rb_max_principle(orc):
+    """Every update is a quarter of four current values (Laplace), so the field
+    stays within [min, max] of the starting data after every iteration."""
+    n = 40
+    u = inputs.uniform(12, 0, n * n, 0, 1).reshape(n, n).astype(np.float32)
+    lo, hi = float(u.min()), float(u.max())
+    cur = u
+    for _ in range(5):
+        cur, _ = orc.rbgs(cur, 7)
+        assert float(cur.min()) >= lo and float(cur.max()) <= hi
+
+
+def pin_rb_checkpoint_semantics(orc):
+    """A checkpoint at k is the residual of the field after k red-black iterations."""
+    n = 20
+    f = inputs.uniform(10, 0, n * n, -1, 1).reshape(n, n)
+    u0 = np.zeros((n, n))
+    _, res = orc.rbgs(u0, 12, f=f, checkpoints=[0, 5, 12])
+    assert res[0] == orc.residual(u0, f=f)
+    for c, k in ((1, 5), (2, 12)):
+        uk, _ = orc.rbgs(u0, k, f=f)
+        assert res[c] == orc.residual(uk, f=f)
+
+
 ALL_PINS = [
     pin_top_row_4x4,
     pin_harmonic_4x4_one_sweep,
@@ -289,4 +439,11 @@ ALL_PINS = [
     pin_residual_identity,
     pin_finite_propagation_mirror,
     pin_checkpoint_semantics,
+    pin_rb_top_row_4x4,
+    pin_rb_halves_are_one_colour_jacobi,
+    pin_rb_exact_rational_small,
+    pin_rb_harmonic_fixed_point,
+    pin_rb_rate,
+    pin_rb_max_principle,
+    pin_rb_checkpoint_semantics,
 ]

@@ -17,8 +17,8 @@ from oracle_pins import ALL_PINS
 MUTANTS = {
     "drop_west": ("T t = (w + e) + (s + n);", "T t = (e + e) + (s + n);"),
     "drop_north": ("T t = (w + e) + (s + n);", "T t = (w + e) + (s + s);"),
-    "source_sign": ("if (b) t = t + b[at(nx, i, j)];", "if (b) t = t - b[at(nx, i, j)];"),
-    "source_dropped": ("if (b) t = t + b[at(nx, i, j)];", "if (b) t = t;"),
+    "source_sign": ("if (b) t = t + b[at(nx, i, j)];\n            B[", "if (b) t = t - b[at(nx, i, j)];\n            B["),
+    "source_dropped": ("if (b) t = t + b[at(nx, i, j)];\n            B[", "if (b) t = t;\n            B["),
     "source_h_not_squared": ("const double hh = h * h;", "const double hh = h;"),
     "east_index": ("const T e = A[at(nx, i, j + 1)];", "const T e = A[at(nx, i, j)];"),
     "south_row": ("const T s = A[at(nx, i - 1, j)];", "const T s = A[at(nx, i - 1, j - 1)];"),
@@ -34,6 +34,17 @@ MUTANTS = {
     "residual_source_sign": ("if (b) t = t + static_cast<double>(b[at(nx, i, j)]);",
                              "if (b) t = t - static_cast<double>(b[at(nx, i, j)]);"),
     "residual_not_sqrt": ("return std::sqrt(acc);", "return acc;"),
+    # red-black Gauss-Seidel
+    "rb_black_first": ("rb_half<T>(nx, ny, U.data(), bp, 0);  // red: i + j even\n        rb_half<T>(nx, ny, U.data(), bp, 1);",
+                       "rb_half<T>(nx, ny, U.data(), bp, 1);  // red: i + j even\n        rb_half<T>(nx, ny, U.data(), bp, 0);"),
+    "rb_black_skipped": ("rb_half<T>(nx, ny, U.data(), bp, 1);  // black", "(void)0;  // black"),
+    "rb_row_parity": ("if (((i + j) & 1) != parity) continue;", "if ((i & 1) != parity) continue;"),
+    "rb_east_index": ("const T east = U[at(nx, i, j + 1)];", "const T east = U[at(nx, i, j)];"),
+    "rb_south_row": ("const T south = U[at(nx, i - 1, j)];", "const T south = U[at(nx, i - 1, j - 1)];"),
+    "rb_source_sign": ("if (b) t = t + b[at(nx, i, j)];\n            U[", "if (b) t = t - b[at(nx, i, j)];\n            U["),
+    "rb_weight": ("U[at(nx, i, j)] = T(0.25) * t;", "U[at(nx, i, j)] = T(0.2) * t;"),
+    "rb_jacobi_instead": ("rb_half<T>(nx, ny, U.data(), bp, 0);  // red: i + j even\n        rb_half<T>(nx, ny, U.data(), bp, 1);",
+                          "{ std::vector<T> V(U); sweep<T>(nx, ny, V.data(), U.data(), bp); }"),
     "two_sweeps_per_step": ("if (k == K) break;\n        sweep<T>", "if (k == K) break;\n        sweep<T>(nx, ny, A.data(), B.data(), bp);\n        A.swap(B);\n        sweep<T>"),
 }
 
