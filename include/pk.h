@@ -72,8 +72,9 @@ extern "C" {
  *   steps", "Fewer handshakes", with exact Jacobi semantics).
  * REGISTER: as RESIDENT, but each block's rows live in VGPRs (one 16-byte
  *   vector per lane per row); only wave-boundary rows and columns go through
- *   LDS. For fields whose bands fit in a block's registers.
- * AUTO: REGISTER, else RESIDENT, when the bands fit, else STREAM.           */
+ *   LDS. Experimental: taken only when asked for; no PK_SWEEP_RB.
+ * AUTO: RESIDENT when the bands fit in LDS (block count and halo depth from a
+ *   cost model), else STREAM.                                               */
 #define PK_LAYOUT_AUTO 0
 #define PK_LAYOUT_STREAM 1
 #define PK_LAYOUT_RESIDENT 2
@@ -89,6 +90,15 @@ extern "C" {
                       /*   each block stamps its slot, barrier, then checks that a  */
                       /*   neighbour's and a remote block's slots carry the stamp;  */
                       /*   pk_result.errors counts mismatches                       */
+#define PK_SWEEP_RB 6 /* n red-black Gauss-Seidel iterations ("Persistent Kernels",  */
+                      /*   "Implementation details and correctness", Figure 3):     */
+                      /*   first every interior node with i + j even (red), then    */
+                      /*   every one with i + j odd (black), each by the same       */
+                      /*   formula as a Jacobi sweep from its neighbours' current   */
+                      /*   values. Equal to the in-place iteration; computed as two */
+                      /*   half-sweeps into the other buffer, so `cur` flips as for */
+                      /*   SWEEP. n <= PK_TASK_N_MAX / 2; not in the REGISTER layout.*/
+                      /*   sweeps_done counts iterations.                           */
 
 /* ---- option flags ------------------------------------------------------- */
 /* Debug only: the grid barrier drops its release/acquire ordering (relaxed

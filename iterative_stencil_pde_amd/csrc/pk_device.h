@@ -117,6 +117,21 @@ __device__ __forceinline__ Vec<T> stencil(const Vec<T>& s, const Vec<T>& m, cons
                                 col, nx);
 }
 
+// Red-black half-sweeps ("Persistent Kernels", "Implementation details and
+// correctness", Figure 3): node (i, j) is red when i + j is even; a half-sweep
+// of colour `parity` updates only the nodes of that colour and keeps the rest.
+// A vector starts at an even column, so in row `row` the updated elements are
+// those whose index k has k mod 2 == (row + parity) mod 2.
+template <typename T>
+__device__ __forceinline__ Vec<T> rb_keep(const Vec<T>& o, const Vec<T>& m, int row, int parity) {
+    constexpr int W = VecW<T>::W;
+    const int rp = (row + parity) & 1;
+    Vec<T> r;
+#pragma unroll
+    for (int k = 0; k < W; ++k) r.v[k] = ((k & 1) == rp) ? o.v[k] : m.v[k];
+    return r;
+}
+
 // rho^2 summed over the interior nodes of one vector, in double:
 //     rho = (((W + E) + (S + N)) + b) - 4u.
 template <typename T, bool HAS_B>
@@ -372,7 +387,7 @@ __device__ __forceinline__ double block_sum(double v, double* s_red) {
 template <typename T, bool HAS_B, int CH>
 __device__ __forceinline__ void stream_unit(const T* __restrict__ src, T* __restrict__ dst,
                                             const T* __restrict__ bsrc, int nx, int pitch, int c0,
-                                            int r_begin, int r_end) {
+                                            int r_begin, int r_end, int parity) {
     constexpr int W = VecW<T>::W;
     const int lane = threadIdx.x & 63;
     const int col = c0 + lane * W;
@@ -403,7 +418,8 @@ __device__ __forceinline__ void stream_unit(const T* __restrict__ src, T* __rest
         }
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
-            const Vec<T> o = stencil<T, HAS_B>(up, mid, dn[k], bb[k], mh, col, nx);
+            Vec<T> o = stencil<T, HAS_B>(up, mid, dn[k], bb[k], mh, col, nx);
+            if (parity >= 0) o = rb_keep(o, mid, r + k, parity);  // wave-uniform
             if (act && r + k < r_end) vstore(dst + static_cast<size_t>(r + k) * p + col, o);
             up = mid;
             mid = dn[k];
@@ -457,9 +473,11 @@ __device__ __forceinline__ double stream_unit_residual(const T* __restrict__ src
     return acc;
 }
 
+// One sweep over all units, src -> dst; parity >= 0: one red-black half-sweep
+// of that colour (the other colour is copied).
 template <typename T, bool HAS_B>
 __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restrict__ src,
-                                             T* __restrict__ dst) {
+                                             T* __restrict__ dst, int parity = -1) {
     constexpr int W = VecW<T>::W;
     const int gw = unit_wave(a);
     const int nw = a.grid * (static_cast<int>(blockDim.x) >> 6);
@@ -472,7 +490,8 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
         if (r_begin >= r_end) continue;
         // rows of loads in flight per wave: fewer when b doubles the traffic
         constexpr int CH = (HAS_B || sizeof(T) == 8) ? 4 : 8;
-        stream_unit<T, HAS_B, CH>(src, dst, bsrc, a.nx, a.pitch, strip * 64 * W, r_begin, r_end);
+        stream_unit<T, HAS_B, CH>(src, dst, bsrc, a.nx, a.pitch, strip * 64 * W, r_begin, r_end,
+                                  parity);
     }
 }
 
@@ -496,7 +515,7 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
 template <typename T, bool HAS_B, int K, int DIR>
 __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* __restrict__ dst,
                                                  const T* __restrict__ bsrc, int nx, int ny,
-                                                 int pitch, int c0, int ov, int r0, int r1) {
+                                                 int pitch, int c0, int ov, int r0, int r1, int h0) {
     constexpr int dir = DIR;
     constexpr int W = VecW<T>::W;
     // rows of loads issued ahead; fewer for deep passes (registers hold K windows)
@@ -552,6 +571,7 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
                 const int row = t - dir * j;  // level j row computed at this step
                 Vec<T> o = stencil<T, HAS_B>(win[j - 1][0], win[j - 1][1], win[j - 1][2], bq[j - 1],
                                              T(0), col, nx);
+                if (h0 >= 0) o = rb_keep(o, win[j - 1][1], row, (h0 + j - 1) & 1);  // wave-uniform
                 if (row <= 0 || row >= ny - 1) o = win[j - 1][1];  // ring rows (and beyond)
                 if (j < K) {
                     win[j][0] = win[j][1];
@@ -566,9 +586,10 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
 }
 
 // One pass of k sweeps (1 <= k <= PK_MAX_PASS) over all units, src -> dst.
+// h0 >= 0: the k levels are red-black half-sweeps, level j of colour (h0+j-1) mod 2.
 template <typename T, bool HAS_B, int K>
 __device__ __forceinline__ void stream_pass_k(const pk_kargs& a, const T* __restrict__ src,
-                                              T* __restrict__ dst) {
+                                              T* __restrict__ dst, int h0) {
     constexpr int W = VecW<T>::W;
     const int ov = (K + W - 1) / W;
     const int stride = (64 - 2 * ov) * W;  // stored columns per strip
@@ -584,25 +605,25 @@ __device__ __forceinline__ void stream_pass_k(const pk_kargs& a, const T* __rest
         if (r0 >= r1) continue;
         if (band & 1)
             stream_pass_unit<T, HAS_B, K, -1>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W,
-                                              ov, r0, r1);
+                                              ov, r0, r1, h0);
         else
             stream_pass_unit<T, HAS_B, K, 1>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W,
-                                             ov, r0, r1);
+                                             ov, r0, r1, h0);
     }
 }
 
 template <typename T, bool HAS_B>
 __device__ __forceinline__ void stream_pass(const pk_kargs& a, const T* __restrict__ src,
-                                            T* __restrict__ dst, int k) {
+                                            T* __restrict__ dst, int k, int h0 = -1) {
     // a source term adds a window of b rows: passes of at most 3 sweeps then
     // (the host caps pass_sweeps accordingly), so the kernel stays within 128 VGPRs
     switch (k) {
-        case 2: stream_pass_k<T, HAS_B, 2>(a, src, dst); break;
-        case 3: stream_pass_k<T, HAS_B, 3>(a, src, dst); break;
+        case 2: stream_pass_k<T, HAS_B, 2>(a, src, dst, h0); break;
+        case 3: stream_pass_k<T, HAS_B, 3>(a, src, dst, h0); break;
         case 4:
-            if (!HAS_B) stream_pass_k<T, HAS_B, 4>(a, src, dst);
+            if (!HAS_B) stream_pass_k<T, HAS_B, 4>(a, src, dst, h0);
             break;
-        default: stream_sweep<T, HAS_B>(a, src, dst); break;
+        default: stream_sweep<T, HAS_B>(a, src, dst, h0); break;
     }
 }
 
@@ -693,9 +714,11 @@ __device__ __forceinline__ TileMap<T> tile_map(int nv, int lp, int nx) {
 }
 
 // Rows [lo, hi) of D from S (LDS row stride lp elements; Bt holds b).
-template <typename T, bool HAS_B>
+// RB: a red-black half-sweep; node colour from the global row (local row +
+// q_row) and column, updated when it equals `parity`.
+template <typename T, bool HAS_B, bool RB>
 __device__ __forceinline__ void resident_rows(const T* S, T* D, const T* Bt, int lo, int hi,
-                                              const TileMap<T>& t) {
+                                              const TileMap<T>& t, int q_row = 0, int parity = 0) {
     constexpr int W = VecW<T>::W;
     if (!t.active) return;
     const int lane = static_cast<int>(threadIdx.x) & 63;
@@ -737,6 +760,7 @@ __device__ __forceinline__ void resident_rows(const T* S, T* D, const T* Bt, int
                 if (HAS_B) x = x + bb.v[k];
                 o.v[k] = keep[k] ? m.v[k] : T(0.25) * x;
             }
+            if (RB) o = rb_keep(o, m, rr + q_row, parity);
             if (act) vstore(D + o0, o);
         }
     }

@@ -589,9 +589,12 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
 int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket) {
     if (!e) return PK_EINVAL;
     if (e->state != RUNNING) return PK_ESTATE;
-    const bool known = t.kind == PK_SWEEP || t.kind == PK_RESIDUAL || t.kind == PK_EXIT ||
-                       t.kind == PK_BARRIER || t.kind == PK_STAMP;
+    const bool known = t.kind == PK_SWEEP || t.kind == PK_SWEEP_RB || t.kind == PK_RESIDUAL ||
+                       t.kind == PK_EXIT || t.kind == PK_BARRIER || t.kind == PK_STAMP;
     if (!known || t.n < 0 || t.n > PK_TASK_N_MAX) return PK_EINVAL;
+    // red-black runs 2n half-sweeps; the register tile has no red-black form
+    if (t.kind == PK_SWEEP_RB && (t.n > PK_TASK_N_MAX / 2 || e->plan.layout == PK_LAYOUT_REGISTER))
+        return PK_EINVAL;
     if (e->mode == PK_LAUNCH) {
         if (t.kind == PK_BARRIER || t.kind == PK_STAMP) return PK_EINVAL;
         const uint64_t seq = e->lresults.size() + 1;
@@ -606,9 +609,12 @@ int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket) {
         pk_result r{};
         r.kind = t.kind;
         hipError_t he = hipSuccess;
-        if (t.kind == PK_SWEEP) {
-            for (int s = 0; s < t.n && he == hipSuccess; ++s) {
-                he = pkk_launch_sweep(e->dtype, e->has_b, e->ka, e->plan.threads, e->cur, e->stream);
+        if (t.kind == PK_SWEEP || t.kind == PK_SWEEP_RB) {
+            // red-black: one launch per half-sweep, red (parity 0) first
+            const int launches = t.kind == PK_SWEEP_RB ? 2 * t.n : t.n;
+            for (int s = 0; s < launches && he == hipSuccess; ++s) {
+                he = pkk_launch_sweep(e->dtype, e->has_b, e->ka, e->plan.threads, e->cur,
+                                      t.kind == PK_SWEEP_RB ? (s & 1) : -1, e->stream);
                 e->cur ^= 1;
                 ++e->launches;
             }
@@ -720,7 +726,7 @@ int pk_run_launch_per_iter(pk_engine* e, int n, int sync_each, double* elapsed_u
     hipError_t he = hipEventRecord(e->ev_start, e->stream);
     const auto t0 = std::chrono::steady_clock::now();
     for (int s = 0; s < n && he == hipSuccess; ++s) {
-        he = pkk_launch_sweep(e->dtype, e->has_b, e->ka, e->plan.threads, e->cur, e->stream);
+        he = pkk_launch_sweep(e->dtype, e->has_b, e->ka, e->plan.threads, e->cur, -1, e->stream);
         e->cur ^= 1;
         ++e->launches;
         if (he == hipSuccess && sync_each) he = hipStreamSynchronize(e->stream);

@@ -189,7 +189,8 @@ __device__ void reg_sweep_task(const pk_kargs& a, int n, int& cur, BarrierCtx& b
 // as its new halo. Alternating global buffers by exchange keeps a fast block
 // from overwriting rows a slow neighbour still reads.
 // ---------------------------------------------------------------------------
-template <typename T, bool HAS_B>
+// n sub-sweeps: Jacobi sweeps, or (RB) red-black half-sweeps, red first.
+template <typename T, bool HAS_B, bool RB>
 __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
     constexpr int W = VecW<T>::W;
     const int lb = logical_block(a.xcd_remap, a.grid);
@@ -247,7 +248,9 @@ __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierC
         for (int s = 1; s <= sc; ++s) {
             const int lo = (r0 == 1) ? 1 : r0 - (sc - s);
             const int hi = (r1 == ny - 1) ? ny - 1 : r1 + (sc - s);
-            resident_rows<T, HAS_B>(S, D, Bt, lo - e0, hi - e0, tm);
+            // colour of this half-sweep: half-sweeps done so far in the task, mod 2
+            const int parity = (n - remaining + s - 1) & 1;
+            resident_rows<T, HAS_B, RB>(S, D, Bt, lo - e0, hi - e0, tm, e0, parity);
             __syncthreads();
             T* t = S;
             S = D;
@@ -501,9 +504,28 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
         double res = 0.0;
         int64_t errs = 0;
         int status = PK_OK;
-        if (kind == PK_SWEEP) {
+        if (kind == PK_SWEEP_RB) {
+            // n red-black iterations = 2n half-sweeps, each computed into the other
+            // buffer with the other colour copied (the in-place result: a node
+            // never reads its own colour)
             if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
-                resident_sweep_task<T, HAS_B>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
+                resident_sweep_task<T, HAS_B, true>(a, 2 * n, cur, bc, reinterpret_cast<T*>(pk_lds));
+            } else if constexpr (LAYOUT == PK_LAYOUT_REGISTER) {
+                status = PK_EINVAL;
+            } else {
+                for (int s = 0; s < 2 * n;) {
+                    const int k = min(a.pass_sweeps, 2 * n - s);
+                    stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), static_cast<T*>(a.u[cur ^ 1]), k,
+                                          s & 1);
+                    grid_barrier(bc, bc.broken);
+                    cur ^= 1;
+                    s += k;
+                }
+            }
+            if (status == PK_OK) sweeps += n;
+        } else if (kind == PK_SWEEP) {
+            if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
+                resident_sweep_task<T, HAS_B, false>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
             } else if constexpr (LAYOUT == PK_LAYOUT_REGISTER) {
                 reg_sweep_task<T, HAS_B>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
             } else {
@@ -553,8 +575,8 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
 
 // ---- launch-per-sweep baseline and setup kernels ----------------------------
 template <typename T, bool HAS_B>
-__global__ void __launch_bounds__(1024) pk_sweep_launch(pk_kargs a, int src) {
-    stream_sweep<T, HAS_B>(a, static_cast<const T*>(a.u[src]), static_cast<T*>(a.u[src ^ 1]));
+__global__ void __launch_bounds__(1024) pk_sweep_launch(pk_kargs a, int src, int parity) {
+    stream_sweep<T, HAS_B>(a, static_cast<const T*>(a.u[src]), static_cast<T*>(a.u[src ^ 1]), parity);
 }
 
 template <typename T, bool HAS_B>
@@ -612,14 +634,14 @@ const void* pkk_sweep_fn(int dtype, bool has_b) {
 }
 
 hipError_t pkk_launch_sweep(int dtype, bool has_b, const pk_kargs& a, int threads, int src,
-                            hipStream_t s) {
+                            int parity, hipStream_t s) {
     const dim3 g(a.grid), b(threads);
     if (dtype == PK_F64) {
-        if (has_b) hipLaunchKernelGGL((pk_sweep_launch<double, true>), g, b, 0, s, a, src);
-        else hipLaunchKernelGGL((pk_sweep_launch<double, false>), g, b, 0, s, a, src);
+        if (has_b) hipLaunchKernelGGL((pk_sweep_launch<double, true>), g, b, 0, s, a, src, parity);
+        else hipLaunchKernelGGL((pk_sweep_launch<double, false>), g, b, 0, s, a, src, parity);
     } else {
-        if (has_b) hipLaunchKernelGGL((pk_sweep_launch<float, true>), g, b, 0, s, a, src);
-        else hipLaunchKernelGGL((pk_sweep_launch<float, false>), g, b, 0, s, a, src);
+        if (has_b) hipLaunchKernelGGL((pk_sweep_launch<float, true>), g, b, 0, s, a, src, parity);
+        else hipLaunchKernelGGL((pk_sweep_launch<float, false>), g, b, 0, s, a, src, parity);
     }
     return hipGetLastError();
 }

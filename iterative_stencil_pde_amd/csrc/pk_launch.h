@@ -10,9 +10,10 @@ const void* pkk_persistent_fn(int dtype, bool has_b, int layout);
 // Kernel symbol of the one-sweep kernel (for the occupancy query).
 const void* pkk_sweep_fn(int dtype, bool has_b);
 
-// One streaming sweep u[src] -> u[src ^ 1] with a.grid blocks of `threads`.
+// One streaming sweep u[src] -> u[src ^ 1] with a.grid blocks of `threads`;
+// parity >= 0: one red-black half-sweep of that colour instead.
 hipError_t pkk_launch_sweep(int dtype, bool has_b, const pk_kargs& a, int threads, int src,
-                            hipStream_t s);
+                            int parity, hipStream_t s);
 // Residual of u[src]: per-block partials, then one block sums them in a fixed
 // order and stores sqrt(sum) at `out` (device-visible).
 hipError_t pkk_launch_residual(int dtype, bool has_b, const pk_kargs& a, int threads, int src,

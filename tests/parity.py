@@ -59,6 +59,9 @@ def run_engine_script(w, timeout_s: float = 120.0, **opts):
             if step[0] == "sweep":
                 r = e.run(pk.PK_SWEEP, step[1], timeout_s)
                 out["results"].append(r)
+            elif step[0] == "sweep_rb":
+                r = e.run(pk.PK_SWEEP_RB, step[1], timeout_s)
+                out["results"].append(r)
             elif step[0] == "residual":
                 r = e.run(pk.PK_RESIDUAL, 0, timeout_s)
                 out["residuals"].append(r.residual)
@@ -71,8 +74,28 @@ def run_engine_script(w, timeout_s: float = 120.0, **opts):
     return out
 
 
+def run_oracle_steps(w):
+    """The oracle's answer for a script that may mix Jacobi sweeps ("sweep") and
+    red-black iterations ("sweep_rb"), one step at a time."""
+    say(f"[oracle, step by step] {w.name}")
+    u = w.u0
+    residuals, fields = [], []
+    for step in w.script:
+        if step[0] == "sweep":
+            u, _ = oracle.jacobi(u, step[1], f=w.f, h=w.h)
+        elif step[0] == "sweep_rb":
+            u, _ = oracle.rbgs(u, step[1], f=w.f, h=w.h)
+        elif step[0] == "residual":
+            residuals.append(oracle.residual(u, f=w.f, h=w.h))
+        elif step[0] == "readback":
+            fields.append(u.copy())
+    return {"residuals": residuals, "readbacks": fields, "final": u}
+
+
 def run_oracle_script(w):
     """The oracle's answer for ``w.script``: residuals and fields at each readback."""
+    if any(s[0] == "sweep_rb" for s in w.script):
+        return run_oracle_steps(w)
     say(f"[oracle] {w.name}")
     res_ck = w.residual_checkpoints
     rb_ck = w.readback_checkpoints

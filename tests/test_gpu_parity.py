@@ -274,6 +274,84 @@ def test_resident_fp64_wide():
     check_against_oracle(w, got, ref, "resident/f64")
 
 
+# ---- red-black Gauss-Seidel ------------------------------------------------
+RB_MODES = {
+    "auto": dict(mode=pk.PK_PERSISTENT),
+    "stream1": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=1),
+    "stream3": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=3),
+    "stream4": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=4),
+    "launch": dict(mode=pk.PK_LAUNCH),
+}
+
+
+@pytest.mark.parametrize("mode", sorted(RB_MODES))
+@pytest.mark.parametrize("poisson", [False, True], ids=["laplace", "poisson"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("shape", [(3, 3), (4, 4), (5, 300), (300, 5), (67, 131), (130, 257),
+                                   (33, 1030), (17, 4100)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_red_black_ragged(shape, dtype, poisson, mode):
+    """Red-black iterations (mixed with Jacobi sweeps) in every layout: each
+    half-sweep computed into the other buffer must equal the in-place oracle."""
+    ny, nx = shape
+    u, f = _random_case(ny, nx, dtype, poisson, seed=13 * ny + nx)
+    w = inputs.Workload(f"rb{ny}x{nx}", nx, ny, dtype, 0.011, u, f,
+                        [("sweep_rb", 5), ("residual",), ("sweep", 3), ("sweep_rb", 1), ("readback",),
+                         ("sweep_rb", 8), ("residual",), ("readback",)], "")
+    ref = run_oracle_script(w)
+    opts = dict(RB_MODES[mode])
+    if poisson and opts.get("pass_sweeps", 0) == 4:
+        opts["pass_sweeps"] = 3
+    got = run_engine_script(w, **opts)
+    check_against_oracle(w, got, ref, f"rb/{ny}x{nx}/{np.dtype(dtype).name}/{mode}")
+    assert got["results"][-1].sweeps_done == 17
+
+
+@pytest.mark.parametrize("blocks,halo", [(1, 0), (5, 1), (8, 3), (16, 4), (32, 7), (64, 2), (127, 1)])
+@pytest.mark.parametrize("exchange", [pk.PK_EXCHANGE_BARRIER, pk.PK_EXCHANGE_NEIGHBOR],
+                         ids=["barrier", "neighbor"])
+def test_red_black_resident(blocks, halo, exchange):
+    """The LDS tile runs 2n half-sweeps per task with m half-sweeps per exchange;
+    odd m puts exchanges between the red and black halves of an iteration."""
+    w = inputs.poisson_uniform(256, 0, 100)
+    w.script = [("residual",), ("sweep_rb", 1), ("sweep_rb", 6), ("residual",), ("sweep", 5),
+                ("sweep_rb", 13), ("residual",), ("readback",)]
+    ref = run_oracle_script(w)
+    try:
+        got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_RESIDENT,
+                                max_blocks=blocks, halo_depth=halo, exchange=exchange)
+    except pk.PkError as ex:
+        assert ex.status == pk.PK_EINVAL
+        pytest.skip(f"{blocks} blocks do not fit")
+    say(f"  grid={got['info'].grid_blocks} halo={got['info'].halo_depth}")
+    check_against_oracle(w, got, ref, f"rb-resident/{blocks}/{halo}/{exchange}")
+
+
+@pytest.mark.parametrize("name,iters", [("laplace64", 300), ("laplace1024", 40), ("laplace4096", 25),
+                                        ("poisson8192", 3)])
+def test_red_black_full_size(name, iters):
+    w = inputs.make(name)
+    w.script = [("residual",), ("sweep_rb", iters), ("residual",), ("readback",)]
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT)
+    check_against_oracle(w, got, ref, f"rb/{name}")
+
+
+def test_red_black_persistent_and_launch_agree_bitwise():
+    w = inputs.laplace_random_interior(1024, 0)
+    w.script = [("sweep_rb", 9), ("residual",), ("readback",)]
+    a = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM)
+    b = run_engine_script(w, mode=pk.PK_LAUNCH)
+    assert np.array_equal(a["final"], b["final"])
+    assert a["residuals"] == b["residuals"]
+
+
+def test_red_black_refused_by_register_layout():
+    w = inputs.poisson_uniform(256, 0)
+    with pk.Engine(w.u0, w.f, h=w.h, layout=pk.PK_LAYOUT_REGISTER, max_blocks=32) as e:
+        assert pk.pk_submit_status(e.h, pk.PK_SWEEP_RB, 1)[0] == pk.PK_EINVAL
+        assert pk.pk_submit_status(e.h, pk.PK_SWEEP_RB, pk.PK_TASK_N_MAX // 2 + 1)[0] == pk.PK_EINVAL
+
+
 # ---- the two largest workloads ---------------------------------------------
 def _golden(name):
     path = os.path.join(GOLDEN, f"{name}.json")
