@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0
 
 
 def step_tasks(w):
-    return [s for s in w.script if s[0] in ("sweep", "residual")]
+    return [s for s in w.script if s[0] in ("sweep", "sweep_rb", "residual")]
 
 
 def run_steps(e, w, steps: int, timeout_s: float = 600.0):
@@ -49,8 +49,8 @@ def run_steps(e, w, steps: int, timeout_s: float = 600.0):
     last = None
     for _ in range(steps):
         for s in step_tasks(w):
-            kind = pk.PK_SWEEP if s[0] == "sweep" else pk.PK_RESIDUAL
-            n = s[1] if s[0] == "sweep" else 0
+            kind = {"sweep": pk.PK_SWEEP, "sweep_rb": pk.PK_SWEEP_RB}.get(s[0], pk.PK_RESIDUAL)
+            n = s[1] if s[0] != "residual" else 0
             while True:
                 rc, t = pk.pk_submit_status(e.h, kind, n)
                 if rc == pk.PK_EBUSY:
@@ -89,11 +89,15 @@ def measure(w, steps, warmup, **opts):
     return t1 - t0, info0, info1
 
 
+def sweep_kind(w):
+    return "sweep_rb" if any(s[0] == "sweep_rb" for s in w.script) else "sweep"
+
+
 def sweep_only(w, steps, warmup, **opts):
     """Variant (i): the same sweeps as one SWEEP task per step, no residuals."""
     import copy
     w1 = copy.copy(w)
-    w1.script = [("sweep", w.sweeps)]
+    w1.script = [(sweep_kind(w), w.sweeps)]
     dt, _, _ = measure(w1, steps, warmup, **opts)
     return dt / (w.sweeps * steps) * 1e6
 
@@ -118,9 +122,26 @@ def overheads(w, opts, n_barrier=20000, n_handshake=2000):
             "barrier_us": round(barrier_us, 4)}
 
 
-def launch_synced(w, n, threads, blocks):
-    """Per-launch baseline with a host synchronization after every launch."""
+def launch_graph(w, n, threads, blocks, per_graph=100):
+    """HIP-graph form of the per-launch baseline: per_graph sweep launches recorded
+    once, replayed until about n sweeps have run (Jacobi only)."""
+    reps = max(1, n // per_graph)
     with pk.Engine(w.u0, w.f, h=w.h, mode=pk.PK_LAUNCH, threads=threads, max_blocks=blocks) as e:
+        e.graph_per_iter(per_graph, 1)
+        return e.graph_per_iter(per_graph, reps) / (per_graph * reps)
+
+
+def launch_synced(w, n, threads, blocks):
+    """Per-launch baseline with a host synchronization after every launch (red-black:
+    after every iteration, i.e. every second launch)."""
+    with pk.Engine(w.u0, w.f, h=w.h, mode=pk.PK_LAUNCH, threads=threads, max_blocks=blocks) as e:
+        if sweep_kind(w) == "sweep_rb":
+            for _ in range(min(n, 50)):
+                e.run(pk.PK_SWEEP_RB, 1)
+            t0 = time.perf_counter()
+            for _ in range(n):
+                e.run(pk.PK_SWEEP_RB, 1)
+            return (time.perf_counter() - t0) / n * 1e6
         e.launch_per_iter(min(n, 50), True)
         return e.launch_per_iter(n, True) / n
 
@@ -233,6 +254,9 @@ def main():
     ap.add_argument("--launch-steps", type=int, default=0,
                     help="steps for the per-launch comparison (default: same as --steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--method", default="jacobi", choices=["jacobi", "rb"],
+                    help="rb: the same script with red-black Gauss-Seidel iterations instead of "
+                         "Jacobi sweeps (one iteration = red then black half-sweep)")
     ap.add_argument("--sweeps-only", action="store_true",
                     help="a step is one SWEEP task of the workload's sweep count (no residuals)")
     ap.add_argument("--launch-only", action="store_true",
@@ -271,8 +295,10 @@ def main():
         torch.cuda.empty_cache()
 
     w = inputs.make(args.workload)
+    if args.method == "rb":
+        w.script = [("sweep_rb", s[1]) if s[0] == "sweep" else s for s in w.script]
     if args.sweeps_only:
-        w.script = [("sweep", w.sweeps)]
+        w.script = [(sweep_kind(w), w.sweeps)]
     layout = {"auto": pk.PK_LAYOUT_AUTO, "stream": pk.PK_LAYOUT_STREAM,
               "resident": pk.PK_LAYOUT_RESIDENT, "register": pk.PK_LAYOUT_REGISTER}[args.layout]
     barrier = {"auto": pk.PK_BARRIER_AUTO, "flat": pk.PK_BARRIER_FLAT,
@@ -314,12 +340,15 @@ def main():
     # per-launch baseline, same block count as the persistent grid
     lsteps = args.launch_steps or args.steps
     if args.persistent_only:
-        ldt, linfo, lvalue, lsync = float("nan"), info, float("nan"), None
+        ldt, linfo, lvalue, lsync, lgraph = float("nan"), info, float("nan"), None, None
     else:
         ldt, linfo, _ = measure(w, lsteps, 1, mode=pk.PK_LAUNCH, threads=info.threads,
                                 max_blocks=info.grid_blocks)
         lvalue = cells_per_step * lsteps / ldt / 1e9
         lsync = launch_synced(w, min(w.sweeps, 2000), info.threads, info.grid_blocks)
+        lgraph = None
+        if sweep_kind(w) == "sweep":
+            lgraph = launch_graph(w, min(w.sweeps, 10000), info.threads, info.grid_blocks)
 
     rec = {
         "metric": METRIC,
@@ -338,6 +367,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name,
+            "method": "red_black_gauss_seidel" if args.method == "rb" else "jacobi",
             "shape": [w.ny, w.nx],
             "sweeps_per_step": w.sweeps,
             "residuals_per_step": sum(1 for s in step_tasks(w) if s[0] == "residual"),
@@ -355,10 +385,13 @@ def main():
             "value": round(lvalue, 4),
             "us_per_iteration": round(ldt / (w.sweeps * lsteps) * 1e6, 4),
             "us_per_iteration_synced": round(lsync, 4),
+            "us_per_iteration_graph": round(lgraph, 4) if lgraph else None,
             "steps": lsteps,
             "grid_blocks": linfo.grid_blocks,
-            "kernel_launches_per_step": w.sweeps + 2 * sum(1 for s in step_tasks(w) if s[0] == "residual"),
+            "kernel_launches_per_step": (2 if args.method == "rb" else 1) * w.sweeps
+                                        + 2 * sum(1 for s in step_tasks(w) if s[0] == "residual"),
             "speedup_persistent": round(value / lvalue, 3),
+            "speedup_persistent_vs_graph": round(lgraph / us_iter, 3) if lgraph else None,
         },
         "overheads": fixed,
         "roofline": {

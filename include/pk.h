@@ -258,6 +258,17 @@ int pk_readback(pk_engine* e, void* dst, size_t bytes);
  * CUs, extra launches could not run), PK_EBUSY (tasks in flight), PK_EINVAL. */
 int pk_run_launch_per_iter(pk_engine* e, int n, int sync_each, double* elapsed_us);
 
+/* PK_LAUNCH engines only: the HIP-graph form of the per-launch baseline
+ * ("Persistent Kernels", "Reflections and next steps", the stronger baseline
+ * that records a standard kernel's launch sequence once and replays it). The
+ * n sweep launches are recorded once into a graph (stream capture on the
+ * engine's stream) and the graph is replayed reps times, advancing the field
+ * by n * reps sweeps. *elapsed_us (may be NULL) receives the host wall time
+ * of the replays, from the first graph launch until the last sweep finished;
+ * recording and instantiation are not included. Errors: PK_EINVAL (n < 1,
+ * reps < 1), PK_ESTATE (persistent engine, or poisoned), PK_EDEVICE. */
+int pk_run_graph_per_iter(pk_engine* e, int n, int reps, double* elapsed_us);
+
 /* Engine geometry and counters. */
 int pk_get_info(pk_engine* e, pk_info* info);
 

@@ -104,7 +104,8 @@ class Workload:
 
     @property
     def sweeps(self) -> int:
-        return sum(s[1] for s in self.script if s[0] == "sweep")
+        """Sweeps (Jacobi) plus iterations (red-black) in the script."""
+        return sum(s[1] for s in self.script if s[0] in ("sweep", "sweep_rb"))
 
     @property
     def residual_checkpoints(self) -> list:

@@ -33,7 +33,8 @@ PK_BARRIER_AUTO, PK_BARRIER_FLAT, PK_BARRIER_TWO_LEVEL, PK_BARRIER_XCD = 0, 1, 2
 PK_EXCHANGE_AUTO, PK_EXCHANGE_BARRIER, PK_EXCHANGE_NEIGHBOR = 0, 1, 2
 
 EXPORTED = ["pk_opts_default", "pk_create", "pk_submit", "pk_wait", "pk_readback",
-            "pk_run_launch_per_iter", "pk_get_info", "pk_destroy", "pk_strerror"]
+            "pk_run_launch_per_iter", "pk_run_graph_per_iter", "pk_get_info", "pk_destroy",
+            "pk_strerror"]
 
 
 class pk_opts(ctypes.Structure):
@@ -98,6 +99,8 @@ def load(path: str = LIB_PATH):
     lib.pk_readback.argtypes = [vp, vp, ctypes.c_size_t]
     lib.pk_run_launch_per_iter.restype = ip
     lib.pk_run_launch_per_iter.argtypes = [vp, ip, ip, ctypes.POINTER(ctypes.c_double)]
+    lib.pk_run_graph_per_iter.restype = ip
+    lib.pk_run_graph_per_iter.argtypes = [vp, ip, ip, ctypes.POINTER(ctypes.c_double)]
     lib.pk_get_info.restype = ip
     lib.pk_get_info.argtypes = [vp, ctypes.POINTER(pk_info)]
     lib.pk_destroy.restype = ip
@@ -186,6 +189,12 @@ def pk_run_launch_per_iter(eng: int, n: int, sync_each: bool = False) -> float:
     return us.value
 
 
+def pk_run_graph_per_iter(eng: int, n: int, reps: int) -> float:
+    us = ctypes.c_double()
+    _check(load().pk_run_graph_per_iter(eng, n, reps, ctypes.byref(us)), "pk_run_graph_per_iter")
+    return us.value
+
+
 def pk_get_info(eng: int) -> pk_info:
     i = pk_info()
     _check(load().pk_get_info(eng, ctypes.byref(i)), "pk_get_info")
@@ -232,6 +241,9 @@ class Engine:
 
     def launch_per_iter(self, n: int, sync_each: bool = False) -> float:
         return pk_run_launch_per_iter(self.h, n, sync_each)
+
+    def graph_per_iter(self, n: int, reps: int) -> float:
+        return pk_run_graph_per_iter(self.h, n, reps)
 
     def close(self):
         if self.h:

@@ -274,6 +274,49 @@ def test_resident_fp64_wide():
     check_against_oracle(w, got, ref, "resident/f64")
 
 
+# ---- HIP-graph launch baseline -----------------------------------------------
+@pytest.mark.parametrize("poisson", [False, True], ids=["laplace", "poisson"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
+def test_graph_baseline_replays(dtype, poisson):
+    """Sweeps recorded once into a graph and replayed (odd and even graph lengths,
+    eager launches and tasks in between) leave the field the oracle computes
+    for the same total number of sweeps, after every batch of replays."""
+    u, f = _random_case(130, 257, dtype, poisson, seed=99)
+    h = 0.013
+    with pk.Engine(u, f, h=h, mode=pk.PK_LAUNCH) as e:
+        done = 0
+        for kind, n, reps in (("graph", 7, 3), ("eager", 2, 0), ("graph", 4, 2), ("task", 3, 0),
+                              ("graph", 1, 5), ("graph", 9, 1)):
+            if kind == "graph":
+                us = e.graph_per_iter(n, reps)
+                assert us > 0
+                done += n * reps
+            elif kind == "eager":
+                e.launch_per_iter(n)
+                done += n
+            else:
+                e.sweep(n)
+                done += n
+            ref, _ = oracle.jacobi(u, done, f=f, h=h)
+            ok, err, tol, nonbit = field_gate(e.readback(), ref)
+            say(f"  graph batch {kind} n={n} reps={reps}: total {done} max_abs={err:.3e} non_bitwise={nonbit}")
+            assert ok and nonbit == 0
+        assert e.info().sweeps_done == done
+
+
+def test_graph_baseline_refused_for_persistent_and_bad_arguments():
+    w = inputs.laplace_top_edge(64, 0)
+    with pk.Engine(w.u0, None) as e:
+        with pytest.raises(pk.PkError) as ex:
+            e.graph_per_iter(4, 2)
+        assert ex.value.status == pk.PK_ESTATE
+    with pk.Engine(w.u0, None, mode=pk.PK_LAUNCH) as e:
+        for n, reps in ((0, 1), (1, 0), (-1, 3)):
+            with pytest.raises(pk.PkError) as ex:
+                e.graph_per_iter(n, reps)
+            assert ex.value.status == pk.PK_EINVAL
+
+
 # ---- red-black Gauss-Seidel ------------------------------------------------
 RB_MODES = {
     "auto": dict(mode=pk.PK_PERSISTENT),
