@@ -194,7 +194,35 @@ struct BarrierCtx {
     uint32_t xmembers;   // XCD barrier: blocks on this XCD
     uint32_t xgroups;    // XCD barrier: XCDs with at least one block
     uint32_t nbr_epoch;  // neighbour exchanges completed (identical in every block)
+    uint32_t nbar;       // grid barriers passed (identical in every block)
+    // task carry (leader thread only): the slot word of task carry_seq, read
+    // ahead once at task start; compared at the first ordered barrier at least
+    // carry_age ticks later (so the read has returned and stalls nothing: loads
+    // complete in order, and the barrier's own atomics would wait behind it)
+    uint64_t carry_seq;
+    uint64_t carry_word;
+    uint64_t carry_t0;
+    uint64_t carry_age;
+    bool carry_pending;
 };
+
+// Leader only, before it arrives at an ordered grid barrier: if the task read
+// ahead has been published by the host, hand it on through the barrier. The
+// stores are ordered before the barrier's arrival, so every block sees them
+// after the barrier. One try per task: a task not yet published then goes the
+// ordinary way (poll, broadcast barrier).
+__device__ __forceinline__ void carry_at_barrier(BarrierCtx& bc) {
+    if (!bc.carry_pending || wall_clock64() - bc.carry_t0 < bc.carry_age) return;
+    bc.carry_pending = false;
+    const uint64_t w = bc.carry_word;
+    if (static_cast<uint32_t>(w >> 32) != static_cast<uint32_t>(bc.carry_seq)) return;
+    pk_carry* c = &bc.st->carry[bc.carry_seq & 1];
+    __hip_atomic_store(&c->kind, static_cast<int32_t>((w >> 28) & 0xF), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c->n, static_cast<int32_t>(w & PK_TASK_N_MAX), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c->seq, bc.carry_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Lane 0 spins until *gen reaches `target` (relaxed loads, bounded in time).
 __device__ __forceinline__ void spin_until(BarrierCtx& bc, uint32_t* gen, uint32_t target) {
@@ -236,6 +264,7 @@ __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); 
 // Blocks are grouped by the XCD they actually run on, read from the hardware
 // at launch, so placement does not affect correctness.
 __device__ __forceinline__ void xcd_barrier(BarrierCtx& bc) {
+    if (threadIdx.x == 0) carry_at_barrier(bc);
     wait_vm();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -287,10 +316,12 @@ __device__ __forceinline__ void neighbor_sync(BarrierCtx& bc, uint32_t* nbr, int
 }
 
 __device__ __forceinline__ void grid_barrier(BarrierCtx& bc, bool relaxed = false) {
+    bc.nbar += 1;
     if (bc.xcd && !relaxed && bc.grid > 1) {
         xcd_barrier(bc);
         return;
     }
+    if (threadIdx.x == 0 && !relaxed) carry_at_barrier(bc);
     __syncthreads();
     if (threadIdx.x == 0 && bc.grid > 1) {
         const uint32_t target = bc.epoch + 1;

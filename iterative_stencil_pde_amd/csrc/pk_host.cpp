@@ -562,6 +562,9 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     const double idle_s = o.idle_timeout_s > 0 ? o.idle_timeout_s : 120.0;
     e->ka.idle_ticks = static_cast<uint64_t>(idle_s * wclk_khz * 1000.0);
     e->ka.spin_ticks = static_cast<uint64_t>((idle_s + 10.0) * wclk_khz * 1000.0);
+    // a read of host memory over the bus takes ~1-2 us; compare a read-ahead
+    // task slot only 2.5 us after issuing it
+    e->ka.carry_age_ticks = static_cast<uint64_t>(2.5e-6 * wclk_khz * 1000.0);
     PK_TRY(hipStreamSynchronize(e->stream));
     e->ring.attach(e->h_mail);
 

@@ -391,7 +391,7 @@ template <typename T, bool HAS_B, int LAYOUT>
 __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_kargs a) {
     extern __shared__ __align__(16) unsigned char pk_lds[];
     __shared__ double s_red[16];
-    __shared__ int s_kind, s_n, s_exit;
+    __shared__ int s_kind, s_n, s_exit, s_carried;
     __shared__ unsigned long long s_seq;
 
     BarrierCtx bc;
@@ -407,6 +407,12 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
     bc.xmembers = 1;
     bc.xgroups = 1;
     bc.nbr_epoch = 0;
+    bc.nbar = 0;
+    bc.carry_seq = 0;
+    bc.carry_word = 0;
+    bc.carry_t0 = 0;
+    bc.carry_age = a.carry_age_ticks;
+    bc.carry_pending = false;
     if (a.barrier_kind == PK_BARRIER_XCD && a.grid > 1 && !bc.broken) {
         // count the blocks on each XCD (one flat barrier, generation 1), then
         // switch to the XCD barrier, whose counters start from zero
@@ -430,46 +436,68 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
     int cur = a.cur0;
     int64_t sweeps = 0;
     uint64_t next_seq = 1;
+    bool may_carry = false;  // the last task passed an ordered barrier (uniform)
     uint32_t stamp_round = 0;
     pk_mailbox* mail = a.mail;
 
     for (;;) {
-        if (leader) {
-            uint32_t fault = __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            int kind = PK_EXIT, nn = 0;
-            if (!bc.faulted && fault == 0) {
-                const uint64_t t0 = wall_clock64();
-                bool idle = false;
-                // the slot word carries the whole task: poll it until its
-                // sequence half is the one expected (one bus read per poll)
-                const uint64_t* slot = &mail->slot[next_seq % PK_RING].word;
-                uint64_t w = 0;
-                for (;;) {
-                    w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    if (static_cast<uint32_t>(w >> 32) == static_cast<uint32_t>(next_seq)) break;
-                    __builtin_amdgcn_s_sleep(1);
-                    if (wall_clock64() - t0 > a.idle_ticks) {
-                        idle = true;
-                        break;
+        // Fast path: the previous task's last ordered barrier carried this task
+        // in (the leader had read it ahead); every block reads the same carry
+        // word after that barrier, so all take the same path.
+        if (threadIdx.x == 0) {
+            s_carried = 0;
+        }
+        if (may_carry && threadIdx.x == 0) {
+            const pk_carry* c = &a.st->carry[next_seq & 1];
+            const uint64_t cs = __hip_atomic_load(&c->seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_carried = cs == next_seq ? 1 : 0;
+            if (s_carried) {
+                s_kind = __hip_atomic_load(&c->kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_n = __hip_atomic_load(&c->n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_seq = next_seq;
+            }
+        }
+        __syncthreads();
+        if (!s_carried) {
+            if (leader) {
+                uint32_t fault = __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                int kind = PK_EXIT, nn = 0;
+                if (!bc.faulted && fault == 0) {
+                    const uint64_t t0 = wall_clock64();
+                    bool idle = false;
+                    // the slot word carries the whole task: poll it until its
+                    // sequence half is the one expected (one bus read per poll)
+                    const uint64_t* slot = &mail->slot[next_seq % PK_RING].word;
+                    uint64_t w = 0;
+                    for (;;) {
+                        w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                        if (static_cast<uint32_t>(w >> 32) == static_cast<uint32_t>(next_seq)) break;
+                        __builtin_amdgcn_s_sleep(1);
+                        if (wall_clock64() - t0 > a.idle_ticks) {
+                            idle = true;
+                            break;
+                        }
+                    }
+                    if (idle) {
+                        __hip_atomic_store(&a.st->fault, static_cast<uint32_t>(PK_FAULT_IDLE_TIMEOUT),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    } else {
+                        kind = static_cast<int>((w >> 28) & 0xF);
+                        nn = static_cast<int>(w & PK_TASK_N_MAX);
                     }
                 }
-                if (idle) {
-                    __hip_atomic_store(&a.st->fault, static_cast<uint32_t>(PK_FAULT_IDLE_TIMEOUT),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                } else {
-                    kind = static_cast<int>((w >> 28) & 0xF);
-                    nn = static_cast<int>(w & PK_TASK_N_MAX);
-                }
+                a.st->task_seq = next_seq;
+                a.st->task_kind = kind;
+                a.st->task_n = nn;
             }
-            a.st->task_seq = next_seq;
-            a.st->task_kind = kind;
-            a.st->task_n = nn;
+            grid_barrier(bc);
+            if (threadIdx.x == 0) {
+                s_kind = __hip_atomic_load(&a.st->task_kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_n = __hip_atomic_load(&a.st->task_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_seq = __hip_atomic_load(&a.st->task_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
-        grid_barrier(bc);
         if (threadIdx.x == 0) {
-            s_kind = __hip_atomic_load(&a.st->task_kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_n = __hip_atomic_load(&a.st->task_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_seq = __hip_atomic_load(&a.st->task_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const uint32_t f = __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             s_exit = (bc.faulted || f != 0 || s_kind == PK_EXIT) ? 1 : 0;
         }
@@ -477,6 +505,18 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
         const int kind = s_kind, n = s_n;
         const uint64_t seq = s_seq;
         const uint64_t t_begin = leader ? wall_clock64() : 0;
+        const uint32_t nbar0 = bc.nbar;
+        // read the next slot ahead for work tasks (not for the timing tasks, and
+        // not for empty sweeps, whose only barrier comes at once)
+        const bool work = ((kind == PK_SWEEP || kind == PK_SWEEP_RB) && n > 0) || kind == PK_RESIDUAL ||
+                          kind == PK_TASK_READBACK;
+        if (leader && !bc.broken && work) {
+            bc.carry_seq = seq + 1;
+            bc.carry_t0 = wall_clock64();
+            bc.carry_word = __hip_atomic_load(&mail->slot[(seq + 1) % PK_RING].word, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_SYSTEM);
+            bc.carry_pending = true;
+        }
 
         if (s_exit) {
             if (leader) {
@@ -556,6 +596,14 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
         } else {
             status = PK_EINVAL;
         }
+        // A carry is published only at an ordered barrier of the task before the
+        // one it carries. The leader therefore writes carry[(seq + 1) & 1] only
+        // after every block has passed either that barrier or, on the ordinary
+        // path, the broadcast barrier of this task, i.e. after every block read
+        // carry[(seq - 1) & 1], the same word. A task without a barrier carries
+        // nothing, so the next one starts the ordinary way.
+        if (leader) bc.carry_pending = false;  // never publish it outside its task
+        may_carry = !bc.broken && bc.nbar != nbar0;
         if (leader) {
             pk_done_rec* d = &mail->done[seq % PK_RING];
             d->kind = kind;
@@ -568,8 +616,8 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
             d->cur = cur;
             d->seq = seq;
             __hip_atomic_store(&mail->done_seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-            next_seq = seq + 1;
         }
+        next_seq = seq + 1;
     }
 }
 

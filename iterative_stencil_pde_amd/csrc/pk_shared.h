@@ -69,6 +69,14 @@ struct alignas(256) pk_word256 {
     uint32_t v;
 };
 
+// A task handed on by the leader inside the previous task's barrier, so the
+// next task needs no broadcast barrier of its own; indexed by seq & 1.
+struct alignas(PK_LINE) pk_carry {
+    uint64_t seq;
+    int32_t kind;
+    int32_t n;
+};
+
 struct pk_dev_state {
     alignas(PK_LINE) uint32_t bar_count;   // arrivals, monotonically increasing
     alignas(PK_LINE) uint32_t bar_gen;     // completed barrier generations
@@ -87,6 +95,7 @@ struct pk_dev_state {
     alignas(PK_LINE) uint64_t task_seq;    // task broadcast (written by the leader)
     int32_t task_kind;
     int32_t task_n;
+    pk_carry carry[2];
     alignas(PK_LINE) uint32_t fault;       // device-side fault, read by every block
     alignas(PK_LINE) uint64_t stamp_errors;
 };
@@ -120,6 +129,7 @@ struct pk_kargs {
     uint32_t flags;
     uint64_t idle_ticks;   // wall-clock ticks without a task before leaving
     uint64_t spin_ticks;   // wall-clock ticks a barrier may wait before faulting
+    uint64_t carry_age_ticks;  // wall-clock ticks after which a read-ahead task slot has arrived
     pk_dev_state* st;
     pk_mailbox* mail;      // device-visible address of the host mailbox
     double* partials;      // one double per block
