@@ -393,7 +393,8 @@ def main():
             "speedup_persistent": round(value / lvalue, 3),
             "speedup_persistent_vs_graph": round(lgraph / us_iter, 3) if lgraph else None,
         },
-        "overheads": fixed,
+        "overheads": dict(fixed, tasks_carried=int(info_end.tasks_carried),
+                          tasks_done=int(info_end.tasks_done)),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2) if achieved else None,

@@ -99,6 +99,8 @@ extern "C" {
                       /*   half-sweeps into the other buffer, so `cur` flips as for */
                       /*   SWEEP. n <= PK_TASK_N_MAX / 2; not in the REGISTER layout.*/
                       /*   sweeps_done counts iterations.                           */
+#define PK_SWEEP_UNTIL 7 /* Jacobi sweeps until the residual reaches a tolerance:   */
+                      /*   submitted with pk_submit_until (see there), not pk_submit */
 
 /* ---- option flags ------------------------------------------------------- */
 /* Debug only: the grid barrier drops its release/acquire ordering (relaxed
@@ -207,6 +209,9 @@ typedef struct pk_info {
     int64_t sweeps_done;
     int64_t tasks_done;
     int64_t kernel_launches; /* launches made so far (persistent: 1)                     */
+    int64_t tasks_carried;   /* PERSISTENT: tasks that started without a poll and a      */
+                             /* broadcast barrier: the previous task's barrier carried */
+                             /* them (the host had queued them ahead)                   */
 } pk_info;
 
 typedef struct pk_engine pk_engine;
@@ -234,6 +239,21 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* o,
  * kind in PK_LAUNCH mode), PK_EBUSY (ring full: wait on an older ticket first), PK_ESTATE
  * (after EXIT, or on a poisoned engine). */
 int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket);
+
+/* Queue a PK_SWEEP_UNTIL task: Jacobi sweeps with an in-kernel stop on a
+ * residual threshold ("Persistent Kernels", "Reflections and next steps",
+ * GPU-side scheduling; "Grid-Wide Barriers and Persistent Work Queues", "What
+ * the barrier buys": the convergence check as a grid reduction whose result
+ * every block sees). The task computes R (as PK_RESIDUAL) of the current
+ * field; while R > tol and fewer than max_sweeps sweeps are done, it runs
+ * min(check_every, sweeps left) sweeps and computes R again. Every block sums
+ * the per-block partials in the same fixed order, so all blocks take the same
+ * decision without a further broadcast. pk_result.residual is the last R,
+ * sweeps_done the running total. In PK_LAUNCH mode the same loop runs on the
+ * host, synchronously, inside this call (each check waits for the GPU).
+ * Errors: PK_EINVAL (max_sweeps < 0 or > PK_TASK_N_MAX, check_every < 1,
+ * tol < 0 or not a number), otherwise as pk_submit. */
+int pk_submit_until(pk_engine* e, int max_sweeps, int check_every, double tol, uint64_t* ticket);
 
 /* Busy-poll (no sleep) until ticket has completed, at most timeout_s seconds
  * (<= 0 => 60 s). r (may be NULL) receives that task's result.

@@ -532,7 +532,7 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     }
     PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_st), sizeof(pk_dev_state)));
     PK_TRY(hipMemsetAsync(e->d_st, 0, sizeof(pk_dev_state), e->stream));
-    PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_partials), sizeof(double) * e->plan.grid));
+    PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_partials), sizeof(double) * 2 * e->plan.grid));
     PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_stamp), sizeof(uint32_t) * 2 * 64 * e->plan.grid));
     PK_TRY(hipMemsetAsync(e->d_stamp, 0, sizeof(uint32_t) * 2 * 64 * e->plan.grid, e->stream));
     const size_t nbr_bytes = sizeof(uint32_t) * PK_NBR_WORDS * e->plan.grid;
@@ -644,6 +644,65 @@ int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket) {
     const int rc = e->ring.publish(t.kind, t.n, &seq);
     if (rc != PK_OK) return rc;
     if (t.kind == PK_EXIT) e->state = EXITED;
+    if (ticket) *ticket = seq;
+    return PK_OK;
+}
+
+int pk_submit_until(pk_engine* e, int max_sweeps, int check_every, double tol, uint64_t* ticket) {
+    if (!e) return PK_EINVAL;
+    if (e->state != RUNNING) return PK_ESTATE;
+    if (max_sweeps < 0 || max_sweeps > PK_TASK_N_MAX || check_every < 1 || !(tol >= 0.0)) return PK_EINVAL;
+    if (e->mode == PK_LAUNCH) {
+        // the same loop on the host; every check waits for the GPU
+        if (hipStreamSynchronize(e->stream) != hipSuccess) { e->state = POISONED; return PK_EDEVICE; }
+        const uint64_t seq = e->lresults.size() + 1;
+        if (seq > PK_RING) {  // the event and residual slot of an older ticket are reused
+            pk_result& old = e->lresults[seq - PK_RING - 1];
+            if (old.kind == PK_RESIDUAL) old.residual = e->h_lres[(seq - PK_RING) % PK_RING];
+        }
+        double* slot = e->d_lres + seq % PK_RING;
+        auto residual = [&](double* out) -> hipError_t {
+            hipError_t he = pkk_launch_residual(e->dtype, e->has_b, e->ka, e->plan.threads, e->cur, slot,
+                                                e->stream);
+            e->launches += 2;
+            if (he == hipSuccess) he = hipStreamSynchronize(e->stream);
+            if (he == hipSuccess) *out = e->h_lres[seq % PK_RING];
+            return he;
+        };
+        double rres = 0.0;
+        int done = 0;
+        hipError_t he = residual(&rres);
+        while (he == hipSuccess && !(rres <= tol) && done < max_sweeps) {
+            const int k = std::min(check_every, max_sweeps - done);
+            for (int s = 0; s < k && he == hipSuccess; ++s) {
+                he = pkk_launch_sweep(e->dtype, e->has_b, e->ka, e->plan.threads, e->cur, -1, e->stream);
+                e->cur ^= 1;
+                ++e->launches;
+            }
+            done += k;
+            if (he == hipSuccess) he = residual(&rres);
+        }
+        if (he == hipSuccess) he = hipEventRecord(e->ev_ticket[seq % PK_RING], e->stream);
+        if (he != hipSuccess) { e->state = POISONED; return PK_EDEVICE; }
+        e->sweeps_done += done;
+        pk_result r{};
+        r.kind = PK_SWEEP_UNTIL;
+        r.residual = rres;
+        r.sweeps_done = e->sweeps_done;
+        e->lresults.push_back(r);
+        if (ticket) *ticket = seq;
+        return PK_OK;
+    }
+    if (__atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE)) {
+        e->state = EXITED;
+        return PK_ESTATE;
+    }
+    pk_param prm{};
+    prm.tol = tol;
+    prm.every = check_every;
+    uint64_t seq = 0;
+    const int rc = e->ring.publish(PK_SWEEP_UNTIL, max_sweeps, &seq, &prm);
+    if (rc != PK_OK) return rc;
     if (ticket) *ticket = seq;
     return PK_OK;
 }
@@ -817,6 +876,7 @@ int pk_get_info(pk_engine* e, pk_info* info) {
     if (e->mode == PK_PERSISTENT) {
         info->sweeps_done = e->ring.sweeps_seen();
         info->tasks_done = static_cast<int64_t>(e->ring.done_seen());
+        info->tasks_carried = static_cast<int64_t>(e->ring.carried_seen());
         // once the kernel has said it is leaving, its end event completes promptly
         if (__atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE) &&
             hipEventSynchronize(e->ev_end) == hipSuccess) {

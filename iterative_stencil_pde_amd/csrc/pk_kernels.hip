@@ -382,6 +382,50 @@ __device__ int64_t stamp_task(const pk_kargs& a, int n, uint32_t& round, Barrier
 // ---------------------------------------------------------------------------
 // Blocks of up to 1024 threads (128 VGPRs per lane); the register-tile layout
 // uses 512 so that each lane can hold 16 rows of u and b (256 VGPRs per lane).
+// n Jacobi sweeps of the field in u[cur] in the engine's layout (cur flips).
+template <typename T, bool HAS_B, int LAYOUT>
+__device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
+    if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
+        resident_sweep_task<T, HAS_B, false>(a, n, cur, bc, lds);
+    } else if constexpr (LAYOUT == PK_LAYOUT_REGISTER) {
+        reg_sweep_task<T, HAS_B>(a, n, cur, bc, lds);
+    } else {
+        for (int s = 0; s < n;) {
+            const int k = min(a.pass_sweeps, n - s);
+            stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), static_cast<T*>(a.u[cur ^ 1]), k);
+            grid_barrier(bc, bc.broken);
+            cur ^= 1;
+            s += k;
+        }
+    }
+}
+
+// One residual round: each block's partial goes to the half of `partials` of
+// this round's parity, a grid barrier, then the sum in a fixed order (blocks in
+// order, the same code everywhere, so bitwise the same in every block). Only
+// the blocks that ask (all) read the partials back. Rounds alternate halves: a
+// block writes round r + 2 only after passing round r + 1's barrier, which every
+// reader of round r reaches only after its reads. Returns R in every thread of
+// a block that asked (0 elsewhere).
+template <typename T, bool HAS_B>
+__device__ __forceinline__ double residual_round(const pk_kargs& a, int cur, BarrierCtx& bc,
+                                                 uint32_t& round, double* s_red, bool all) {
+    double* part = a.partials + static_cast<size_t>(round & 1u) * a.grid;
+    round += 1;
+    const double p = stream_residual_block<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), s_red);
+    if (threadIdx.x == 0) part[blockIdx.x] = p;
+    grid_barrier(bc);
+    double r = 0.0;
+    if (all || blockIdx.x == 0) {
+        const double tot = sum_partials(part, a.grid);
+        if (threadIdx.x == 0) s_red[0] = sqrt(tot);
+        __syncthreads();
+        r = s_red[0];
+        __syncthreads();
+    }
+    return r;
+}
+
 template <int LAYOUT>
 struct PkMaxThreads {
     static constexpr int value = LAYOUT == PK_LAYOUT_REGISTER ? 512 : 1024;
@@ -391,7 +435,8 @@ template <typename T, bool HAS_B, int LAYOUT>
 __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_kargs a) {
     extern __shared__ __align__(16) unsigned char pk_lds[];
     __shared__ double s_red[16];
-    __shared__ int s_kind, s_n, s_exit, s_carried;
+    __shared__ int s_kind, s_n, s_exit, s_carried, s_every;
+    __shared__ double s_tol;
     __shared__ unsigned long long s_seq;
 
     BarrierCtx bc;
@@ -437,6 +482,7 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
     int64_t sweeps = 0;
     uint64_t next_seq = 1;
     bool may_carry = false;  // the last task passed an ordered barrier (uniform)
+    uint32_t res_round = 0;  // residual rounds so far (uniform): partials half
     uint32_t stamp_round = 0;
     pk_mailbox* mail = a.mail;
 
@@ -509,7 +555,7 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
         // read the next slot ahead for work tasks (not for the timing tasks, and
         // not for empty sweeps, whose only barrier comes at once)
         const bool work = ((kind == PK_SWEEP || kind == PK_SWEEP_RB) && n > 0) || kind == PK_RESIDUAL ||
-                          kind == PK_TASK_READBACK;
+                          kind == PK_SWEEP_UNTIL || kind == PK_TASK_READBACK;
         if (leader && !bc.broken && work) {
             bc.carry_seq = seq + 1;
             bc.carry_t0 = wall_clock64();
@@ -532,6 +578,7 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
                     d->t_end = t_begin;
                     d->errors = 0;
                     d->cur = cur;
+                    d->carried = s_carried;
                     d->seq = seq;
                     __hip_atomic_store(&mail->done_seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
                 }
@@ -569,23 +616,34 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
             } else if constexpr (LAYOUT == PK_LAYOUT_REGISTER) {
                 reg_sweep_task<T, HAS_B>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
             } else {
-                for (int s = 0; s < n;) {
-                    const int k = min(a.pass_sweeps, n - s);
-                    stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), static_cast<T*>(a.u[cur ^ 1]), k);
-                    grid_barrier(bc, bc.broken);
-                    cur ^= 1;
-                    s += k;
-                }
+                sweeps_task<T, HAS_B, LAYOUT>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
             }
             sweeps += n;
         } else if (kind == PK_RESIDUAL) {
-            const double part = stream_residual_block<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), s_red);
-            if (threadIdx.x == 0) a.partials[blockIdx.x] = part;
-            grid_barrier(bc);
-            if (blockIdx.x == 0) {
-                const double tot = sum_partials(a.partials, a.grid);
-                if (threadIdx.x == 0) res = sqrt(tot);
+            res = residual_round<T, HAS_B>(a, cur, bc, res_round, s_red, false);
+        } else if (kind == PK_SWEEP_UNTIL) {
+            // parameters: each block acquires the slot word the host released
+            // after writing them, then reads them
+            if (threadIdx.x == 0) {
+                (void)__hip_atomic_load(&mail->slot[seq % PK_RING].word, __ATOMIC_ACQUIRE,
+                                        __HIP_MEMORY_SCOPE_SYSTEM);
+                const pk_param* prm = &mail->param[seq % PK_RING];
+                s_tol = __hip_atomic_load(&prm->tol, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                s_every = __hip_atomic_load(&prm->every, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
             }
+            __syncthreads();
+            const double tol = s_tol;
+            const int every = s_every;
+            double r = residual_round<T, HAS_B>(a, cur, bc, res_round, s_red, true);
+            int done = 0;
+            while (!(r <= tol) && done < n) {  // the same decision in every block
+                const int k = min(every, n - done);
+                sweeps_task<T, HAS_B, LAYOUT>(a, k, cur, bc, reinterpret_cast<T*>(pk_lds));
+                done += k;
+                r = residual_round<T, HAS_B>(a, cur, bc, res_round, s_red, true);
+            }
+            sweeps += done;
+            res = r;
         } else if (kind == PK_TASK_READBACK) {
             readback_task<T>(a, cur);
             grid_barrier(bc);
@@ -614,6 +672,7 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
             d->t_end = wall_clock64();
             d->errors = errs;
             d->cur = cur;
+            d->carried = s_carried;
             d->seq = seq;
             __hip_atomic_store(&mail->done_seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
         }

@@ -32,6 +32,7 @@ struct DoneInfo {
     uint64_t t_begin = 0, t_end = 0;
     int64_t errors = 0;
     int cur = 0;
+    int carried = 0;
 };
 
 inline void cpu_relax() {
@@ -46,13 +47,15 @@ public:
         m_ = m;
         next_ = 1;
         harvested_ = 0;
+        carried_ = 0;
         done_.assign(1, DoneInfo{});
     }
 
     // Publish a task. PK_EBUSY when PK_RING tasks are already in flight.
-    int publish(int kind, int n, uint64_t* seq) {
+    int publish(int kind, int n, uint64_t* seq, const pk_param* prm = nullptr) {
         harvest();
         if (next_ - 1 - harvested_ >= PK_RING) return PK_EBUSY;
+        if (prm) m_->param[next_ % PK_RING] = *prm;  // ordered before the slot's release
         __atomic_store_n(&m_->slot[next_ % PK_RING].word, pk_slot_pack(next_, kind, n),
                          __ATOMIC_RELEASE);
         if (seq) *seq = next_;
@@ -76,6 +79,8 @@ public:
             x.t_end = r.t_end;
             x.errors = r.errors;
             x.cur = r.cur;
+            x.carried = r.carried;
+            carried_ += r.carried ? 1 : 0;
             done_.push_back(x);
             harvested_ = s;
         }
@@ -113,11 +118,13 @@ public:
     uint64_t issued() const { return next_ - 1; }
     int64_t sweeps_seen() const { return harvested_ ? done_[harvested_].sweeps_done : 0; }
     int last_cur() const { return harvested_ ? done_[harvested_].cur : 0; }
+    uint64_t carried_seen() const { return carried_; }
 
 private:
     pk_mailbox* m_ = nullptr;
     uint64_t next_ = 1;
     uint64_t harvested_ = 0;
+    uint64_t carried_ = 0;
     std::vector<DoneInfo> done_;  // index = ticket
 };
 

@@ -52,6 +52,15 @@ struct alignas(PK_LINE) pk_done_rec {
     uint64_t t_end;
     int64_t errors;
     int32_t cur;  // buffer index that holds the whole field after this task
+    int32_t carried;  // 1: the task was handed on by the previous task's barrier
+};
+
+// Parameters of a PK_SWEEP_UNTIL task, written by the host before it releases
+// the task's slot word.
+struct alignas(PK_LINE) pk_param {
+    double tol;
+    int32_t every;
+    int32_t pad;
 };
 
 struct pk_mailbox {
@@ -59,6 +68,7 @@ struct pk_mailbox {
     alignas(PK_LINE) uint32_t exited;    // device writes 1 when the kernel leaves
     alignas(PK_LINE) uint32_t fault;     // device writes a PK_FAULT_* code
     pk_slot slot[PK_RING];
+    pk_param param[PK_RING];
     pk_done_rec done[PK_RING];
 };
 
@@ -132,7 +142,7 @@ struct pk_kargs {
     uint64_t carry_age_ticks;  // wall-clock ticks after which a read-ahead task slot has arrived
     pk_dev_state* st;
     pk_mailbox* mail;      // device-visible address of the host mailbox
-    double* partials;      // one double per block
+    double* partials;      // residual partials: 2 x grid doubles (alternating rounds)
     void* staging;         // readback target (pinned host, device-visible)
     uint32_t* stamp;       // 2 x grid x 64 words for the visibility check
     uint32_t* nbr;         // neighbour exchange flags, PK_NBR_WORDS words per block

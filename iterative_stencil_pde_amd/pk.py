@@ -26,13 +26,13 @@ PK_OK, PK_EINVAL, PK_ENOMEM, PK_ELAUNCH, PK_EDEVICE, PK_EBUSY, PK_ESTATE, PK_ETI
 PK_F32, PK_F64 = 0, 1
 PK_PERSISTENT, PK_LAUNCH = 0, 1
 PK_LAYOUT_AUTO, PK_LAYOUT_STREAM, PK_LAYOUT_RESIDENT, PK_LAYOUT_REGISTER = 0, 1, 2, 3
-PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP, PK_SWEEP_RB = 1, 2, 3, 4, 5, 6
+PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP, PK_SWEEP_RB, PK_SWEEP_UNTIL = 1, 2, 3, 4, 5, 6, 7
 PK_DBG_BROKEN_BARRIER = 0x1
 PK_TASK_N_MAX = 0x0FFFFFFF
 PK_BARRIER_AUTO, PK_BARRIER_FLAT, PK_BARRIER_TWO_LEVEL, PK_BARRIER_XCD = 0, 1, 2, 3
 PK_EXCHANGE_AUTO, PK_EXCHANGE_BARRIER, PK_EXCHANGE_NEIGHBOR = 0, 1, 2
 
-EXPORTED = ["pk_opts_default", "pk_create", "pk_submit", "pk_wait", "pk_readback",
+EXPORTED = ["pk_opts_default", "pk_create", "pk_submit", "pk_submit_until", "pk_wait", "pk_readback",
             "pk_run_launch_per_iter", "pk_run_graph_per_iter", "pk_get_info", "pk_destroy",
             "pk_strerror"]
 
@@ -66,7 +66,8 @@ class pk_info(ctypes.Structure):
                 ("strips", ctypes.c_int), ("barrier", ctypes.c_int), ("pass_sweeps", ctypes.c_int),
                 ("exchange", ctypes.c_int), ("lds_bytes", ctypes.c_size_t),
                 ("kernel_ms", ctypes.c_double), ("sweeps_done", ctypes.c_int64),
-                ("tasks_done", ctypes.c_int64), ("kernel_launches", ctypes.c_int64)]
+                ("tasks_done", ctypes.c_int64), ("kernel_launches", ctypes.c_int64),
+                ("tasks_carried", ctypes.c_int64)]
 
 
 class PkError(RuntimeError):
@@ -93,6 +94,8 @@ def load(path: str = LIB_PATH):
     lib.pk_create.argtypes = [ip, ip, vp, vp, ctypes.POINTER(pk_opts), ctypes.POINTER(vp)]
     lib.pk_submit.restype = ip
     lib.pk_submit.argtypes = [vp, pk_task, ctypes.POINTER(ctypes.c_uint64)]
+    lib.pk_submit_until.restype = ip
+    lib.pk_submit_until.argtypes = [vp, ip, ip, ctypes.c_double, ctypes.POINTER(ctypes.c_uint64)]
     lib.pk_wait.restype = ip
     lib.pk_wait.argtypes = [vp, ctypes.c_uint64, ctypes.c_double, ctypes.POINTER(pk_result)]
     lib.pk_readback.restype = ip
@@ -162,6 +165,12 @@ def pk_submit(eng: int, kind: int, n: int = 0) -> int:
     return t.value
 
 
+def pk_submit_until(eng: int, max_sweeps: int, check_every: int, tol: float) -> int:
+    t = ctypes.c_uint64()
+    _check(load().pk_submit_until(eng, max_sweeps, check_every, tol, ctypes.byref(t)), "pk_submit_until")
+    return t.value
+
+
 def pk_submit_status(eng: int, kind: int, n: int = 0):
     """Like pk_submit but returns (status, ticket) instead of raising."""
     t = ctypes.c_uint64()
@@ -228,6 +237,10 @@ class Engine:
 
     def sweep_rb(self, n: int) -> pk_result:
         return self.run(PK_SWEEP_RB, n)
+
+    def sweep_until(self, max_sweeps: int, check_every: int, tol: float,
+                    timeout_s: float = 60.0) -> pk_result:
+        return self.wait(pk_submit_until(self.h, max_sweeps, check_every, tol), timeout_s)
 
     def residual(self) -> float:
         return self.run(PK_RESIDUAL).residual

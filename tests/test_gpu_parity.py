@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from iterative_stencil_pde_amd import inputs, pk
-from parity import field_gate, residual_gate, run_engine_script, run_oracle_script, say
+from parity import run_engine_pipelined, run_oracle_pipelined, field_gate, residual_gate, run_engine_script, run_oracle_script, say
 
 pytestmark = pytest.mark.gpu
 
@@ -272,6 +272,74 @@ def test_resident_fp64_wide():
                             halo_depth=2)
     assert got["info"].band_rows == 2 and got["info"].halo_depth == 2
     check_against_oracle(w, got, ref, "resident/f64")
+
+
+# ---- early stop on a residual threshold, and pipelined (carried) tasks ---------
+def _tol_between(w, every, j):
+    """A tolerance between the oracle's residuals after j and j+1 checks, so the
+    stop point does not hang on summation-order differences (~1e-13)."""
+    rs = []
+    u = w.u0
+    for _ in range(j + 2):
+        rs.append(oracle.residual(u, f=w.f, h=w.h))
+        u, _ = oracle.jacobi(u, every, f=w.f, h=w.h)
+    return float(np.sqrt(rs[j] * rs[j + 1]))
+
+
+UNTIL_MODES = {
+    "auto": dict(mode=pk.PK_PERSISTENT),
+    "stream3": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=3),
+    "register": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_REGISTER, max_blocks=32),
+    "launch": dict(mode=pk.PK_LAUNCH),
+}
+
+
+@pytest.mark.parametrize("mode", sorted(UNTIL_MODES))
+def test_sweep_until_stops_where_the_oracle_does(mode):
+    w = inputs.poisson_uniform(256, 0, 100)
+    tol = _tol_between(w, 50, 3)  # R after 150 sweeps > tol >= R after 200
+    for max_sweeps, every, t, want in ((2000, 50, tol, 200), (230, 50, 0.0, 230), (500, 70, 1e30, 0)):
+        w2 = inputs.Workload(w.name, w.nx, w.ny, w.dtype, w.h, w.u0, w.f,
+                             [("until", max_sweeps, every, t), ("residual",)], "")
+        ref = run_oracle_pipelined(w2)
+        assert ref["until_done"] == [want]
+        got = run_engine_pipelined(w2, **UNTIL_MODES[mode])
+        r_until = got["results"][0][1]
+        say(f"  until max={max_sweeps} every={every} tol={t:.3e}: done {r_until.sweeps_done} (want {want})")
+        assert r_until.sweeps_done == want
+        check_against_oracle(w2, got, ref, f"until/{mode}/{max_sweeps}")
+
+
+@pytest.mark.parametrize("name,layout", [("laplace64", None), ("poisson256", None),
+                                         ("poisson256", pk.PK_LAYOUT_STREAM), ("laplace1024", None),
+                                         ("laplace4096", None)])
+def test_pipelined_tasks(name, layout):
+    """Tasks submitted ahead run on the carried path: every residual (including
+    back-to-back ones, which share the per-block partials) and the final field
+    must equal the oracle's."""
+    w = inputs.make(name)
+    small = name == "laplace4096"
+    script = [("residual",)]
+    for k in range(12):
+        n = (k * 7) % 23 + 1 if not small else (k % 3) + 1
+        script += [("sweep", n), ("residual",)]
+        if k % 4 == 1:
+            script += [("residual",), ("residual",), ("sweep_rb", (k % 5) + 1), ("residual",)]
+        if k % 5 == 2:
+            script += [("until", 40 if not small else 4, 9 if not small else 2, 0.0)]
+    script += [("residual",)] * 6
+    w.script = script
+    ref = run_oracle_pipelined(w)
+    opts = dict(mode=pk.PK_PERSISTENT)
+    if layout is not None:
+        opts["layout"] = layout
+    got = run_engine_pipelined(w, **opts)
+    dones = [r.sweeps_done for s0, r in got["results"] if s0[0] == "until"]
+    assert len(dones) == len(ref["until_done"])
+    check_against_oracle(w, got, ref, f"pipelined/{name}")
+    carried = got["info_end"].tasks_carried
+    say(f"  {carried} of {len(w.script)} tasks started on the carried path")
+    assert carried > len(w.script) // 2
 
 
 # ---- HIP-graph launch baseline -----------------------------------------------
