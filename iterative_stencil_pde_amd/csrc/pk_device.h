@@ -296,19 +296,22 @@ __device__ __forceinline__ void xcd_barrier(BarrierCtx& bc) {
 // Point-to-point halo sync between the blocks of neighbouring bands. Every
 // wave waits for its own stores (the edge rows just published), the block
 // meets, and thread 0 publishes the new exchange count on the block's flag
-// with agent-scope release, then acquires the flags of logical blocks lb-1 and
-// lb+1 (bounded spin). Blocks meet only their neighbours ("Persistent
+// with agent-scope release, then acquires the flags of logical blocks lb-d and
+// lb+d for d = 1..dist (bounded spins): all blocks whose bands its halo reaches. Blocks meet only their neighbours ("Persistent
 // Kernels", "Reflections and next steps", GPU-side scheduling).
-__device__ __forceinline__ void neighbor_sync(BarrierCtx& bc, uint32_t* nbr, int lb) {
+__device__ __forceinline__ void neighbor_sync(BarrierCtx& bc, uint32_t* nbr, int lb, int dist) {
     wait_vm();
     __syncthreads();
     const uint32_t target = bc.nbr_epoch + 1;
     if (threadIdx.x == 0 && !bc.faulted) {
         __hip_atomic_store(nbr + static_cast<size_t>(lb) * PK_NBR_WORDS, target, __ATOMIC_RELEASE,
                            __HIP_MEMORY_SCOPE_AGENT);
-        if (lb > 0) spin_until(bc, nbr + static_cast<size_t>(lb - 1) * PK_NBR_WORDS, target);
-        if (lb + 1 < static_cast<int>(bc.grid))
-            spin_until(bc, nbr + static_cast<size_t>(lb + 1) * PK_NBR_WORDS, target);
+        // every block whose band the halo reaches: dist bands on each side
+        for (int d = 1; d <= dist; ++d) {
+            if (lb - d >= 0) spin_until(bc, nbr + static_cast<size_t>(lb - d) * PK_NBR_WORDS, target);
+            if (lb + d < static_cast<int>(bc.grid))
+                spin_until(bc, nbr + static_cast<size_t>(lb + d) * PK_NBR_WORDS, target);
+        }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     bc.nbr_epoch = target;

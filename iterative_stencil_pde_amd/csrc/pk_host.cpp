@@ -29,6 +29,7 @@ struct Plan {
     int grid = 1;
     int strips = 1, bands = 1, band_rows = 1;
     int res_q = 0, res_rem = 0, res_halo = 0, res_ext_rows = 0, lds_pitch = 0;
+    int res_dist = 1;  // bands the tile's halo reaches on each side
     int reg_cw = 1, reg_rows = 0;
     size_t lds_bytes = 0;
     int xcd_remap = 0;
@@ -132,15 +133,20 @@ void release(pk_engine* e) {
 
 // ---------------------------------------------------------------------------
 // Planning of the tile layouts (RESIDENT in LDS, REGISTER in VGPRs): one band of
-// interior rows per block, bands of q or q+1 rows, halo depth m <= q (a block's
-// halo rows come from its neighbours' bands), tile height ext = band + 2m.
-// Estimated time per sweep = sub-sweep + exchange / m, with costs fitted to
-// measurements on MI355X (one block of 16 waves per CU):
-//   LDS sub-sweep: 0.37 us + 0.19 us per work item (a 64-lane row segment)
+// interior rows per block, bands of q or q+1 rows, halo depth m (the register
+// tile: m <= q), tile height ext = band + 2m.
+// Estimated time per sweep = sub-sweep + exchange / m, with costs fitted to 146
+// measured configurations on MI355X (one block of 16 waves per CU; 256^2 and
+// 1024^2, block counts that are multiples of 8, halos up to 20 rows; rms error
+// 0.06 us per sweep):
+//   LDS sub-sweep: 0.31 us + 0.30 us per work item (a 64-lane row segment)
 //     per wave, over the rows of an average sub-sweep (band + m - 1);
-//   exchange with the grid barrier:   2.5 us + 0.046 us per KB published + 0.0064 us per block;
-//   exchange with neighbour flags:    1.4 us + 0.069 us per KB published + 0.015 us per block
-//     (every block writes its XCD's L2 back on its own, so this grows faster with blocks).
+//   exchange with the grid barrier:   2.48 us + 0.0105 us per block;
+//   exchange with neighbour flags:    1.39 us + 0.0034 us per KB moved + 0.020 us per block
+//     + 0.29 us per further band the halo reaches (one more pair of flags to poll;
+//     every block also writes its XCD's L2 back on its own).
+// The halo may reach past the adjacent bands (m > q): every block then
+// publishes min(band, 2m) rows and reloads 2m.
 // The register tile keeps its own rough estimate (~25 ns per register row).
 // ---------------------------------------------------------------------------
 struct TilePlan {
@@ -156,12 +162,14 @@ double barrier_estimate_us(int g) {
     return 1.6 + 0.0078 * g;
 }
 
-double exchange_estimate_us(int exchange, int g, double kb) {
-    return exchange == PK_EXCHANGE_NEIGHBOR ? 1.4 + 0.069 * kb + 0.015 * g
-                                            : 2.5 + 0.046 * kb + 0.0064 * g;
+// dist: bands the halo reaches on each side (neighbour flags polled per side)
+double exchange_estimate_us(int exchange, int g, double kb, int dist) {
+    return exchange == PK_EXCHANGE_NEIGHBOR ? 1.39 + 0.0034 * kb + 0.020 * g + 0.286 * (dist - 1)
+                                            : 2.48 + 0.0105 * g;
 }
 
 constexpr int kRegRows = 8;  // rows per wave held in registers (PK_REG_RMAX)
+constexpr int kMaxHalo = 64;  // deepest LDS-tile halo the planner considers
 constexpr int kRegThreads = 512;  // block size of the register-tile kernel
 
 // One candidate block count g for the LDS (register == false) or register tile.
@@ -176,7 +184,9 @@ TilePlan tile_candidate(int nx, int ny, int esize, bool has_b, int nwv, size_t l
     const int band_max = q + (rem ? 1 : 0);
     const int nvec = (nx + W - 1) / W;
     const int lp = nvec * W;
-    int m_hi = g == 1 ? (1 << 20) : q;
+    // the register tile takes its halo from the adjacent bands only (m <= q);
+    // the LDS tile's halo may reach several bands (their blocks all sync)
+    int m_hi = g == 1 ? (1 << 20) : (register_tile ? q : kMaxHalo);
     if (want_m > 0) m_hi = std::min(m_hi, want_m);
     auto ext_of = [&](int m) { return g == 1 ? ny : std::min(ny, band_max + 2 * m); };
     t.g = g;
@@ -222,7 +232,7 @@ TilePlan tile_candidate(int nx, int ny, int esize, bool has_b, int nwv, size_t l
     const int segs = (nvec + sw - 1) / sw;
     auto sub_us = [&](double rows) {
         const double items = std::ceil(rows / rpi) * segs;
-        return 0.37 + 0.19 * items / nwv;
+        return 0.311 + 0.295 * items / nwv;
     };
     if (g == 1) {
         if (ny > max_rows) return TilePlan{};
@@ -232,12 +242,23 @@ TilePlan tile_candidate(int nx, int ny, int esize, bool has_b, int nwv, size_t l
         t.cost = sub_us(interior);
         return t;
     }
-    for (int m = 1; m <= std::min(m_hi, ny); ++m) {
+    // an explicit halo depth is taken as given (the deepest that fits, if less);
+    // otherwise every depth is costed
+    int m_lo = 1;
+    if (want_m > 0) {
+        int mf = std::min(m_hi, ny);
+        while (mf > 1 && ext_of(mf) > max_rows) --mf;
+        m_lo = mf;
+    }
+    for (int m = m_lo; m <= std::min(m_hi, ny); ++m) {
         if (ext_of(m) > max_rows) break;
-        const double kb = 2.0 * m * lp * esize / 1024.0;
+        // bytes per exchange: min(band, 2m) rows published, 2m rows reloaded (the
+        // fit used 2m + 2m, so count their mean twice)
+        const double kb = (std::min(q, 2 * m) + 2.0 * m) * lp * esize / 1024.0;
+        const int dist = (m + q - 1) / q;  // bands the halo reaches on each side
         for (int x = PK_EXCHANGE_BARRIER; x <= PK_EXCHANGE_NEIGHBOR; ++x) {
             if (!(exchanges & (1 << x))) continue;
-            const double c = sub_us(band_max + m - 1.0) + exchange_estimate_us(x, g, kb) / m;
+            const double c = sub_us(band_max + m - 1.0) + exchange_estimate_us(x, g, kb, dist) / m;
             if (c < t.cost) {
                 t.cost = c;
                 t.m = m;
@@ -258,11 +279,20 @@ TilePlan best_tile(int nx, int ny, int esize, bool has_b, int nwv, size_t lds_ma
     const int interior = ny - 2;
     const int lo = want_g > 0 ? want_g : 1;
     const int hi = want_g > 0 ? want_g : std::min(cus, interior);
+    TilePlan single;
     for (int g = lo; g <= hi; ++g) {
+        // from 8 blocks up, only multiples of 8: then consecutive bands sit on one
+        // XCD (measured ~0.1 us per sweep faster than neighbouring counts)
+        if (want_g <= 0 && g >= 8 && g % 8 != 0) continue;
         const TilePlan t = tile_candidate(nx, ny, esize, has_b, nwv, lds_max, g, want_m, register_tile,
                                           exchanges);
+        if (t.g == 1) single = t;
         if (t.g && t.cost < best.cost) best = t;
     }
+    // one block needs no synchronisation at all; the fit (made on multi-block
+    // tiles) overrates its sub-sweeps: 64^2 measured 0.52 us with one block
+    // against 0.58 with the seven the model preferred
+    if (want_g <= 0 && single.g == 1 && single.cost <= 1.2 * best.cost) best = single;
     return best;
 }
 
@@ -302,6 +332,7 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
             p.res_q = t.q;
             p.res_rem = t.rem;
             p.res_halo = t.m;
+            p.res_dist = (t.g == 1 || t.q < 1) ? 1 : (t.m + t.q - 1) / t.q;
             p.res_ext_rows = t.ext;
             p.reg_cw = t.cw;
             p.reg_rows = t.rows;
@@ -389,6 +420,7 @@ void fill_kargs(pk_engine* e) {
     a.reg_cw = p.reg_cw;
     a.reg_rows = p.reg_rows;
     a.res_halo = p.res_halo;
+    a.res_dist = p.res_dist;
     a.res_ext_rows = p.res_ext_rows;
     a.lds_pitch = p.lds_pitch;
     a.layout = p.layout;

@@ -246,8 +246,11 @@ __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierC
     while (remaining > 0) {
         const int sc = min(m, remaining);
         for (int s = 1; s <= sc; ++s) {
-            const int lo = (r0 == 1) ? 1 : r0 - (sc - s);
-            const int hi = (r1 == ny - 1) ? ny - 1 : r1 + (sc - s);
+            // rows of this sub-sweep: the owned band widened by the sub-sweeps
+            // still to come, within the interior (a halo deeper than the
+            // neighbouring band reaches back to the ring)
+            const int lo = max(1, r0 - (sc - s));
+            const int hi = min(ny - 1, r1 + (sc - s));
             // colour of this half-sweep: half-sweeps done so far in the task, mod 2
             const int parity = (n - remaining + s - 1) & 1;
             resident_rows<T, HAS_B, RB>(S, D, Bt, lo - e0, hi - e0, tm, e0, parity);
@@ -278,14 +281,14 @@ __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierC
             }
         }
         if (remaining > 0 && a.exchange == PK_EXCHANGE_NEIGHBOR)
-            neighbor_sync(bc, a.nbr, lb);
+            neighbor_sync(bc, a.nbr, lb, a.res_dist);
         else
             grid_barrier(bc, bc.broken);
         cur ^= 1;
         if (remaining > 0) {  // the neighbours' edge rows become this block's halo
             const T* g = static_cast<const T*>(a.u[cur]);
-            const int above = (r0 > 1) ? mn : 0;
-            const int below = (r1 < ny - 1) ? mn : 0;
+            const int above = min(mn, r0 - 1);       // interior rows only: row 0 is ring
+            const int below = min(mn, ny - 1 - r1);
             const int tot = (above + below) * nv;
             // several loads in flight per thread before the LDS stores: each
             // one is a trip to memory (the release/acquire pair of the

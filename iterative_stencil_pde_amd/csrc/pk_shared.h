@@ -130,6 +130,7 @@ struct pk_kargs {
     int res_q, res_rem;
     int reg_cw, reg_rows;  // register layout: column waves, rows per wave
     int res_halo;          // sweeps per halo exchange
+    int res_dist;          // bands a halo reaches on each side: ceil(halo / shortest band)
     int res_ext_rows;      // LDS rows per buffer
     int lds_pitch;         // LDS row stride in elements
     int layout;            // PK_LAYOUT_STREAM or PK_LAYOUT_RESIDENT

@@ -241,6 +241,25 @@ def test_resident_exchange_kinds(exchange, blocks, halo):
     check_against_oracle(w, got, ref, f"exchange{exchange}/{blocks}/{halo}")
 
 
+@pytest.mark.parametrize("exchange", [pk.PK_EXCHANGE_BARRIER, pk.PK_EXCHANGE_NEIGHBOR],
+                         ids=["barrier", "neighbor"])
+@pytest.mark.parametrize("blocks,halo", [(32, 12), (64, 10), (85, 16), (127, 9), (200, 5), (16, 18)])
+def test_resident_halo_deeper_than_band(exchange, blocks, halo):
+    """A halo deeper than a block's band reaches several neighbouring bands (and,
+    near the edges, the ring): same field and residuals as the oracle, for task
+    lengths that end part-way through a period, also in red-black."""
+    w = inputs.poisson_uniform(256, 0, 100)
+    w.script = [("residual",), ("sweep", 3), ("sweep", 29), ("residual",), ("sweep_rb", 7),
+                ("sweep", 41), ("residual",), ("readback",)]
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_RESIDENT,
+                            max_blocks=blocks, halo_depth=halo, exchange=exchange)
+    info = got["info"]
+    say(f"  grid={info.grid_blocks} band={info.band_rows} halo={info.halo_depth}")
+    assert info.halo_depth == halo and info.band_rows < halo
+    check_against_oracle(w, got, ref, f"deep-halo/{blocks}/{halo}/{exchange}")
+
+
 @pytest.mark.parametrize("shape,dtype,poisson,threads,blocks,halo", [
     ((20, 4100), np.float32, False, 1024, 9, 1),  # 1025 vectors a row: more segments than waves
     ((40, 1030), np.float32, True, 256, 12, 1),   # 258 vectors, 4 waves: segments taken in turn
