@@ -24,9 +24,13 @@ struct VecW {
     static constexpr int W = 16 / sizeof(T);
 };
 
+// The compiler's vector type of one 16-byte vector (elements indexed as v[k]).
+template <typename T>
+using NativeVec = T __attribute__((ext_vector_type(VecW<T>::W)));
+
 template <typename T>
 struct alignas(16) Vec {
-    T v[VecW<T>::W];
+    NativeVec<T> v;
 };
 
 template <typename T>
@@ -45,6 +49,26 @@ __device__ __forceinline__ Vec<T> vload(const T* p) {
 template <typename T>
 __device__ __forceinline__ void vstore(T* p, const Vec<T>& x) {
     *reinterpret_cast<Vec<T>*>(p) = x;
+}
+
+// The same for device (global) memory, through address-space-1 pointers: the
+// field pointers are chosen at run time (u[cur]), so the compiler cannot infer
+// their address space and would otherwise emit flat loads and stores.
+template <typename T>
+__device__ __forceinline__ Vec<T> gload(const T* p) {
+    Vec<T> r;
+    r.v = *((__attribute__((address_space(1))) const NativeVec<T>*)(p));
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void gstore(T* p, const Vec<T>& x) {
+    *((__attribute__((address_space(1))) NativeVec<T>*)(p)) = x.v;
+}
+
+template <typename T>
+__device__ __forceinline__ T gload1(const T* p) {
+    return *((__attribute__((address_space(1))) const T*)(p));
 }
 
 // ---------------------------------------------------------------------------
@@ -195,33 +219,45 @@ struct BarrierCtx {
     uint32_t xgroups;    // XCD barrier: XCDs with at least one block
     uint32_t nbr_epoch;  // neighbour exchanges completed (identical in every block)
     uint32_t nbar;       // grid barriers passed (identical in every block)
-    // task carry (leader thread only): the slot word of task carry_seq, read
-    // ahead once at task start; compared at the first ordered barrier at least
-    // carry_age ticks later (so the read has returned and stalls nothing: loads
-    // complete in order, and the barrier's own atomics would wait behind it)
-    uint64_t carry_seq;
+    // task carry: leader-only state in the block's shared memory (registers
+    // live across every pass cost the streaming kernels spills), except the
+    // read-ahead slot word, which must stay a register for its load to be in
+    // flight while the task runs
+    struct CarryState* carry;
     uint64_t carry_word;
-    uint64_t carry_t0;
-    uint64_t carry_age;
-    bool carry_pending;
+};
+
+// Task carry state of the leader (block 0, thread 0), in shared memory: the
+// task read ahead once at task start (seq), when (t0), and whether it still
+// waits to be compared (pending); `age` is how long a bus read takes.
+struct CarryState {
+    uint64_t seq;
+    uint64_t t0;
+    uint64_t age;
+    int pending;
 };
 
 // Leader only, before it arrives at an ordered grid barrier: if the task read
-// ahead has been published by the host, hand it on through the barrier. The
-// stores are ordered before the barrier's arrival, so every block sees them
-// after the barrier. One try per task: a task not yet published then goes the
-// ordinary way (poll, broadcast barrier).
+// ahead has been published by the host, hand it on through the barrier. It is
+// compared at the first ordered barrier at least `age` after the read was
+// issued (so the read has returned and stalls nothing: loads complete in order,
+// and the barrier's own atomics would wait behind it). The stores are ordered
+// before the barrier's arrival, so every block sees them after the barrier.
+// One try per task: a task not yet published goes the ordinary way (poll,
+// broadcast barrier).
 __device__ __forceinline__ void carry_at_barrier(BarrierCtx& bc) {
-    if (!bc.carry_pending || wall_clock64() - bc.carry_t0 < bc.carry_age) return;
-    bc.carry_pending = false;
+    CarryState* cs = bc.carry;
+    if (!cs->pending || wall_clock64() - cs->t0 < cs->age) return;
+    cs->pending = 0;
     const uint64_t w = bc.carry_word;
-    if (static_cast<uint32_t>(w >> 32) != static_cast<uint32_t>(bc.carry_seq)) return;
-    pk_carry* c = &bc.st->carry[bc.carry_seq & 1];
+    const uint64_t seq = cs->seq;
+    if (static_cast<uint32_t>(w >> 32) != static_cast<uint32_t>(seq)) return;
+    pk_carry* c = &bc.st->carry[seq & 1];
     __hip_atomic_store(&c->kind, static_cast<int32_t>((w >> 28) & 0xF), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(&c->n, static_cast<int32_t>(w & PK_TASK_N_MAX), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&c->seq, bc.carry_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&c->seq, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Lane 0 spins until *gen reaches `target` (relaxed loads, bounded in time).
@@ -430,9 +466,9 @@ __device__ __forceinline__ void stream_unit(const T* __restrict__ src, T* __rest
     const bool hact = (lane == 0) ? (c0 > 0) : ((lane == 63) && (c0 + 64 * W < nx));
     const size_t p = static_cast<size_t>(pitch);
 
-    Vec<T> up = act ? vload(src + static_cast<size_t>(r_begin - 1) * p + col) : vzero<T>();
-    Vec<T> mid = act ? vload(src + static_cast<size_t>(r_begin) * p + col) : vzero<T>();
-    T mh = hact ? src[static_cast<size_t>(r_begin) * p + hcol] : T(0);
+    Vec<T> up = act ? gload(src + static_cast<size_t>(r_begin - 1) * p + col) : vzero<T>();
+    Vec<T> mid = act ? gload(src + static_cast<size_t>(r_begin) * p + col) : vzero<T>();
+    T mh = hact ? gload1(src + static_cast<size_t>(r_begin) * p + hcol) : T(0);
 
     for (int r = r_begin; r < r_end; r += CH) {
         Vec<T> dn[CH];
@@ -441,11 +477,11 @@ __device__ __forceinline__ void stream_unit(const T* __restrict__ src, T* __rest
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
             const int rl = min(r + k + 1, r_end);  // r_end itself is a valid row
-            dn[k] = act ? vload(src + static_cast<size_t>(rl) * p + col) : vzero<T>();
-            dh[k] = hact ? src[static_cast<size_t>(rl) * p + hcol] : T(0);
+            dn[k] = act ? gload(src + static_cast<size_t>(rl) * p + col) : vzero<T>();
+            dh[k] = hact ? gload1(src + static_cast<size_t>(rl) * p + hcol) : T(0);
             if (HAS_B) {
                 const int rb = min(r + k, r_end - 1);
-                bb[k] = act ? vload(bsrc + static_cast<size_t>(rb) * p + col) : vzero<T>();
+                bb[k] = act ? gload(bsrc + static_cast<size_t>(rb) * p + col) : vzero<T>();
             } else {
                 bb[k] = vzero<T>();
             }
@@ -454,7 +490,7 @@ __device__ __forceinline__ void stream_unit(const T* __restrict__ src, T* __rest
         for (int k = 0; k < CH; ++k) {
             Vec<T> o = stencil<T, HAS_B>(up, mid, dn[k], bb[k], mh, col, nx);
             if (parity >= 0) o = rb_keep(o, mid, r + k, parity);  // wave-uniform
-            if (act && r + k < r_end) vstore(dst + static_cast<size_t>(r + k) * p + col, o);
+            if (act && r + k < r_end) gstore(dst + static_cast<size_t>(r + k) * p + col, o);
             up = mid;
             mid = dn[k];
             mh = dh[k];
@@ -475,9 +511,9 @@ __device__ __forceinline__ double stream_unit_residual(const T* __restrict__ src
     const bool hact = (lane == 0) ? (c0 > 0) : ((lane == 63) && (c0 + 64 * W < nx));
     const size_t p = static_cast<size_t>(pitch);
 
-    Vec<T> up = act ? vload(src + static_cast<size_t>(r_begin - 1) * p + col) : vzero<T>();
-    Vec<T> mid = act ? vload(src + static_cast<size_t>(r_begin) * p + col) : vzero<T>();
-    T mh = hact ? src[static_cast<size_t>(r_begin) * p + hcol] : T(0);
+    Vec<T> up = act ? gload(src + static_cast<size_t>(r_begin - 1) * p + col) : vzero<T>();
+    Vec<T> mid = act ? gload(src + static_cast<size_t>(r_begin) * p + col) : vzero<T>();
+    T mh = hact ? gload1(src + static_cast<size_t>(r_begin) * p + hcol) : T(0);
     double acc = 0.0;
     for (int r = r_begin; r < r_end; r += CH) {
         Vec<T> dn[CH];
@@ -486,11 +522,11 @@ __device__ __forceinline__ double stream_unit_residual(const T* __restrict__ src
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
             const int rl = min(r + k + 1, r_end);
-            dn[k] = act ? vload(src + static_cast<size_t>(rl) * p + col) : vzero<T>();
-            dh[k] = hact ? src[static_cast<size_t>(rl) * p + hcol] : T(0);
+            dn[k] = act ? gload(src + static_cast<size_t>(rl) * p + col) : vzero<T>();
+            dh[k] = hact ? gload1(src + static_cast<size_t>(rl) * p + hcol) : T(0);
             if (HAS_B) {
                 const int rb = min(r + k, r_end - 1);
-                bb[k] = act ? vload(bsrc + static_cast<size_t>(rb) * p + col) : vzero<T>();
+                bb[k] = act ? gload(bsrc + static_cast<size_t>(rb) * p + col) : vzero<T>();
             } else {
                 bb[k] = vzero<T>();
             }
@@ -579,12 +615,12 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
         for (int c = 0; c < CH; ++c) {
             const int t = t_first + dir * (q0 + c);
             const bool live = q0 + c < nsteps;
-            ld[c] = (act && live && t >= 0 && t < ny) ? vload(src + static_cast<size_t>(t) * p + col)
+            ld[c] = (act && live && t >= 0 && t < ny) ? gload(src + static_cast<size_t>(t) * p + col)
                                                       : vzero<T>();
             if (HAS_B) {
                 const int rb = t - dir;
                 lb[c] = (act && live && rb >= 1 && rb <= ny - 2)
-                            ? vload(bsrc + static_cast<size_t>(rb) * p + col) : vzero<T>();
+                            ? gload(bsrc + static_cast<size_t>(rb) * p + col) : vzero<T>();
             } else {
                 lb[c] = vzero<T>();
             }
@@ -612,7 +648,7 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
                     win[j][1] = win[j][2];
                     win[j][2] = o;
                 } else if (store_lane && row >= r0 && row < r1) {
-                    vstore(dst + static_cast<size_t>(row) * p + col, o);
+                    gstore(dst + static_cast<size_t>(row) * p + col, o);
                 }
             }
         }

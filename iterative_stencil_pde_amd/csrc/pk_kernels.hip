@@ -223,8 +223,8 @@ __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierC
                 if (idx < tot) {
                     const int rr = idx / nv, col = (idx % nv) * W;
                     const size_t go = static_cast<size_t>(e0 + rr) * p + col;
-                    x[u] = vload(g + go);
-                    if (HAS_B) xb[u] = vload(gb + go);
+                    x[u] = gload(g + go);
+                    if (HAS_B) xb[u] = gload(gb + go);
                     dst[u] = rr * lp + col;
                 }
             }
@@ -277,7 +277,7 @@ __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierC
             for (int idx = tid; idx < tot; idx += nt) {
                 const int k = idx / nv, col = (idx % nv) * W;
                 const int rr = (k < ntop) ? r0 + k : bot_begin + (k - ntop);
-                vstore(g + static_cast<size_t>(rr) * p + col, vload(S + (rr - e0) * lp + col));
+                gstore(g + static_cast<size_t>(rr) * p + col, vload(S + (rr - e0) * lp + col));
             }
         }
         if (remaining > 0 && a.exchange == PK_EXCHANGE_NEIGHBOR)
@@ -304,7 +304,7 @@ __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierC
                     if (idx < tot) {
                         const int k = idx / nv, col = (idx % nv) * W;
                         const int rr = (k < above) ? r0 - above + k : r1 + (k - above);
-                        x[u] = vload(g + static_cast<size_t>(rr) * p + col);
+                        x[u] = gload(g + static_cast<size_t>(rr) * p + col);
                         dst[u] = (rr - e0) * lp + col;
                     }
                 }
@@ -386,16 +386,23 @@ __device__ int64_t stamp_task(const pk_kargs& a, int n, uint32_t& round, Barrier
 // Blocks of up to 1024 threads (128 VGPRs per lane); the register-tile layout
 // uses 512 so that each lane can hold 16 rows of u and b (256 VGPRs per lane).
 // n Jacobi sweeps of the field in u[cur] in the engine's layout (cur flips).
+// n sub-sweeps in the engine's layout: Jacobi sweeps, or (rb) red-black
+// half-sweeps, red first (not in the register layout).
 template <typename T, bool HAS_B, int LAYOUT>
-__device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
+__device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, int& cur, BarrierCtx& bc,
+                                            T* lds) {
     if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
-        resident_sweep_task<T, HAS_B, false>(a, n, cur, bc, lds);
+        if (rb)
+            resident_sweep_task<T, HAS_B, true>(a, n, cur, bc, lds);
+        else
+            resident_sweep_task<T, HAS_B, false>(a, n, cur, bc, lds);
     } else if constexpr (LAYOUT == PK_LAYOUT_REGISTER) {
         reg_sweep_task<T, HAS_B>(a, n, cur, bc, lds);
     } else {
         for (int s = 0; s < n;) {
             const int k = min(a.pass_sweeps, n - s);
-            stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), static_cast<T*>(a.u[cur ^ 1]), k);
+            stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), static_cast<T*>(a.u[cur ^ 1]), k,
+                                  rb ? (s & 1) : -1);
             grid_barrier(bc, bc.broken);
             cur ^= 1;
             s += k;
@@ -456,11 +463,16 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
     bc.xgroups = 1;
     bc.nbr_epoch = 0;
     bc.nbar = 0;
-    bc.carry_seq = 0;
+    __shared__ CarryState s_carry;
+    if (threadIdx.x == 0) {
+        s_carry.seq = 0;
+        s_carry.t0 = 0;
+        s_carry.age = a.carry_age_ticks;
+        s_carry.pending = 0;
+    }
+    __syncthreads();
+    bc.carry = &s_carry;
     bc.carry_word = 0;
-    bc.carry_t0 = 0;
-    bc.carry_age = a.carry_age_ticks;
-    bc.carry_pending = false;
     if (a.barrier_kind == PK_BARRIER_XCD && a.grid > 1 && !bc.broken) {
         // count the blocks on each XCD (one flat barrier, generation 1), then
         // switch to the XCD barrier, whose counters start from zero
@@ -560,11 +572,11 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
         const bool work = ((kind == PK_SWEEP || kind == PK_SWEEP_RB) && n > 0) || kind == PK_RESIDUAL ||
                           kind == PK_SWEEP_UNTIL || kind == PK_TASK_READBACK;
         if (leader && !bc.broken && work) {
-            bc.carry_seq = seq + 1;
-            bc.carry_t0 = wall_clock64();
+            s_carry.seq = seq + 1;
+            s_carry.t0 = wall_clock64();
+            s_carry.pending = 1;
             bc.carry_word = __hip_atomic_load(&mail->slot[(seq + 1) % PK_RING].word, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_SYSTEM);
-            bc.carry_pending = true;
         }
 
         if (s_exit) {
@@ -594,59 +606,49 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
         double res = 0.0;
         int64_t errs = 0;
         int status = PK_OK;
-        if (kind == PK_SWEEP_RB) {
-            // n red-black iterations = 2n half-sweeps, each computed into the other
-            // buffer with the other colour copied (the in-place result: a node
-            // never reads its own colour)
-            if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
-                resident_sweep_task<T, HAS_B, true>(a, 2 * n, cur, bc, reinterpret_cast<T*>(pk_lds));
-            } else if constexpr (LAYOUT == PK_LAYOUT_REGISTER) {
+        if (kind == PK_SWEEP || kind == PK_SWEEP_RB || kind == PK_RESIDUAL || kind == PK_SWEEP_UNTIL) {
+            // The sweeping tasks share one loop (one copy of the sweep and
+            // residual code in the kernel): an optional residual check, then up
+            // to `every` sweeps, until the budget is spent or R <= tol.
+            const bool rb = kind == PK_SWEEP_RB;
+            const bool until = kind == PK_SWEEP_UNTIL;
+            const bool check = until || kind == PK_RESIDUAL;
+            const int budget = kind == PK_RESIDUAL ? 0 : n;
+            double tol = -1.0;  // R >= 0: never stops a plain residual
+            int every = budget;
+            if (until) {
+                // parameters: each block acquires the slot word the host released
+                // after writing them, then reads them
+                if (threadIdx.x == 0) {
+                    (void)__hip_atomic_load(&mail->slot[seq % PK_RING].word, __ATOMIC_ACQUIRE,
+                                            __HIP_MEMORY_SCOPE_SYSTEM);
+                    const pk_param* prm = &mail->param[seq % PK_RING];
+                    s_tol = __hip_atomic_load(&prm->tol, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    s_every = __hip_atomic_load(&prm->every, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                }
+                __syncthreads();
+                tol = s_tol;
+                every = s_every;
+            }
+            if (rb && LAYOUT == PK_LAYOUT_REGISTER) {
                 status = PK_EINVAL;
             } else {
-                for (int s = 0; s < 2 * n;) {
-                    const int k = min(a.pass_sweeps, 2 * n - s);
-                    stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), static_cast<T*>(a.u[cur ^ 1]), k,
-                                          s & 1);
-                    grid_barrier(bc, bc.broken);
-                    cur ^= 1;
-                    s += k;
+                int done = 0;
+                for (;;) {  // the same decisions in every block
+                    if (check) {
+                        res = residual_round<T, HAS_B>(a, cur, bc, res_round, s_red, until);
+                        if (res <= tol) break;
+                    }
+                    if (done >= budget) break;
+                    const int k = min(every, budget - done);
+                    // red-black: k iterations = 2k half-sweeps, each computed into
+                    // the other buffer with the other colour copied (the in-place
+                    // result: a node never reads its own colour)
+                    sweeps_task<T, HAS_B, LAYOUT>(a, rb ? 2 * k : k, rb, cur, bc, reinterpret_cast<T*>(pk_lds));
+                    done += k;
                 }
+                sweeps += done;
             }
-            if (status == PK_OK) sweeps += n;
-        } else if (kind == PK_SWEEP) {
-            if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
-                resident_sweep_task<T, HAS_B, false>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
-            } else if constexpr (LAYOUT == PK_LAYOUT_REGISTER) {
-                reg_sweep_task<T, HAS_B>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
-            } else {
-                sweeps_task<T, HAS_B, LAYOUT>(a, n, cur, bc, reinterpret_cast<T*>(pk_lds));
-            }
-            sweeps += n;
-        } else if (kind == PK_RESIDUAL) {
-            res = residual_round<T, HAS_B>(a, cur, bc, res_round, s_red, false);
-        } else if (kind == PK_SWEEP_UNTIL) {
-            // parameters: each block acquires the slot word the host released
-            // after writing them, then reads them
-            if (threadIdx.x == 0) {
-                (void)__hip_atomic_load(&mail->slot[seq % PK_RING].word, __ATOMIC_ACQUIRE,
-                                        __HIP_MEMORY_SCOPE_SYSTEM);
-                const pk_param* prm = &mail->param[seq % PK_RING];
-                s_tol = __hip_atomic_load(&prm->tol, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                s_every = __hip_atomic_load(&prm->every, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            }
-            __syncthreads();
-            const double tol = s_tol;
-            const int every = s_every;
-            double r = residual_round<T, HAS_B>(a, cur, bc, res_round, s_red, true);
-            int done = 0;
-            while (!(r <= tol) && done < n) {  // the same decision in every block
-                const int k = min(every, n - done);
-                sweeps_task<T, HAS_B, LAYOUT>(a, k, cur, bc, reinterpret_cast<T*>(pk_lds));
-                done += k;
-                r = residual_round<T, HAS_B>(a, cur, bc, res_round, s_red, true);
-            }
-            sweeps += done;
-            res = r;
         } else if (kind == PK_TASK_READBACK) {
             readback_task<T>(a, cur);
             grid_barrier(bc);
@@ -663,7 +665,7 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
         // path, the broadcast barrier of this task, i.e. after every block read
         // carry[(seq - 1) & 1], the same word. A task without a barrier carries
         // nothing, so the next one starts the ordinary way.
-        if (leader) bc.carry_pending = false;  // never publish it outside its task
+        if (leader) s_carry.pending = 0;  // never publish it outside its task
         may_carry = !bc.broken && bc.nbar != nbar0;
         if (leader) {
             pk_done_rec* d = &mail->done[seq % PK_RING];
