@@ -63,18 +63,22 @@ extern "C" {
 #define PK_PERSISTENT 0 /* one co-resident launch driven through the task ring */
 #define PK_LAUNCH 1     /* one kernel launch per sweep (baseline)               */
 
-/* Work layout of the persistent SWEEP task.
+/* Work layout of the persistent sweeping tasks.
  * STREAM: every sweep streams the field through HBM (grid-stride over bands
  *   of rows x 64-lane column strips, 128-bit row loads, 3-row register window).
  * RESIDENT: each block keeps its band of rows (plus halo rows) in LDS for the
  *   whole task; only the halo rows go through HBM, once every halo_depth sweeps
  *   (the wider-halo scheme of "Persistent Kernels", "Reflections and next
  *   steps", "Fewer handshakes", with exact Jacobi semantics).
- * REGISTER: as RESIDENT, but each block's rows live in VGPRs (one 16-byte
- *   vector per lane per row); only wave-boundary rows and columns go through
- *   LDS. Experimental: taken only when asked for; no PK_SWEEP_RB.
- * AUTO: RESIDENT when the bands fit in LDS (block count and halo depth from a
- *   cost model), else STREAM.                                               */
+ * REGISTER: as RESIDENT (same bands, halos and exchanges, same results), but
+ *   each block's rows live in VGPRs: a wave holds up to 4 consecutive rows of
+ *   one 64-lane column strip (one 16-byte vector per lane per row); only
+ *   wave-boundary rows and columns go through LDS. Needs rows of at most
+ *   (threads / 64) x 64 vectors and band + 2 x halo_depth <= 4 x the waves of
+ *   a column strip.
+ * AUTO: the tile (RESIDENT or REGISTER) with the lower modelled time per sweep
+ *   when one fits (block count and halo depth from the cost model), else
+ *   STREAM.                                                                 */
 #define PK_LAYOUT_AUTO 0
 #define PK_LAYOUT_STREAM 1
 #define PK_LAYOUT_RESIDENT 2
@@ -97,7 +101,7 @@ extern "C" {
                       /*   formula as a Jacobi sweep from its neighbours' current   */
                       /*   values. Equal to the in-place iteration; computed as two */
                       /*   half-sweeps into the other buffer, so `cur` flips as for */
-                      /*   SWEEP. n <= PK_TASK_N_MAX / 2; not in the REGISTER layout.*/
+                      /*   SWEEP. n <= PK_TASK_N_MAX / 2.                          */
                       /*   sweeps_done counts iterations.                           */
 #define PK_SWEEP_UNTIL 7 /* Jacobi sweeps until the residual reaches a tolerance:   */
                       /*   submitted with pk_submit_until (see there), not pk_submit */
@@ -127,7 +131,7 @@ extern "C" {
 #define PK_BARRIER_TWO_LEVEL 2
 #define PK_BARRIER_XCD 3
 
-/* Halo exchange of the RESIDENT layout between the sweeps of one task
+/* Halo exchange of the tile layouts (RESIDENT, REGISTER) between the sweeps of one task
  * (after every halo_depth sweeps, each block publishes its edge rows to device
  * memory and reloads its neighbours').
  * BARRIER: a grid barrier between publish and reload.
@@ -154,8 +158,8 @@ typedef struct pk_opts {
     int threads;           /* threads per block, multiple of 64, <= 1024; 0 = auto   */
     int max_blocks;        /* grid size in blocks; 0 = automatic. STREAM uses it as */
                            /* given (PK_ELAUNCH if that grid cannot be co-resident),*/
-                           /* RESIDENT as an upper bound (one band per block)       */
-    int halo_depth;        /* RESIDENT: sweeps per halo exchange; 0 = automatic     */
+                           /* the tiles as an upper bound (one band per block)    */
+    int halo_depth;        /* RESIDENT, REGISTER: sweeps per halo exchange; 0 = auto*/
     unsigned flags;        /* PK_DBG_* flags                                         */
     void* stream;          /* hipStream_t to use; NULL => the engine makes its own  */
                            /* non-blocking stream (the persistent kernel must not   */
@@ -169,7 +173,7 @@ typedef struct pk_opts {
                            /* at most 3 with a source term (pk_info reports it)     */
     int band_rows;         /* STREAM passes: rows per band (a unit is a band x one  */
                            /* strip, one per wave); 0 = automatic                   */
-    int exchange;          /* RESIDENT: PK_EXCHANGE_*                                */
+    int exchange;          /* RESIDENT, REGISTER: PK_EXCHANGE_*                      */
     int reserved[4];       /* must be zero                                           */
 } pk_opts;
 
@@ -196,12 +200,12 @@ typedef struct pk_info {
     int threads;            /* threads per block                                         */
     int blocks_per_cu_max;  /* occupancy query result for the persistent kernel          */
     int cus;                /* compute units on the device                               */
-    int halo_depth;         /* RESIDENT: sweeps per exchange; 0 otherwise                */
-    int band_rows;          /* rows per band (RESIDENT: per block; STREAM: per unit)     */
+    int halo_depth;         /* RESIDENT, REGISTER: sweeps per exchange; 0 otherwise      */
+    int band_rows;          /* rows per band (tiles: per block; STREAM: per unit)        */
     int strips;             /* STREAM: column strips                                     */
     int barrier;            /* PK_BARRIER_FLAT, _TWO_LEVEL or _XCD                       */
     int pass_sweeps;        /* STREAM: sweeps per pass                                   */
-    int exchange;           /* RESIDENT: PK_EXCHANGE_BARRIER or _NEIGHBOR; 0 otherwise   */
+    int exchange;           /* tiles: PK_EXCHANGE_BARRIER or _NEIGHBOR; 0 otherwise      */
     size_t lds_bytes;       /* dynamic LDS per block                                     */
     double kernel_ms;       /* PERSISTENT: launch-to-exit time of the kernel (HIP        */
                             /* events on its stream), valid after EXIT; LAUNCH: total   */

@@ -105,6 +105,27 @@ __device__ __forceinline__ double from_upper(double edge, double v) {
                                 static_cast<long long>(static_cast<unsigned>(lo)));
 }
 
+// Per-lane bit blend: `keep_val` where the mask word is all ones, else
+// `new_val`, as one v_bfi_b32 per 32 bits (written out: the optimiser would
+// otherwise turn the choice into a select, and that into a branch around the
+// arithmetic, or split it into two logic operations).
+__device__ __forceinline__ uint32_t lane_mask(bool b) { return b ? 0xffffffffu : 0u; }
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float blend(uint32_t mask, float keep_val, float new_val) {
+    return __uint_as_float(bfi(mask, __float_as_uint(keep_val), __float_as_uint(new_val)));
+}
+__device__ __forceinline__ double blend(uint32_t mask, double keep_val, double new_val) {
+    const unsigned long long k = static_cast<unsigned long long>(__double_as_longlong(keep_val));
+    const unsigned long long x = static_cast<unsigned long long>(__double_as_longlong(new_val));
+    const uint32_t lo = bfi(mask, static_cast<uint32_t>(k), static_cast<uint32_t>(x));
+    const uint32_t hi = bfi(mask, static_cast<uint32_t>(k >> 32), static_cast<uint32_t>(x >> 32));
+    return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
 // ---------------------------------------------------------------------------
 // The stencil on one lane's vector. `col` is the first column of the vector;
 // columns 0 and nx-1 (the Dirichlet ring) and padding columns >= nx keep

@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstdint>
 #include <cstring>
+#include <functional>
 #include <new>
 #include <vector>
 
@@ -156,21 +157,14 @@ struct TilePlan {
     double cost = 1e30;
 };
 
-double barrier_estimate_us(int g) {
-    if (g <= 1) return 0.2;
-    if (g < 16) return 1.4;
-    return 1.6 + 0.0078 * g;
-}
-
 // dist: bands the halo reaches on each side (neighbour flags polled per side)
 double exchange_estimate_us(int exchange, int g, double kb, int dist) {
     return exchange == PK_EXCHANGE_NEIGHBOR ? 1.39 + 0.0034 * kb + 0.020 * g + 0.286 * (dist - 1)
                                             : 2.48 + 0.0105 * g;
 }
 
-constexpr int kRegRows = 8;  // rows per wave held in registers (PK_REG_RMAX)
+constexpr int kRegRows = 4;  // rows per wave held in registers (PK_REG_RMAX)
 constexpr int kMaxHalo = 64;  // deepest LDS-tile halo the planner considers
-constexpr int kRegThreads = 512;  // block size of the register-tile kernel
 
 // One candidate block count g for the LDS (register == false) or register tile.
 // `exchanges` lists the exchange kinds to consider (LDS tile only).
@@ -184,62 +178,51 @@ TilePlan tile_candidate(int nx, int ny, int esize, bool has_b, int nwv, size_t l
     const int band_max = q + (rem ? 1 : 0);
     const int nvec = (nx + W - 1) / W;
     const int lp = nvec * W;
-    // the register tile takes its halo from the adjacent bands only (m <= q);
-    // the LDS tile's halo may reach several bands (their blocks all sync)
-    int m_hi = g == 1 ? (1 << 20) : (register_tile ? q : kMaxHalo);
+    int m_hi = g == 1 ? (1 << 20) : kMaxHalo;
     if (want_m > 0) m_hi = std::min(m_hi, want_m);
     auto ext_of = [&](int m) { return g == 1 ? ny : std::min(ny, band_max + 2 * m); };
     t.g = g;
     t.q = q;
     t.rem = rem;
+    // tile rows a block can hold, time per sub-sweep of `rows` rows on average
+    int max_rows = 0;
+    std::function<double(double, int)> sub_us;
+    std::function<int(int)> reg_rows;
     if (register_tile) {
-        int m = 0, rows = 0;
+        // cw column groups of 64 lanes x rw row groups of waves, kRegRows rows each
         const int cw = (nvec + 63) / 64;
         if (cw > nwv) return TilePlan{};
         const int rw = nwv / cw;
-        // deepest halo whose tile fits in kRegRows rows per wave; the kernel holds
-        // a power of two of rows per wave (2, 4 or 8)
-        for (int mm = std::min(m_hi, ny); mm >= 1; --mm) {
-            const int r = (ext_of(mm) + rw - 1) / rw;
-            if (r <= kRegRows) {
-                m = mm;
-                rows = 2;
-                while (rows < r) rows *= 2;
-                break;
-            }
-        }
-        if (m == 0) return TilePlan{};
-        if (g == 1) m = 1 << 20;
-        size_t lds = static_cast<size_t>(2) * nwv * (2 * 64 * W + 2 * kRegRows) * esize;
-        if (has_b) lds += static_cast<size_t>(ext_of(m == (1 << 20) ? ny : m)) * lp * esize;
-        if (lds > lds_max) return TilePlan{};
-        t.m = m;
-        t.ext = ext_of(m);
-        t.rows = rows;
+        max_rows = rw * kRegRows;
         t.cw = cw;
-        t.lds = lds;
-        const double exchange = barrier_estimate_us(g) + (g > 1 ? 1.0 : 0.0);
-        t.cost = (g == 1 ? 0.0 : exchange / m) + 0.10 + 0.025 * rows;
-        return t;
+        t.lds = static_cast<size_t>(2) * nwv * (2 * 64 * W + 2 * kRegRows) * esize;
+        if (t.lds > lds_max) return TilePlan{};
+        reg_rows = [rw](int ext) { return (ext + rw - 1) / rw <= 2 ? 2 : kRegRows; };
+        // the waves go round the CU's 4 SIMDs, so the active row segments of a
+        // sub-sweep spread over them; column groups add an edge exchange
+        sub_us = [cw](double rows, int) { return 0.14 + (cw > 1 ? 0.06 : 0.0) + 0.075 * rows * cw / 4.0; };
+    } else {
+        const size_t row_bytes = static_cast<size_t>(lp) * esize * (has_b ? 3 : 2);
+        max_rows = static_cast<int>(lds_max / row_bytes);
+        // work items per row: rows narrower than 64 vectors share a wave
+        int sw = 1;
+        while (sw < nvec && sw < 64) sw *= 2;
+        const int rpi = 64 / sw;
+        const int segs = (nvec + sw - 1) / sw;
+        sub_us = [rpi, segs, nwv](double rows, int) {
+            const double items = std::ceil(rows / rpi) * segs;
+            return 0.311 + 0.295 * items / nwv;
+        };
+        t.lds = row_bytes;  // per tile row, scaled below
     }
-    const size_t row_bytes = static_cast<size_t>(lp) * esize * (has_b ? 3 : 2);
-    const int max_rows = static_cast<int>(lds_max / row_bytes);
     if (ext_of(1) > max_rows && !(g == 1 && ny <= max_rows)) return TilePlan{};
-    // work items per row: rows narrower than 64 vectors share a wave
-    int sw = 1;
-    while (sw < nvec && sw < 64) sw *= 2;
-    const int rpi = 64 / sw;
-    const int segs = (nvec + sw - 1) / sw;
-    auto sub_us = [&](double rows) {
-        const double items = std::ceil(rows / rpi) * segs;
-        return 0.311 + 0.295 * items / nwv;
-    };
     if (g == 1) {
         if (ny > max_rows) return TilePlan{};
         t.m = 1 << 20;
         t.ext = ny;
-        t.lds = static_cast<size_t>(ny) * row_bytes;
-        t.cost = sub_us(interior);
+        t.rows = register_tile ? reg_rows(ny) : 0;
+        if (!register_tile) t.lds *= static_cast<size_t>(ny);
+        t.cost = sub_us(interior, t.rows);
         return t;
     }
     // an explicit halo depth is taken as given (the deepest that fits, if less);
@@ -256,19 +239,21 @@ TilePlan tile_candidate(int nx, int ny, int esize, bool has_b, int nwv, size_t l
         // fit used 2m + 2m, so count their mean twice)
         const double kb = (std::min(q, 2 * m) + 2.0 * m) * lp * esize / 1024.0;
         const int dist = (m + q - 1) / q;  // bands the halo reaches on each side
+        const int r = register_tile ? reg_rows(ext_of(m)) : 0;
         for (int x = PK_EXCHANGE_BARRIER; x <= PK_EXCHANGE_NEIGHBOR; ++x) {
             if (!(exchanges & (1 << x))) continue;
-            const double c = sub_us(band_max + m - 1.0) + exchange_estimate_us(x, g, kb, dist) / m;
+            const double c = sub_us(band_max + m - 1.0, r) + exchange_estimate_us(x, g, kb, dist) / m;
             if (c < t.cost) {
                 t.cost = c;
                 t.m = m;
                 t.exchange = x;
+                t.rows = r;
             }
         }
     }
     if (t.m == 0) return TilePlan{};
     t.ext = ext_of(t.m);
-    t.lds = static_cast<size_t>(t.ext) * row_bytes;
+    if (!register_tile) t.lds *= static_cast<size_t>(t.ext);
     return t;
 }
 
@@ -314,12 +299,9 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         const int exchanges = o.exchange != PK_EXCHANGE_AUTO ? (1 << o.exchange)
                               : (o.flags & PK_DBG_BROKEN_BARRIER) ? (1 << PK_EXCHANGE_BARRIER)
                               : ((1 << PK_EXCHANGE_BARRIER) | (1 << PK_EXCHANGE_NEIGHBOR));
-        const int reg_threads = std::min(p.threads, kRegThreads);
-        // the register tile is taken only on request: on MI355X it has not beaten
-        // the LDS tile at any measured size
-        if (o.layout == PK_LAYOUT_REGISTER)
-            reg = best_tile(e->nx, e->ny, e->esize, e->has_b, reg_threads / 64, lds_max, e->cus,
-                            o.max_blocks, o.halo_depth, true, 0);
+        if (o.layout == PK_LAYOUT_AUTO || o.layout == PK_LAYOUT_REGISTER)
+            reg = best_tile(e->nx, e->ny, e->esize, e->has_b, nwv, lds_max, e->cus, o.max_blocks,
+                            o.halo_depth, true, exchanges);
         if (o.layout == PK_LAYOUT_AUTO || o.layout == PK_LAYOUT_RESIDENT)
             lds = best_tile(e->nx, e->ny, e->esize, e->has_b, nwv, lds_max, e->cus, o.max_blocks,
                             o.halo_depth, false, exchanges);
@@ -327,7 +309,6 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         const TilePlan& t = use_reg ? reg : lds;
         if (t.g) {
             p.layout = use_reg ? PK_LAYOUT_REGISTER : PK_LAYOUT_RESIDENT;
-            if (use_reg) p.threads = reg_threads;
             p.grid = t.g;
             p.res_q = t.q;
             p.res_rem = t.rem;
@@ -338,7 +319,7 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
             p.reg_rows = t.rows;
             p.lds_pitch = static_cast<int>(round_up(static_cast<size_t>(e->nx), W));
             p.lds_bytes = t.lds;
-            p.exchange = use_reg ? 0 : t.exchange;
+            p.exchange = t.exchange;
             tiled = true;
         } else if (o.layout == PK_LAYOUT_RESIDENT || o.layout == PK_LAYOUT_REGISTER) {
             return PK_EINVAL;  // asked for, but the bands do not fit
@@ -627,8 +608,8 @@ int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket) {
     const bool known = t.kind == PK_SWEEP || t.kind == PK_SWEEP_RB || t.kind == PK_RESIDUAL ||
                        t.kind == PK_EXIT || t.kind == PK_BARRIER || t.kind == PK_STAMP;
     if (!known || t.n < 0 || t.n > PK_TASK_N_MAX) return PK_EINVAL;
-    // red-black runs 2n half-sweeps; the register tile has no red-black form
-    if (t.kind == PK_SWEEP_RB && (t.n > PK_TASK_N_MAX / 2 || e->plan.layout == PK_LAYOUT_REGISTER))
+    // red-black runs 2n half-sweeps
+    if (t.kind == PK_SWEEP_RB && t.n > PK_TASK_N_MAX / 2)
         return PK_EINVAL;
     if (e->mode == PK_LAUNCH) {
         if (t.kind == PK_BARRIER || t.kind == PK_STAMP) return PK_EINVAL;

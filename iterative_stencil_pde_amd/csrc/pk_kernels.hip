@@ -20,24 +20,23 @@ __device__ __forceinline__ int band_begin(const pk_kargs& a, int L) {
 }
 
 // ---------------------------------------------------------------------------
-// Register-tile SWEEP task (PK_LAYOUT_REGISTER). Same band / halo / publish /
-// barrier protocol as the LDS-resident task below, but each block keeps its
-// rows [r0 - m, r1 + m) in VGPRs: the waves form cw column groups (64 lanes x
-// W columns each) times rw row groups, and a lane holds one 16-byte vector for
-// each of its R rows. A sub-sweep updates those rows in place in registers;
-// W/E come from DPP lane shifts, and only what crosses a wave boundary goes
-// through LDS: each wave's first and last row, and its first and last column.
-// Every row of the tile is recomputed each sub-sweep; values that depend on
-// the zero fill beyond the tile spread one row per sub-sweep and never reach
-// the owned rows within a period of m <= (halo) sub-sweeps. Ring rows and
-// columns keep their values.
+// Register-tile SWEEP task (PK_LAYOUT_REGISTER). Same bands, halos, sub-sweep
+// row ranges, publish / exchange / reload protocol as the LDS-resident task
+// below (so the same results, bit for bit), but the tile rows live in VGPRs:
+// the waves form cw column groups (64 lanes x W columns each) times rw row
+// groups, and a lane holds one 16-byte vector of each of its RT consecutive
+// rows (and of b). A sub-sweep updates the active rows in place, marching
+// down the wave's rows with the old value of the row above in a register, so
+// the stencil reads nothing from memory; W/E come from DPP lane shifts. Only
+// what crosses a wave boundary goes through LDS: each wave's first and last
+// row, and its first and last column. The instruction count per row is about
+// half that of the LDS tile, whose sub-sweeps are bound by vector issue.
 // ---------------------------------------------------------------------------
-constexpr int PK_REG_RMAX = 8;  // rows per wave; the layout runs 512-thread blocks
+constexpr int PK_REG_RMAX = 4;  // rows per wave
 
 // Exchange slot of one wave for one sub-sweep parity: its first row, its last
 // row, its first column (element 0 of lane 0, one per row) and its last column
-// (element W-1 of lane 63). Columns are stored contiguously so a consumer lane
-// reads them with 16-byte LDS loads.
+// (element W-1 of lane 63).
 template <typename T>
 struct RegSlot {
     static constexpr int W = VecW<T>::W;
@@ -46,10 +45,11 @@ struct RegSlot {
                          last_col = 2 * 64 * W + PK_REG_RMAX;
 };
 
-template <typename T, bool HAS_B, int RT>
-__device__ void reg_sweep_rows(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
+template <typename T, bool HAS_B, bool RB, int RT>
+__device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
     constexpr int W = VecW<T>::W;
     using S = RegSlot<T>;
+    static_assert(RT <= PK_REG_RMAX, "rows per wave");
     const int lb = logical_block(a.xcd_remap, a.grid);
     const int ny = a.ny, nx = a.nx;
     const int r0 = band_begin(a, lb), r1 = band_begin(a, lb + 1);
@@ -65,49 +65,49 @@ __device__ void reg_sweep_rows(const pk_kargs& a, int n, int& cur, BarrierCtx& b
     const bool lane_live = wave_live && col < nx;
     const int row_base = e0 + rg * RT;
     const size_t p = static_cast<size_t>(a.pitch);
-    const int lp = a.lds_pitch;
-    T* lds_b = lds + static_cast<size_t>(2 * nwv) * S::size;
     const bool has_left = cg > 0, has_right = cg + 1 < cw;  // wave-uniform
+    uint32_t keep[W];  // ring and padding columns keep their value
+#pragma unroll
+    for (int k = 0; k < W; ++k) keep[k] = lane_mask((col + k == 0) || (col + k >= nx - 1));
 
-    Vec<T> u[RT];
+    Vec<T> u[RT], bb[RT];
     {
         const T* g = static_cast<const T*>(a.u[cur]);
+        const T* gb = static_cast<const T*>(a.b);
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             const int row = row_base + r;
-            u[r] = (lane_live && row < e1) ? vload(g + static_cast<size_t>(row) * p + col) : vzero<T>();
-        }
-        if (HAS_B) {
-            const T* gb = static_cast<const T*>(a.b);
-            const int nv = lp / W;
-            const int tot = (e1 - e0) * nv;
-            for (int idx = static_cast<int>(threadIdx.x); idx < tot; idx += static_cast<int>(blockDim.x)) {
-                const int rr = idx / nv, c = (idx % nv) * W;
-                vstore(lds_b + rr * lp + c, vload(gb + static_cast<size_t>(e0 + rr) * p + c));
-            }
+            const bool ok = lane_live && row < e1;
+            u[r] = ok ? gload(g + static_cast<size_t>(row) * p + col) : vzero<T>();
+            if (HAS_B) bb[r] = ok ? gload(gb + static_cast<size_t>(row) * p + col) : vzero<T>();
         }
     }
     int par = 0;
     int remaining = n;
     while (remaining > 0) {
         const int sc = min(m, remaining);
-        for (int s = 0; s < sc; ++s) {
+        for (int s = 1; s <= sc; ++s) {
+            // rows of this sub-sweep (as in the LDS tile) and, red-black, the colour
+            const int lo = max(1, r0 - (sc - s));
+            const int hi = min(ny - 1, r1 + (sc - s));
+            const int parity = (n - remaining + s - 1) & 1;
             T* base = lds + static_cast<size_t>(par * nwv) * S::size;
             T* mine = base + static_cast<size_t>(wave) * S::size;
             if (wave_live) {
                 vstore(mine + S::top + lane * W, u[0]);
                 vstore(mine + S::bottom + lane * W, u[RT - 1]);
-                if (lane == 0) {
+                if (cw > 1 && (lane == 0 || lane == 63)) {
+                    const bool first = lane == 0;
+                    T* dst = mine + (first ? S::first_col : S::last_col);
 #pragma unroll
-                    for (int r = 0; r < RT; ++r) mine[S::first_col + r] = u[r].v[0];
-                }
-                if (lane == 63) {
-#pragma unroll
-                    for (int r = 0; r < RT; ++r) mine[S::last_col + r] = u[r].v[W - 1];
+                    for (int r = 0; r < RT; ++r) dst[r] = first ? u[r].v[0] : u[r].v[W - 1];
                 }
             }
             __syncthreads();
-            if (wave_live) {
+            // wave-uniform: which of this wave's rows take part (a bit per row)
+            const int first = max(0, lo - row_base), last = min(RT, hi - row_base);
+            const uint32_t act = (wave_live && first < last) ? ((1u << last) - (1u << first)) : 0u;
+            if (act) {
                 const Vec<T> above = rg > 0 ? vload(base + static_cast<size_t>(wave - cw) * S::size + S::bottom + lane * W)
                                             : vzero<T>();
                 const Vec<T> below = rg + 1 < rw ? vload(base + static_cast<size_t>(wave + cw) * S::size + S::top + lane * W)
@@ -128,52 +128,75 @@ __device__ void reg_sweep_rows(const pk_kargs& a, int n, int& cur, BarrierCtx& b
                 Vec<T> prev = above;
 #pragma unroll
                 for (int r = 0; r < RT; ++r) {
-                    const Vec<T> nxt = (r + 1 < RT) ? u[r + 1 < RT ? r + 1 : r] : below;
+                    const Vec<T> old = u[r];
                     const int row = row_base + r;
-                    Vec<T> bb = vzero<T>();
-                    if (HAS_B && row < e1) bb = vload(lds_b + (row - e0) * lp + col);
-                    const Vec<T> o = stencil<T, HAS_B>(prev, u[r], nxt, bb, edge[r], col, nx);
-                    prev = u[r];
-                    const bool keep = row <= 0 || row >= ny - 1 || row >= e1;  // wave-uniform
-                    if (!keep) u[r] = o;
+                    if (act & (1u << r)) {  // wave-uniform
+                        const Vec<T> nxt = (r + 1 < RT) ? u[r + 1 < RT ? r + 1 : r] : below;
+                        const T e = edge[r];
+                        const T west = from_lower(e, old.v[W - 1]);
+                        const T east = from_upper(e, old.v[0]);
+                        Vec<T> o;
+#pragma unroll
+                        for (int k = 0; k < W; ++k) {
+                            const T w = (k == 0) ? west : old.v[k - 1];
+                            const T ea = (k == W - 1) ? east : old.v[k + 1];
+                            T x = (w + ea) + (prev.v[k] + nxt.v[k]);
+                            if (HAS_B) x = x + bb[r].v[k];
+                            o.v[k] = blend(keep[k], old.v[k], T(0.25) * x);
+                        }
+                        if (RB) o = rb_keep(o, old, row, parity);
+                        u[r] = o;
+                    }
+                    prev = old;
                 }
             }
             par ^= 1;
         }
         remaining -= sc;
         const int mn = min(m, remaining);
-        {   // publish edge rows for the neighbours, or every owned row at the end
+        {   // publish: edge rows for the neighbours, or every owned row at the end
             T* g = static_cast<T*>(a.u[cur ^ 1]);
+            int top_end, bot_begin;
+            if (remaining == 0) {
+                top_end = r1;
+                bot_begin = r1;
+            } else {
+                top_end = (r0 > 1) ? min(r1, r0 + mn) : r0;
+                bot_begin = (r1 < ny - 1) ? max(top_end, r1 - mn) : r1;
+            }
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 const int row = row_base + r;
-                const bool own = row >= r0 && row < r1;
-                const bool need = remaining == 0 || (r0 > 1 && row < r0 + mn) || (r1 < ny - 1 && row >= r1 - mn);
-                if (lane_live && own && need) vstore(g + static_cast<size_t>(row) * p + col, u[r]);
+                const bool out = (row >= r0 && row < top_end) || (row >= bot_begin && row < r1);
+                if (lane_live && out) gstore(g + static_cast<size_t>(row) * p + col, u[r]);
             }
         }
-        grid_barrier(bc, bc.broken);
+        if (remaining > 0 && a.exchange == PK_EXCHANGE_NEIGHBOR)
+            neighbor_sync(bc, a.nbr, lb, a.res_dist);
+        else
+            grid_barrier(bc, bc.broken);
         cur ^= 1;
         if (remaining > 0) {  // the neighbours' edge rows become this block's halo
             const T* g = static_cast<const T*>(a.u[cur]);
+            const int above = min(mn, r0 - 1);  // interior rows only: row 0 is ring
+            const int below = min(mn, ny - 1 - r1);
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 const int row = row_base + r;
-                const bool halo = (r0 > 1 && row >= r0 - mn && row < r0) || (r1 < ny - 1 && row >= r1 && row < r1 + mn);
-                if (lane_live && row < e1 && halo) u[r] = vload(g + static_cast<size_t>(row) * p + col);
+                const bool halo = (row >= r0 - above && row < r0) || (row >= r1 && row < r1 + below);
+                if (lane_live && halo) u[r] = gload(g + static_cast<size_t>(row) * p + col);
             }
         }
     }
 }
 
-// Rows per wave are a compile-time count (2, 4 or 8), chosen per engine.
-template <typename T, bool HAS_B>
-__device__ void reg_sweep_task(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
-    switch (a.reg_rows) {
-        case 2: reg_sweep_rows<T, HAS_B, 2>(a, n, cur, bc, lds); break;
-        case 4: reg_sweep_rows<T, HAS_B, 4>(a, n, cur, bc, lds); break;
-        default: reg_sweep_rows<T, HAS_B, 8>(a, n, cur, bc, lds); break;
-    }
+// Rows per wave are a compile-time count (2 or 4), chosen per engine.
+template <typename T, bool HAS_B, bool RB>
+__device__ __forceinline__ void reg_sweep_task(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
+    if (a.reg_rows == 2)
+        reg_sweep_rows<T, HAS_B, RB, 2>(a, n, cur, bc, lds);
+    else
+        reg_sweep_rows<T, HAS_B, RB, 4>(a, n, cur, bc, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -191,7 +214,7 @@ __device__ void reg_sweep_task(const pk_kargs& a, int n, int& cur, BarrierCtx& b
 // ---------------------------------------------------------------------------
 // n sub-sweeps: Jacobi sweeps, or (RB) red-black half-sweeps, red first.
 template <typename T, bool HAS_B, bool RB>
-__device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
+__device__ __forceinline__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
     constexpr int W = VecW<T>::W;
     const int lb = logical_block(a.xcd_remap, a.grid);
     const int ny = a.ny;
@@ -319,7 +342,7 @@ __device__ void resident_sweep_task(const pk_kargs& a, int n, int& cur, BarrierC
 
 // Copy the field (unpadded rows) into the pinned host staging buffer.
 template <typename T>
-__device__ void readback_task(const pk_kargs& a, int cur) {
+__device__ __forceinline__ void readback_task(const pk_kargs& a, int cur) {
     const T* g = static_cast<const T*>(a.u[cur]);
     T* h = static_cast<T*>(a.staging);
     const int lane = threadIdx.x & 63;
@@ -340,7 +363,7 @@ __device__ void readback_task(const pk_kargs& a, int cur) {
 // Slots alternate by round parity so a fast block never overwrites a slot that
 // a slow block is still checking (the stamp/validate pattern of the ping-pong
 // example on the persistent-thread page, "Task Dispatch").
-__device__ int64_t stamp_task(const pk_kargs& a, int n, uint32_t& round, BarrierCtx& bc,
+__device__ __forceinline__ int64_t stamp_task(const pk_kargs& a, int n, uint32_t& round, BarrierCtx& bc,
                               double* s_red) {
     int64_t errs = 0;
     const int g = a.grid;
@@ -387,7 +410,7 @@ __device__ int64_t stamp_task(const pk_kargs& a, int n, uint32_t& round, Barrier
 // uses 512 so that each lane can hold 16 rows of u and b (256 VGPRs per lane).
 // n Jacobi sweeps of the field in u[cur] in the engine's layout (cur flips).
 // n sub-sweeps in the engine's layout: Jacobi sweeps, or (rb) red-black
-// half-sweeps, red first (not in the register layout).
+// half-sweeps, red first.
 template <typename T, bool HAS_B, int LAYOUT>
 __device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, int& cur, BarrierCtx& bc,
                                             T* lds) {
@@ -397,7 +420,10 @@ __device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, i
         else
             resident_sweep_task<T, HAS_B, false>(a, n, cur, bc, lds);
     } else if constexpr (LAYOUT == PK_LAYOUT_REGISTER) {
-        reg_sweep_task<T, HAS_B>(a, n, cur, bc, lds);
+        if (rb)
+            reg_sweep_task<T, HAS_B, true>(a, n, cur, bc, lds);
+        else
+            reg_sweep_task<T, HAS_B, false>(a, n, cur, bc, lds);
     } else {
         for (int s = 0; s < n;) {
             const int k = min(a.pass_sweeps, n - s);
@@ -438,7 +464,7 @@ __device__ __forceinline__ double residual_round(const pk_kargs& a, int cur, Bar
 
 template <int LAYOUT>
 struct PkMaxThreads {
-    static constexpr int value = LAYOUT == PK_LAYOUT_REGISTER ? 512 : 1024;
+    static constexpr int value = 1024;
 };
 
 template <typename T, bool HAS_B, int LAYOUT>
@@ -630,9 +656,7 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
                 tol = s_tol;
                 every = s_every;
             }
-            if (rb && LAYOUT == PK_LAYOUT_REGISTER) {
-                status = PK_EINVAL;
-            } else {
+            {
                 int done = 0;
                 for (;;) {  // the same decisions in every block
                     if (check) {
