@@ -247,8 +247,8 @@ def main():
     ap.add_argument("--max-blocks", type=int, default=0)
     ap.add_argument("--halo", type=int, default=0)
     ap.add_argument("--barrier", default="auto", choices=["auto", "flat", "two_level", "xcd"])
-    ap.add_argument("--exchange", default="auto", choices=["auto", "barrier", "neighbor"],
-                    help="resident layout: halo exchange by grid barrier or neighbour flags")
+    ap.add_argument("--exchange", default="auto", choices=["auto", "barrier", "neighbor", "tagged"],
+                    help="tile layouts: halo exchange by grid barrier, neighbour flags or tagged words")
     ap.add_argument("--pass-sweeps", type=int, default=0, help="stream layout: sweeps per pass")
     ap.add_argument("--band-rows", type=int, default=0, help="stream passes: rows per band")
     ap.add_argument("--launch-steps", type=int, default=0,
@@ -304,7 +304,7 @@ def main():
     barrier = {"auto": pk.PK_BARRIER_AUTO, "flat": pk.PK_BARRIER_FLAT,
                "two_level": pk.PK_BARRIER_TWO_LEVEL, "xcd": pk.PK_BARRIER_XCD}[args.barrier]
     exchange = {"auto": pk.PK_EXCHANGE_AUTO, "barrier": pk.PK_EXCHANGE_BARRIER,
-                "neighbor": pk.PK_EXCHANGE_NEIGHBOR}[args.exchange]
+                "neighbor": pk.PK_EXCHANGE_NEIGHBOR, "tagged": pk.PK_EXCHANGE_TAGGED}[args.exchange]
     opts = dict(layout=layout, threads=args.threads, max_blocks=args.max_blocks,
                 halo_depth=args.halo, idle_timeout_s=args.idle_timeout, barrier=barrier,
                 pass_sweeps=args.pass_sweeps, band_rows=args.band_rows, exchange=exchange)
@@ -378,7 +378,7 @@ def main():
             "halo_depth": info.halo_depth,
             "band_rows": info.band_rows,
             "barrier": {1: "flat", 2: "two_level", 3: "xcd"}[info.barrier],
-            "exchange": {0: None, 1: "barrier", 2: "neighbor"}[info.exchange],
+            "exchange": {0: None, 1: "barrier", 2: "neighbor", 3: "tagged"}[info.exchange],
             "pass_sweeps": info.pass_sweeps,
         },
         "per_launch": None if args.persistent_only else {

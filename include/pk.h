@@ -145,10 +145,22 @@ extern "C" {
  *   one exchange ahead of a neighbour, which the two device buffers allow.
  *   The last exchange of every task is still a grid barrier, so a task ends
  *   with the whole field in device memory.
- * AUTO: NEIGHBOR, or BARRIER under PK_DBG_BROKEN_BARRIER.                     */
+ * TAGGED (REGISTER layout only): no barrier and no flag. Every published
+ *   32-bit half of a halo value travels in one 64-bit word together with the
+ *   exchange number, stored and loaded as relaxed device-scope atomics into
+ *   one of two buffers (by exchange parity); a reader loads its halo words
+ *   until every one carries the current number. A word is written whole or
+ *   not at all, so a matching tag proves its value; no cache write-back or
+ *   invalidation is needed. A block publishes exchange e + 2 into the buffer
+ *   of exchange e only after it has read its neighbours' exchange e + 1,
+ *   which they publish only after reading e. The last exchange of every task
+ *   is a grid barrier, as above.
+ * AUTO: the cheaper of the kinds the layout supports by the cost model, or
+ *   BARRIER under PK_DBG_BROKEN_BARRIER.                                      */
 #define PK_EXCHANGE_AUTO 0
 #define PK_EXCHANGE_BARRIER 1
 #define PK_EXCHANGE_NEIGHBOR 2
+#define PK_EXCHANGE_TAGGED 3
 
 typedef struct pk_opts {
     int dtype;             /* PK_F32 or PK_F64                                       */
@@ -205,7 +217,7 @@ typedef struct pk_info {
     int strips;             /* STREAM: column strips                                     */
     int barrier;            /* PK_BARRIER_FLAT, _TWO_LEVEL or _XCD                       */
     int pass_sweeps;        /* STREAM: sweeps per pass                                   */
-    int exchange;           /* tiles: PK_EXCHANGE_BARRIER or _NEIGHBOR; 0 otherwise      */
+    int exchange;           /* tiles: PK_EXCHANGE_BARRIER, _NEIGHBOR or _TAGGED; else 0  */
     size_t lds_bytes;       /* dynamic LDS per block                                     */
     double kernel_ms;       /* PERSISTENT: launch-to-exit time of the kernel (HIP        */
                             /* events on its stream), valid after EXIT; LAUNCH: total   */

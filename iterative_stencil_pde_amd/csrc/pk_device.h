@@ -72,6 +72,45 @@ __device__ __forceinline__ T gload1(const T* p) {
 }
 
 // ---------------------------------------------------------------------------
+// Tagged halo words: a 16-byte vector travels as four 64-bit words, each a
+// 32-bit quarter of the data (low half) and the exchange tag (high half),
+// stored and loaded as relaxed device-scope atomics. A 64-bit atomic access is
+// whole, so a word whose tag matches carries that exchange's data. Quarter k
+// of the vectors of a row lies in plane k (`plane` words apart), so the lanes
+// of a wave touch consecutive words in every access.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void tag_store(uint64_t* p, int plane, const Vec<T>& x, uint32_t tag) {
+    const NativeVec<T> v = x.v;
+    const uint32_t* h = reinterpret_cast<const uint32_t*>(&v);
+    const uint64_t hi = static_cast<uint64_t>(tag) << 32;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        __hip_atomic_store(p + static_cast<size_t>(k) * plane, hi | h[k], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Loads the four words; true when every one carries `tag` (x is then the data).
+template <typename T>
+__device__ __forceinline__ bool tag_load(const uint64_t* p, int plane, Vec<T>& x, uint32_t tag) {
+    uint64_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = __hip_atomic_load(const_cast<uint64_t*>(p + static_cast<size_t>(k) * plane), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    NativeVec<T> v;
+    uint32_t* h = reinterpret_cast<uint32_t*>(&v);
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        h[k] = static_cast<uint32_t>(w[k]);
+        ok = ok && static_cast<uint32_t>(w[k] >> 32) == tag;
+    }
+    x.v = v;
+    return ok;
+}
+
+// ---------------------------------------------------------------------------
 // Whole-wave lane shifts (DPP wave_shr:1 / wave_shl:1). Lane l receives the
 // value of lane l-1 (from_lower) or l+1 (from_upper); the lane with no source
 // (0 or 63) keeps `edge`, which the caller loads from memory for exactly that
@@ -239,6 +278,7 @@ struct BarrierCtx {
     uint32_t xmembers;   // XCD barrier: blocks on this XCD
     uint32_t xgroups;    // XCD barrier: XCDs with at least one block
     uint32_t nbr_epoch;  // neighbour exchanges completed (identical in every block)
+    uint32_t tag_epoch;  // tagged exchanges completed (identical in every block)
     uint32_t nbar;       // grid barriers passed (identical in every block)
     // task carry: leader-only state in the block's shared memory (registers
     // live across every pass cost the streaming kernels spills), except the

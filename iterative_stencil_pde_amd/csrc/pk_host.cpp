@@ -74,6 +74,7 @@ struct pk_engine {
     double* d_partials = nullptr;
     uint32_t* d_stamp = nullptr;
     uint32_t* d_nbr = nullptr;
+    uint64_t* d_tag = nullptr;  // tagged halo words (PK_EXCHANGE_TAGGED only)
     pk_mailbox* h_mail = nullptr;
     pk_mailbox* d_mail = nullptr;
     void* h_staging = nullptr;
@@ -125,6 +126,7 @@ void release(pk_engine* e) {
     if (e->d_partials) (void)hipFree(e->d_partials);
     if (e->d_stamp) (void)hipFree(e->d_stamp);
     if (e->d_nbr) (void)hipFree(e->d_nbr);
+    if (e->d_tag) (void)hipFree(e->d_tag);
     if (e->h_mail) (void)hipHostFree(e->h_mail);
     if (e->h_staging) (void)hipHostFree(e->h_staging);
     if (e->h_lres) (void)hipHostFree(e->h_lres);
@@ -134,21 +136,31 @@ void release(pk_engine* e) {
 
 // ---------------------------------------------------------------------------
 // Planning of the tile layouts (RESIDENT in LDS, REGISTER in VGPRs): one band of
-// interior rows per block, bands of q or q+1 rows, halo depth m (the register
-// tile: m <= q), tile height ext = band + 2m.
-// Estimated time per sweep = sub-sweep + exchange / m, with costs fitted to 146
+// interior rows per block, bands of q or q+1 rows, halo depth m, tile height
+// ext = band + 2m (the halo may reach past the adjacent bands, m > q: every
+// block then publishes min(band, 2m) rows and reloads 2m).
+// Estimated time per sweep = sub-sweep + exchange / m, with costs fitted to
 // measured configurations on MI355X (one block of 16 waves per CU; 256^2 and
 // 1024^2, block counts that are multiples of 8, halos up to 20 rows; rms error
-// 0.06 us per sweep):
+// about 0.05 us per sweep). With A = band + m - 1, the rows of an average
+// sub-sweep:
 //   LDS sub-sweep: 0.31 us + 0.30 us per work item (a 64-lane row segment)
-//     per wave, over the rows of an average sub-sweep (band + m - 1);
+//     per wave;
 //   exchange with the grid barrier:   2.48 us + 0.0105 us per block;
 //   exchange with neighbour flags:    1.39 us + 0.0034 us per KB moved + 0.020 us per block
 //     + 0.29 us per further band the halo reaches (one more pair of flags to poll;
 //     every block also writes its XCD's L2 back on its own).
-// The halo may reach past the adjacent bands (m > q): every block then
-// publishes min(band, 2m) rows and reloads 2m.
-// The register tile keeps its own rough estimate (~25 ns per register row).
+// The register tile, from 606 configurations (256^2 fp32 Poisson, 512^2 and
+// 1024^2 Laplace; rms error 0.08 us per sweep), with r rows per wave:
+//   sub-sweep: 0.36 us (+ 0.11 with several column strips) + 0.033 us per row
+//     segment per SIMD (ceil(A / r) r x strips / 4: the waves go round the 4
+//     SIMDs of the CU);
+//   exchange with the grid barrier:   2.38 us + 0.019 us per KB moved + 0.0086 us per block;
+//   exchange with neighbour flags:    0.91 us + 0.046 us per KB + 0.015 us per block
+//     + 0.32 us per further band;
+//   exchange with tagged words:       0.72 us + 0.048 us per KB of field rows moved
+//     + 0.0028 us per block + 0.08 us per further band (the words are twice
+//     the data, uncached).
 // ---------------------------------------------------------------------------
 struct TilePlan {
     int g = 0, q = 0, rem = 0, m = 0, ext = 0, rows = 0, cw = 1;
@@ -158,7 +170,12 @@ struct TilePlan {
 };
 
 // dist: bands the halo reaches on each side (neighbour flags polled per side)
-double exchange_estimate_us(int exchange, int g, double kb, int dist) {
+double exchange_estimate_us(int exchange, int g, double kb, int dist, bool register_tile) {
+    if (register_tile) {
+        if (exchange == PK_EXCHANGE_TAGGED) return 0.720 + 0.0479 * kb + 0.0028 * g + 0.081 * (dist - 1);
+        if (exchange == PK_EXCHANGE_NEIGHBOR) return 0.913 + 0.0458 * kb + 0.0147 * g + 0.321 * (dist - 1);
+        return 2.38 + 0.0189 * kb + 0.0086 * g;
+    }
     return exchange == PK_EXCHANGE_NEIGHBOR ? 1.39 + 0.0034 * kb + 0.020 * g + 0.286 * (dist - 1)
                                             : 2.48 + 0.0105 * g;
 }
@@ -199,8 +216,11 @@ TilePlan tile_candidate(int nx, int ny, int esize, bool has_b, int nwv, size_t l
         if (t.lds > lds_max) return TilePlan{};
         reg_rows = [rw](int ext) { return (ext + rw - 1) / rw <= 2 ? 2 : kRegRows; };
         // the waves go round the CU's 4 SIMDs, so the active row segments of a
-        // sub-sweep spread over them; column groups add an edge exchange
-        sub_us = [cw](double rows, int) { return 0.14 + (cw > 1 ? 0.06 : 0.0) + 0.075 * rows * cw / 4.0; };
+        // sub-sweep spread over them (in whole waves of r rows); column groups
+        // add an edge exchange
+        sub_us = [cw](double rows, int r) {
+            return 0.362 + (cw > 1 ? 0.109 : 0.0) + 0.0334 * std::ceil(rows / r) * r * cw / 4.0;
+        };
     } else {
         const size_t row_bytes = static_cast<size_t>(lp) * esize * (has_b ? 3 : 2);
         max_rows = static_cast<int>(lds_max / row_bytes);
@@ -240,9 +260,9 @@ TilePlan tile_candidate(int nx, int ny, int esize, bool has_b, int nwv, size_t l
         const double kb = (std::min(q, 2 * m) + 2.0 * m) * lp * esize / 1024.0;
         const int dist = (m + q - 1) / q;  // bands the halo reaches on each side
         const int r = register_tile ? reg_rows(ext_of(m)) : 0;
-        for (int x = PK_EXCHANGE_BARRIER; x <= PK_EXCHANGE_NEIGHBOR; ++x) {
+        for (int x = PK_EXCHANGE_BARRIER; x <= PK_EXCHANGE_TAGGED; ++x) {
             if (!(exchanges & (1 << x))) continue;
-            const double c = sub_us(band_max + m - 1.0, r) + exchange_estimate_us(x, g, kb, dist) / m;
+            const double c = sub_us(band_max + m - 1.0, r) + exchange_estimate_us(x, g, kb, dist, register_tile) / m;
             if (c < t.cost) {
                 t.cost = c;
                 t.m = m;
@@ -295,17 +315,22 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     bool tiled = false;
     if (e->mode == PK_PERSISTENT && o.layout != PK_LAYOUT_STREAM) {
         TilePlan reg, lds;
-        // exchange kinds the LDS tile may use (bit per PK_EXCHANGE_* value)
+        // exchange kinds each tile may use (bit per PK_EXCHANGE_* value); tagged
+        // words are the register tile's only
         const int exchanges = o.exchange != PK_EXCHANGE_AUTO ? (1 << o.exchange)
                               : (o.flags & PK_DBG_BROKEN_BARRIER) ? (1 << PK_EXCHANGE_BARRIER)
-                              : ((1 << PK_EXCHANGE_BARRIER) | (1 << PK_EXCHANGE_NEIGHBOR));
+                              : ((1 << PK_EXCHANGE_BARRIER) | (1 << PK_EXCHANGE_NEIGHBOR) |
+                                 (1 << PK_EXCHANGE_TAGGED));
         if (o.layout == PK_LAYOUT_AUTO || o.layout == PK_LAYOUT_REGISTER)
             reg = best_tile(e->nx, e->ny, e->esize, e->has_b, nwv, lds_max, e->cus, o.max_blocks,
                             o.halo_depth, true, exchanges);
-        if (o.layout == PK_LAYOUT_AUTO || o.layout == PK_LAYOUT_RESIDENT)
+        if ((o.layout == PK_LAYOUT_AUTO || o.layout == PK_LAYOUT_RESIDENT) &&
+            (exchanges & ~(1 << PK_EXCHANGE_TAGGED)))
             lds = best_tile(e->nx, e->ny, e->esize, e->has_b, nwv, lds_max, e->cus, o.max_blocks,
-                            o.halo_depth, false, exchanges);
-        const bool use_reg = reg.g && (!lds.g || reg.cost <= lds.cost);
+                            o.halo_depth, false, exchanges & ~(1 << PK_EXCHANGE_TAGGED));
+        // one block needs no synchronisation at all: the single-block LDS tile
+        // keeps its 1.2x preference against the register tile too
+        const bool use_reg = reg.g && (!lds.g || (lds.g == 1 ? reg.cost * 1.2 < lds.cost : reg.cost <= lds.cost));
         const TilePlan& t = use_reg ? reg : lds;
         if (t.g) {
             p.layout = use_reg ? PK_LAYOUT_REGISTER : PK_LAYOUT_RESIDENT;
@@ -419,6 +444,8 @@ void fill_kargs(pk_engine* e) {
     a.stamp = e->d_stamp;
     a.nbr = e->d_nbr;
     a.exchange = p.exchange;
+    a.tag = e->d_tag;
+    a.tag_pitch = 4 * (e->pitch * e->esize / 16);
 }
 
 bool poll_exited(void* ctx) {
@@ -469,9 +496,12 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     // the negative control relaxes the flat/two-level barriers; the XCD barrier keeps
     // separate counters, so the two are not combined
     if ((o.flags & PK_DBG_BROKEN_BARRIER) && o.barrier == PK_BARRIER_XCD) return PK_EINVAL;
-    if (o.exchange < PK_EXCHANGE_AUTO || o.exchange > PK_EXCHANGE_NEIGHBOR) return PK_EINVAL;
+    if (o.exchange < PK_EXCHANGE_AUTO || o.exchange > PK_EXCHANGE_TAGGED) return PK_EINVAL;
     // the negative control weakens the grid barrier only
-    if ((o.flags & PK_DBG_BROKEN_BARRIER) && o.exchange == PK_EXCHANGE_NEIGHBOR) return PK_EINVAL;
+    if ((o.flags & PK_DBG_BROKEN_BARRIER) && o.exchange >= PK_EXCHANGE_NEIGHBOR) return PK_EINVAL;
+    // tagged words: the register tile only
+    if (o.exchange == PK_EXCHANGE_TAGGED && o.layout != PK_LAYOUT_AUTO && o.layout != PK_LAYOUT_REGISTER)
+        return PK_EINVAL;
     for (int r : o.reserved)
         if (r != 0) return PK_EINVAL;
     double h = o.h;
@@ -551,6 +581,12 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     const size_t nbr_bytes = sizeof(uint32_t) * PK_NBR_WORDS * e->plan.grid;
     PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_nbr), nbr_bytes));
     PK_TRY(hipMemsetAsync(e->d_nbr, 0, nbr_bytes, e->stream));
+    if (e->plan.exchange == PK_EXCHANGE_TAGGED) {
+        // two parities x ny rows x 4 words per 16-byte vector; tag 0 is never current
+        const size_t tag_bytes = sizeof(uint64_t) * 2 * static_cast<size_t>(ny) * 4 * (e->pitch * e->esize / 16);
+        PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_tag), tag_bytes));
+        PK_TRY(hipMemsetAsync(e->d_tag, 0, tag_bytes, e->stream));
+    }
     PK_TRY(hipHostMalloc(reinterpret_cast<void**>(&e->h_mail), sizeof(pk_mailbox),
                          hipHostMallocCoherent | hipHostMallocMapped));
     std::memset(e->h_mail, 0, sizeof(pk_mailbox));
@@ -578,6 +614,9 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     // a read of host memory over the bus takes ~1-2 us; compare a read-ahead
     // task slot only 2.5 us after issuing it
     e->ka.carry_age_ticks = static_cast<uint64_t>(2.5e-6 * wclk_khz * 1000.0);
+    // a neighbour's halo words arrive within microseconds of each other's; 2 s
+    // without them means a fault
+    e->ka.tag_ticks = static_cast<uint64_t>(2.0 * wclk_khz * 1000.0);
     PK_TRY(hipStreamSynchronize(e->stream));
     e->ring.attach(e->h_mail);
 

@@ -13,6 +13,16 @@ using namespace pkd;
 
 namespace {
 
+// Sweeps of the next period of a tile task with `remaining` sweeps left and
+// halo depth m: the remaining sweeps split into the fewest periods of at most m
+// sweeps, as evenly as possible (the same number of exchanges as periods of m,
+// and narrower trapezoids). Every block computes the same sequence.
+__device__ __forceinline__ int period_len(int remaining, int m) {
+    if (remaining <= 0) return 0;
+    const int periods = (remaining - 1) / m + 1;
+    return (remaining - 1) / periods + 1;
+}
+
 // Interior rows of band L when the interior is split into `grid` bands of
 // q or q+1 rows (the first `rem` bands get the extra row).
 __device__ __forceinline__ int band_begin(const pk_kargs& a, int L) {
@@ -85,7 +95,7 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
     int par = 0;
     int remaining = n;
     while (remaining > 0) {
-        const int sc = min(m, remaining);
+        const int sc = period_len(remaining, m);
         for (int s = 1; s <= sc; ++s) {
             // rows of this sub-sweep (as in the LDS tile) and, red-black, the colour
             const int lo = max(1, r0 - (sc - s));
@@ -153,17 +163,68 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
             par ^= 1;
         }
         remaining -= sc;
-        const int mn = min(m, remaining);
-        {   // publish: edge rows for the neighbours, or every owned row at the end
-            T* g = static_cast<T*>(a.u[cur ^ 1]);
-            int top_end, bot_begin;
-            if (remaining == 0) {
-                top_end = r1;
-                bot_begin = r1;
-            } else {
-                top_end = (r0 > 1) ? min(r1, r0 + mn) : r0;
-                bot_begin = (r1 < ny - 1) ? max(top_end, r1 - mn) : r1;
+        const int mn = period_len(remaining, m);  // the next period, 0 at the end
+        // rows to publish: edge rows for the neighbours, or every owned row at the end
+        int top_end, bot_begin;
+        if (remaining == 0) {
+            top_end = r1;
+            bot_begin = r1;
+        } else {
+            top_end = (r0 > 1) ? min(r1, r0 + mn) : r0;
+            bot_begin = (r1 < ny - 1) ? max(top_end, r1 - mn) : r1;
+        }
+        // rows to reload: the neighbours' edge rows (interior rows only: the ring
+        // never changes)
+        const int above = min(mn, r0 - 1);
+        const int below = min(mn, ny - 1 - r1);
+        if (remaining > 0 && a.exchange == PK_EXCHANGE_TAGGED) {
+            const uint32_t tag = bc.tag_epoch + 1;
+            uint64_t* tb = a.tag + static_cast<size_t>(bc.tag_epoch & 1u) * ny * a.tag_pitch;
+            const int vi = cg * 64 + lane;   // this lane's vector: word vi of each plane
+            const int plane = a.tag_pitch / 4;
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int row = row_base + r;
+                const bool out = (row >= r0 && row < top_end) || (row >= bot_begin && row < r1);
+                if (lane_live && out) tag_store(tb + static_cast<size_t>(row) * a.tag_pitch + vi, plane, u[r], tag);
             }
+            uint32_t need = 0;  // halo rows of this wave, a bit per row (wave-uniform)
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const int row = row_base + r;
+                if ((row >= r0 - above && row < r0) || (row >= r1 && row < r1 + below)) need |= 1u << r;
+            }
+            if (!wave_live) need = 0;
+            if (need && !bc.faulted) {
+                // load every halo word of the wave until all carry this exchange's tag
+                // (straight into the rows: their old values are not needed again)
+                const uint64_t t0 = wall_clock64();
+                for (;;) {
+                    bool ok = true;
+#pragma unroll
+                    for (int r = 0; r < RT; ++r) {
+                        if ((need & (1u << r)) && lane_live)
+                            ok = tag_load(tb + static_cast<size_t>(row_base + r) * a.tag_pitch + vi, plane, u[r],
+                                          tag) && ok;
+                    }
+                    if (__ballot(!ok) == 0) break;
+                    const bool late = wall_clock64() - t0 > a.tag_ticks ||
+                                      __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+                    if (late) {  // a fault elsewhere, or a tag that never comes: give up
+                        bc.faulted = true;
+                        if (lane == 0)
+                            __hip_atomic_store(&a.st->fault, static_cast<uint32_t>(PK_FAULT_BARRIER_TIMEOUT),
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            bc.tag_epoch = tag;
+            continue;  // the field buffers are untouched until the task's last exchange
+        }
+        {   // publish into the other field buffer
+            T* g = static_cast<T*>(a.u[cur ^ 1]);
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 const int row = row_base + r;
@@ -178,8 +239,6 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
         cur ^= 1;
         if (remaining > 0) {  // the neighbours' edge rows become this block's halo
             const T* g = static_cast<const T*>(a.u[cur]);
-            const int above = min(mn, r0 - 1);  // interior rows only: row 0 is ring
-            const int below = min(mn, ny - 1 - r1);
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 const int row = row_base + r;
@@ -267,7 +326,7 @@ __device__ __forceinline__ void resident_sweep_task(const pk_kargs& a, int n, in
     const TileMap<T> tm = tile_map<T>(nv, lp, a.nx);
     int remaining = n;
     while (remaining > 0) {
-        const int sc = min(m, remaining);
+        const int sc = period_len(remaining, m);
         for (int s = 1; s <= sc; ++s) {
             // rows of this sub-sweep: the owned band widened by the sub-sweeps
             // still to come, within the interior (a halo deeper than the
@@ -283,7 +342,7 @@ __device__ __forceinline__ void resident_sweep_task(const pk_kargs& a, int n, in
             D = t;
         }
         remaining -= sc;
-        const int mn = min(m, remaining);
+        const int mn = period_len(remaining, m);  // the next period, 0 at the end
 
         {   // publish: edge rows for the neighbours, or every owned row at the end
             T* g = static_cast<T*>(a.u[cur ^ 1]);
@@ -488,6 +547,7 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
     bc.xmembers = 1;
     bc.xgroups = 1;
     bc.nbr_epoch = 0;
+    bc.tag_epoch = 0;
     bc.nbar = 0;
     __shared__ CarryState s_carry;
     if (threadIdx.x == 0) {

@@ -147,5 +147,8 @@ struct pk_kargs {
     void* staging;         // readback target (pinned host, device-visible)
     uint32_t* stamp;       // 2 x grid x 64 words for the visibility check
     uint32_t* nbr;         // neighbour exchange flags, PK_NBR_WORDS words per block
-    int exchange;          // PK_EXCHANGE_BARRIER or PK_EXCHANGE_NEIGHBOR (resident)
+    int exchange;          // PK_EXCHANGE_BARRIER, _NEIGHBOR or _TAGGED (tiles)
+    uint64_t* tag;         // tagged halo words: 2 parities x ny rows x tag_pitch words
+    int tag_pitch;         // words per row: 4 planes of one word per 16-byte vector
+    uint64_t tag_ticks;    // longest wait for a tagged halo word (device clock ticks)
 };

@@ -30,7 +30,7 @@ PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP, PK_SWEEP_RB, PK_SWEEP_UNTI
 PK_DBG_BROKEN_BARRIER = 0x1
 PK_TASK_N_MAX = 0x0FFFFFFF
 PK_BARRIER_AUTO, PK_BARRIER_FLAT, PK_BARRIER_TWO_LEVEL, PK_BARRIER_XCD = 0, 1, 2, 3
-PK_EXCHANGE_AUTO, PK_EXCHANGE_BARRIER, PK_EXCHANGE_NEIGHBOR = 0, 1, 2
+PK_EXCHANGE_AUTO, PK_EXCHANGE_BARRIER, PK_EXCHANGE_NEIGHBOR, PK_EXCHANGE_TAGGED = 0, 1, 2, 3
 
 EXPORTED = ["pk_opts_default", "pk_create", "pk_submit", "pk_submit_until", "pk_wait", "pk_readback",
             "pk_run_launch_per_iter", "pk_run_graph_per_iter", "pk_get_info", "pk_destroy",

@@ -96,10 +96,14 @@ def test_create_rejects_bad_arguments_before_touching_a_device(lib):
     assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
     bad = pk.pk_opts_default(threads=100)
     assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
-    bad = pk.pk_opts_default(exchange=3)
+    bad = pk.pk_opts_default(exchange=4)
     assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
-    bad = pk.pk_opts_default(exchange=pk.PK_EXCHANGE_NEIGHBOR, flags=pk.PK_DBG_BROKEN_BARRIER)
-    assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
+    for x in (pk.PK_EXCHANGE_NEIGHBOR, pk.PK_EXCHANGE_TAGGED):  # the negative control keeps barriers
+        bad = pk.pk_opts_default(exchange=x, flags=pk.PK_DBG_BROKEN_BARRIER)
+        assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
+    for lay in (pk.PK_LAYOUT_STREAM, pk.PK_LAYOUT_RESIDENT):  # tagged words: register tile only
+        bad = pk.pk_opts_default(exchange=pk.PK_EXCHANGE_TAGGED, layout=lay)
+        assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
     bad = pk.pk_opts_default()
     bad.reserved[3] = 1
     assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL

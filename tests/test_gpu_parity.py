@@ -224,13 +224,22 @@ def test_register_layout_shapes(shape, blocks, dtype, poisson):
 TILES = {"lds": pk.PK_LAYOUT_RESIDENT, "register": pk.PK_LAYOUT_REGISTER}
 
 
+EXCHANGES = {"barrier": pk.PK_EXCHANGE_BARRIER, "neighbor": pk.PK_EXCHANGE_NEIGHBOR,
+             "tagged": pk.PK_EXCHANGE_TAGGED}
+
+
+def _tile_exchange_or_skip(tile, exchange):
+    if exchange == pk.PK_EXCHANGE_TAGGED and TILES[tile] != pk.PK_LAYOUT_REGISTER:
+        pytest.skip("tagged words are the register tile's exchange")
+
+
 @pytest.mark.parametrize("tile", sorted(TILES))
-@pytest.mark.parametrize("exchange", [pk.PK_EXCHANGE_BARRIER, pk.PK_EXCHANGE_NEIGHBOR],
-                         ids=["barrier", "neighbor"])
+@pytest.mark.parametrize("exchange", list(EXCHANGES.values()), ids=list(EXCHANGES))
 @pytest.mark.parametrize("blocks,halo", [(2, 5), (5, 3), (32, 7), (127, 2)])
 def test_resident_exchange_kinds(exchange, blocks, halo, tile):
     """Halo exchange by grid barrier or by neighbour flags: same field, same
     residuals. Task lengths are not multiples of the halo depth."""
+    _tile_exchange_or_skip(tile, exchange)
     w = inputs.poisson_uniform(256, 0, 100)
     w.script = [("residual",), ("sweep", 1), ("sweep", 11), ("residual",), ("sweep", 23),
                 ("sweep", 40), ("residual",), ("readback",)]
@@ -246,13 +255,13 @@ def test_resident_exchange_kinds(exchange, blocks, halo, tile):
 
 
 @pytest.mark.parametrize("tile", sorted(TILES))
-@pytest.mark.parametrize("exchange", [pk.PK_EXCHANGE_BARRIER, pk.PK_EXCHANGE_NEIGHBOR],
-                         ids=["barrier", "neighbor"])
+@pytest.mark.parametrize("exchange", list(EXCHANGES.values()), ids=list(EXCHANGES))
 @pytest.mark.parametrize("blocks,halo", [(32, 12), (64, 10), (85, 16), (127, 9), (200, 5), (16, 18)])
 def test_resident_halo_deeper_than_band(exchange, blocks, halo, tile):
     """A halo deeper than a block's band reaches several neighbouring bands (and,
     near the edges, the ring): same field and residuals as the oracle, for task
     lengths that end part-way through a period, also in red-black."""
+    _tile_exchange_or_skip(tile, exchange)
     w = inputs.poisson_uniform(256, 0, 100)
     w.script = [("residual",), ("sweep", 3), ("sweep", 29), ("residual",), ("sweep_rb", 7),
                 ("sweep", 41), ("residual",), ("readback",)]
@@ -314,6 +323,8 @@ UNTIL_MODES = {
     "auto": dict(mode=pk.PK_PERSISTENT),
     "stream3": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=3),
     "register": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_REGISTER, max_blocks=32),
+    "tagged": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_REGISTER, max_blocks=64, halo_depth=9,
+                   exchange=pk.PK_EXCHANGE_TAGGED),
     "launch": dict(mode=pk.PK_LAUNCH),
 }
 
@@ -487,8 +498,7 @@ def test_red_black_persistent_and_launch_agree_bitwise():
 
 
 @pytest.mark.parametrize("blocks,halo", [(1, 0), (8, 3), (32, 7), (64, 2), (127, 1)])
-@pytest.mark.parametrize("exchange", [pk.PK_EXCHANGE_BARRIER, pk.PK_EXCHANGE_NEIGHBOR],
-                         ids=["barrier", "neighbor"])
+@pytest.mark.parametrize("exchange", list(EXCHANGES.values()), ids=list(EXCHANGES))
 def test_red_black_register(blocks, halo, exchange):
     """The register tile runs red-black half-sweeps like the LDS tile; odd halo
     depths put exchanges between the halves of an iteration."""
