@@ -643,7 +643,7 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
 // starting at c0 + ov * W. Results equal K single sweeps bit for bit: every
 // stored value is the same expression on the same operands.
 // ---------------------------------------------------------------------------
-template <typename T, bool HAS_B, int K, int DIR>
+template <typename T, bool HAS_B, int K, int DIR, bool RB>
 __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* __restrict__ dst,
                                                  const T* __restrict__ bsrc, int nx, int ny,
                                                  int pitch, int c0, int ov, int r0, int r1, int h0) {
@@ -702,7 +702,7 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
                 const int row = t - dir * j;  // level j row computed at this step
                 Vec<T> o = stencil<T, HAS_B>(win[j - 1][0], win[j - 1][1], win[j - 1][2], bq[j - 1],
                                              T(0), col, nx);
-                if (h0 >= 0) o = rb_keep(o, win[j - 1][1], row, (h0 + j - 1) & 1);  // wave-uniform
+                if (RB) o = rb_keep(o, win[j - 1][1], row, (h0 + j - 1) & 1);
                 if (row <= 0 || row >= ny - 1) o = win[j - 1][1];  // ring rows (and beyond)
                 if (j < K) {
                     win[j][0] = win[j][1];
@@ -718,7 +718,7 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
 
 // One pass of k sweeps (1 <= k <= PK_MAX_PASS) over all units, src -> dst.
 // h0 >= 0: the k levels are red-black half-sweeps, level j of colour (h0+j-1) mod 2.
-template <typename T, bool HAS_B, int K>
+template <typename T, bool HAS_B, int K, bool RB>
 __device__ __forceinline__ void stream_pass_k(const pk_kargs& a, const T* __restrict__ src,
                                               T* __restrict__ dst, int h0) {
     constexpr int W = VecW<T>::W;
@@ -735,11 +735,11 @@ __device__ __forceinline__ void stream_pass_k(const pk_kargs& a, const T* __rest
         const int r1 = min(a.ny - 1, r0 + a.pband_rows);
         if (r0 >= r1) continue;
         if (band & 1)
-            stream_pass_unit<T, HAS_B, K, -1>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W,
-                                              ov, r0, r1, h0);
+            stream_pass_unit<T, HAS_B, K, -1, RB>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W,
+                                                  ov, r0, r1, h0);
         else
-            stream_pass_unit<T, HAS_B, K, 1>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W,
-                                             ov, r0, r1, h0);
+            stream_pass_unit<T, HAS_B, K, 1, RB>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W,
+                                                 ov, r0, r1, h0);
     }
 }
 
@@ -748,13 +748,26 @@ __device__ __forceinline__ void stream_pass(const pk_kargs& a, const T* __restri
                                             T* __restrict__ dst, int k, int h0 = -1) {
     // a source term adds a window of b rows: passes of at most 3 sweeps then
     // (the host caps pass_sweeps accordingly), so the kernel stays within 128 VGPRs
+    // red-black passes are their own instances: the colour mask stays out of the
+    // Jacobi march
+    if (h0 >= 0) {
+        switch (k) {
+            case 2: stream_pass_k<T, HAS_B, 2, true>(a, src, dst, h0); break;
+            case 3: stream_pass_k<T, HAS_B, 3, true>(a, src, dst, h0); break;
+            case 4:
+                if (!HAS_B) stream_pass_k<T, HAS_B, 4, true>(a, src, dst, h0);
+                break;
+            default: stream_sweep<T, HAS_B>(a, src, dst, h0); break;
+        }
+        return;
+    }
     switch (k) {
-        case 2: stream_pass_k<T, HAS_B, 2>(a, src, dst, h0); break;
-        case 3: stream_pass_k<T, HAS_B, 3>(a, src, dst, h0); break;
+        case 2: stream_pass_k<T, HAS_B, 2, false>(a, src, dst, h0); break;
+        case 3: stream_pass_k<T, HAS_B, 3, false>(a, src, dst, h0); break;
         case 4:
-            if (!HAS_B) stream_pass_k<T, HAS_B, 4>(a, src, dst, h0);
+            if (!HAS_B) stream_pass_k<T, HAS_B, 4, false>(a, src, dst, h0);
             break;
-        default: stream_sweep<T, HAS_B>(a, src, dst, h0); break;
+        default: stream_sweep<T, HAS_B>(a, src, dst, -1); break;
     }
 }
 
