@@ -173,6 +173,14 @@ def stored_traffic(workload: str, steps_in_launch: int):
     return rec["bytes_per_step"] * steps_in_launch
 
 
+def default_plan(args) -> bool:
+    """True when the run uses the plan and method the stored counters were taken
+    with (Jacobi, every planner choice left to the planner)."""
+    return (args.method == "jacobi" and args.layout == "auto" and not args.threads and not args.max_blocks
+            and not args.halo and args.barrier == "auto" and args.exchange == "auto" and not args.pass_sweeps
+            and not args.band_rows)
+
+
 def _counter_rows(d):
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -401,7 +409,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 5) if achieved else None,
-            "traffic": stored_traffic(args.workload, args.steps + args.warmup),
+            # the stored counters were taken with the default plan and method
+            "traffic": stored_traffic(args.workload, args.steps + args.warmup) if default_plan(args) else None,
             "kernel": "pk_persistent",
             "kernel_ms": round(info_end.kernel_ms, 3),
             "algorithmic_bytes_per_launch": launch_bytes,
