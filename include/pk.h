@@ -181,8 +181,8 @@ typedef struct pk_opts {
     int barrier;           /* PK_BARRIER_*                                           */
     int pass_sweeps;       /* STREAM: sweeps per pass, 1..4: each wave carries k     */
                            /* levels of its band in registers, so the field crosses */
-                           /* HBM and the grid barrier once per k sweeps; 0 = 4,   */
-                           /* at most 3 with a source term (pk_info reports it)     */
+                           /* HBM and the grid barrier once per k sweeps; 0 = 4    */
+                           /* (pk_info reports it)                                  */
     int band_rows;         /* STREAM passes: rows per band (a unit is a band x one  */
                            /* strip, one per wave); 0 = automatic                   */
     int exchange;          /* RESIDENT, REGISTER: PK_EXCHANGE_*                      */

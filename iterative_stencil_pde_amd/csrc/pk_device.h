@@ -746,17 +746,13 @@ __device__ __forceinline__ void stream_pass_k(const pk_kargs& a, const T* __rest
 template <typename T, bool HAS_B>
 __device__ __forceinline__ void stream_pass(const pk_kargs& a, const T* __restrict__ src,
                                             T* __restrict__ dst, int k, int h0 = -1) {
-    // a source term adds a window of b rows: passes of at most 3 sweeps then
-    // (the host caps pass_sweeps accordingly), so the kernel stays within 128 VGPRs
     // red-black passes are their own instances: the colour mask stays out of the
     // Jacobi march
     if (h0 >= 0) {
         switch (k) {
             case 2: stream_pass_k<T, HAS_B, 2, true>(a, src, dst, h0); break;
             case 3: stream_pass_k<T, HAS_B, 3, true>(a, src, dst, h0); break;
-            case 4:
-                if (!HAS_B) stream_pass_k<T, HAS_B, 4, true>(a, src, dst, h0);
-                break;
+            case 4: stream_pass_k<T, HAS_B, 4, true>(a, src, dst, h0); break;
             default: stream_sweep<T, HAS_B>(a, src, dst, h0); break;
         }
         return;
@@ -764,9 +760,7 @@ __device__ __forceinline__ void stream_pass(const pk_kargs& a, const T* __restri
     switch (k) {
         case 2: stream_pass_k<T, HAS_B, 2, false>(a, src, dst, h0); break;
         case 3: stream_pass_k<T, HAS_B, 3, false>(a, src, dst, h0); break;
-        case 4:
-            if (!HAS_B) stream_pass_k<T, HAS_B, 4, false>(a, src, dst, h0);
-            break;
+        case 4: stream_pass_k<T, HAS_B, 4, false>(a, src, dst, h0); break;
         default: stream_sweep<T, HAS_B>(a, src, dst, -1); break;
     }
 }

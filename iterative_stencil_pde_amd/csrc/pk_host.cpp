@@ -367,13 +367,10 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     stream_geometry(p, e->nx, e->ny, e->esize, 4);
     // passes of k sweeps (stream layout, persistent only): about one unit per
     // wave, bands at least 4 k rows tall (each band re-reads 2 k halo rows)
-    // default: the deepest pass the kernel carries (4 levels, 3 with a source
-    // term); measured fastest on 4096^2 fp32 and 8192^2 fp64
+    // default: the deepest pass the kernel carries (4 levels)
     p.pass_sweeps = 1;
     if (e->mode == PK_PERSISTENT && p.layout == PK_LAYOUT_STREAM)
         p.pass_sweeps = o.pass_sweeps > 0 ? o.pass_sweeps : PK_MAX_PASS;
-    // with a source term the kernel carries a window of b rows too: at most 3
-    if (e->has_b && p.pass_sweeps > 3) p.pass_sweeps = 3;
     {
         const int k = p.pass_sweeps;
         const int ov = (k + W - 1) / W;

@@ -166,12 +166,12 @@ def test_stream_passes_of_k_sweeps(shape, dtype, poisson, k):
                          ("readback",)], "")
     ref = run_oracle_script(w)
     got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=k)
-    assert got["info"].pass_sweeps == (min(k, 3) if poisson else k)
+    assert got["info"].pass_sweeps == k
     check_against_oracle(w, got, ref, f"pass{k}/{ny}x{nx}/{np.dtype(dtype).name}")
 
 
 @pytest.mark.parametrize("name,sweeps,k", [("laplace4096", 41, 4), ("laplace4096", 23, 3),
-                                           ("poisson8192", 5, 2), ("poisson8192", 7, 3)])
+                                           ("poisson8192", 5, 2), ("poisson8192", 7, 3), ("poisson8192", 9, 4)])
 def test_stream_passes_full_size(name, sweeps, k):
     w = inputs.make(name)
     w.script = [("sweep", sweeps), ("residual",), ("readback",)]
@@ -446,8 +446,6 @@ def test_red_black_ragged(shape, dtype, poisson, mode):
                          ("sweep_rb", 8), ("residual",), ("readback",)], "")
     ref = run_oracle_script(w)
     opts = dict(RB_MODES[mode])
-    if poisson and opts.get("pass_sweeps", 0) == 4:
-        opts["pass_sweeps"] = 3
     try:
         got = run_engine_script(w, **opts)
     except pk.PkError as ex:
