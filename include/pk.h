@@ -167,7 +167,8 @@ typedef struct pk_opts {
     double h;              /* grid spacing; 0 => 1/(nx-1), which requires nx == ny  */
     int mode;              /* PK_PERSISTENT or PK_LAUNCH                             */
     int layout;            /* PK_LAYOUT_*; PK_LAUNCH always streams                  */
-    int threads;           /* threads per block, multiple of 64, <= 1024; 0 = auto   */
+    int threads;           /* threads per block, multiple of 64, <= 1024; 0 = auto;  */
+                           /* the persistent STREAM kernel takes at most 512         */
     int max_blocks;        /* grid size in blocks; 0 = automatic. STREAM uses it as */
                            /* given (PK_ELAUNCH if that grid cannot be co-resident),*/
                            /* the tiles as an upper bound (one band per block)    */
@@ -179,9 +180,9 @@ typedef struct pk_opts {
     double idle_timeout_s; /* the persistent kernel leaves by itself after this     */
                            /* long without a task; 0 => 120 s                       */
     int barrier;           /* PK_BARRIER_*                                           */
-    int pass_sweeps;       /* STREAM: sweeps per pass, 1..4: each wave carries k     */
+    int pass_sweeps;       /* STREAM: sweeps per pass, 1..8: each wave carries k     */
                            /* levels of its band in registers, so the field crosses */
-                           /* HBM and the grid barrier once per k sweeps; 0 = 4    */
+                           /* HBM and the grid barrier once per k sweeps; 0 = 8    */
                            /* (pk_info reports it)                                  */
     int band_rows;         /* STREAM passes: rows per band (a unit is a band x one  */
                            /* strip, one per wave); 0 = automatic                   */

@@ -753,6 +753,10 @@ __device__ __forceinline__ void stream_pass(const pk_kargs& a, const T* __restri
             case 2: stream_pass_k<T, HAS_B, 2, true>(a, src, dst, h0); break;
             case 3: stream_pass_k<T, HAS_B, 3, true>(a, src, dst, h0); break;
             case 4: stream_pass_k<T, HAS_B, 4, true>(a, src, dst, h0); break;
+            case 5: stream_pass_k<T, HAS_B, 5, true>(a, src, dst, h0); break;
+            case 6: stream_pass_k<T, HAS_B, 6, true>(a, src, dst, h0); break;
+            case 7: stream_pass_k<T, HAS_B, 7, true>(a, src, dst, h0); break;
+            case 8: stream_pass_k<T, HAS_B, 8, true>(a, src, dst, h0); break;
             default: stream_sweep<T, HAS_B>(a, src, dst, h0); break;
         }
         return;
@@ -761,6 +765,10 @@ __device__ __forceinline__ void stream_pass(const pk_kargs& a, const T* __restri
         case 2: stream_pass_k<T, HAS_B, 2, false>(a, src, dst, h0); break;
         case 3: stream_pass_k<T, HAS_B, 3, false>(a, src, dst, h0); break;
         case 4: stream_pass_k<T, HAS_B, 4, false>(a, src, dst, h0); break;
+        case 5: stream_pass_k<T, HAS_B, 5, false>(a, src, dst, h0); break;
+        case 6: stream_pass_k<T, HAS_B, 6, false>(a, src, dst, h0); break;
+        case 7: stream_pass_k<T, HAS_B, 7, false>(a, src, dst, h0); break;
+        case 8: stream_pass_k<T, HAS_B, 8, false>(a, src, dst, h0); break;
         default: stream_sweep<T, HAS_B>(a, src, dst, -1); break;
     }
 }

@@ -352,6 +352,9 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     }
     if (!tiled) {
         p.layout = PK_LAYOUT_STREAM;
+        // the persistent streaming kernel runs blocks of at most 512 threads (its
+        // passes keep up to 8 levels of the march in registers)
+        if (e->mode == PK_PERSISTENT) p.threads = std::min(p.threads, 512);
         const int wpb = p.threads / 64;
         // enough blocks for one wave per unit of >= 4 rows, at most one block per CU
         const int strips = ceil_div(e->nx, 64 * W);
@@ -367,7 +370,7 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     stream_geometry(p, e->nx, e->ny, e->esize, 4);
     // passes of k sweeps (stream layout, persistent only): about one unit per
     // wave, bands at least 4 k rows tall (each band re-reads 2 k halo rows)
-    // default: the deepest pass the kernel carries (4 levels)
+    // default: the deepest pass the kernel carries (8 levels)
     p.pass_sweeps = 1;
     if (e->mode == PK_PERSISTENT && p.layout == PK_LAYOUT_STREAM)
         p.pass_sweeps = o.pass_sweeps > 0 ? o.pass_sweeps : PK_MAX_PASS;

@@ -521,9 +521,11 @@ __device__ __forceinline__ double residual_round(const pk_kargs& a, int cur, Bar
     return r;
 }
 
+// The streaming kernel's passes keep up to 8 levels of the march in registers:
+// blocks of at most 512 threads give it 256 VGPRs per lane.
 template <int LAYOUT>
 struct PkMaxThreads {
-    static constexpr int value = 1024;
+    static constexpr int value = LAYOUT == PK_LAYOUT_STREAM ? 512 : 1024;
 };
 
 template <typename T, bool HAS_B, int LAYOUT>

@@ -14,7 +14,7 @@
 #include <stdint.h>
 
 #define PK_RING 64u
-#define PK_MAX_PASS 4
+#define PK_MAX_PASS 8
 #define PK_LINE 128
 
 // Internal task kinds (the public ones are in pk.h); kinds fit in 4 bits.

@@ -151,7 +151,7 @@ def test_xcd_barrier_full_size(name, sweeps):
     check_against_oracle(w, got, ref, f"{name}/xcd")
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("poisson", [False, True], ids=["laplace", "poisson"])
 @pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
 @pytest.mark.parametrize("shape", [(3, 3), (5, 300), (300, 5), (67, 131), (130, 257), (33, 1030),
@@ -170,8 +170,9 @@ def test_stream_passes_of_k_sweeps(shape, dtype, poisson, k):
     check_against_oracle(w, got, ref, f"pass{k}/{ny}x{nx}/{np.dtype(dtype).name}")
 
 
-@pytest.mark.parametrize("name,sweeps,k", [("laplace4096", 41, 4), ("laplace4096", 23, 3),
-                                           ("poisson8192", 5, 2), ("poisson8192", 7, 3), ("poisson8192", 9, 4)])
+@pytest.mark.parametrize("name,sweeps,k", [("laplace4096", 41, 4), ("laplace4096", 23, 3), ("laplace4096", 37, 8),
+                                           ("poisson8192", 5, 2), ("poisson8192", 7, 3), ("poisson8192", 9, 4),
+                                           ("poisson8192", 13, 8), ("poisson8192", 11, 6)])
 def test_stream_passes_full_size(name, sweeps, k):
     w = inputs.make(name)
     w.script = [("sweep", sweeps), ("residual",), ("readback",)]
@@ -426,6 +427,7 @@ RB_MODES = {
     "stream1": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=1),
     "stream3": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=3),
     "stream4": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=4),
+    "stream7": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=7),
     "register": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_REGISTER),
     "launch": dict(mode=pk.PK_LAUNCH),
 }
@@ -489,8 +491,11 @@ def test_red_black_full_size(name, iters):
 def test_red_black_persistent_and_launch_agree_bitwise():
     w = inputs.laplace_random_interior(1024, 0)
     w.script = [("sweep_rb", 9), ("residual",), ("readback",)]
-    a = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM)
-    b = run_engine_script(w, mode=pk.PK_LAUNCH)
+    # the residual's fixed summation order follows the block decomposition, so
+    # both engines take the same block size (the same block count follows)
+    a = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, threads=512)
+    b = run_engine_script(w, mode=pk.PK_LAUNCH, threads=512)
+    assert a["info"].grid_blocks == b["info"].grid_blocks
     assert np.array_equal(a["final"], b["final"])
     assert a["residuals"] == b["residuals"]
 
@@ -604,7 +609,10 @@ def test_eigenmode_decay_full_size_fp64():
 def test_persistent_and_launch_residuals_bitwise_equal():
     w = inputs.poisson_uniform(256, 300, 50)
     w.script = [s for s in w.script if s[0] != "readback"]
-    a = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM)
-    b = run_engine_script(w, mode=pk.PK_LAUNCH)
+    # the residual's fixed summation order follows the block decomposition, so
+    # both engines take the same block size (the same block count follows)
+    a = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, threads=512)
+    b = run_engine_script(w, mode=pk.PK_LAUNCH, threads=512)
+    assert a["info"].grid_blocks == b["info"].grid_blocks
     assert a["residuals"] == b["residuals"]
     assert np.array_equal(a["final"], b["final"])
