@@ -165,6 +165,28 @@ __device__ __forceinline__ double blend(uint32_t mask, double keep_val, double n
     return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
 }
 
+// The same lane shifts where the lane with no source (0 or 63) may receive
+// anything (here zero): its result is not used. Without an old value to keep,
+// the compiler can fold the shift into the add that consumes it.
+__device__ __forceinline__ float from_lower_any(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x138, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float from_upper_any(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x130, 0xf, 0xf, true));
+}
+__device__ __forceinline__ double from_lower_any(double v) {
+    const long long x = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x138, 0xf, 0xf, true);
+    const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(x >> 32), 0x138, 0xf, 0xf, true);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<long long>(static_cast<unsigned>(lo)));
+}
+__device__ __forceinline__ double from_upper_any(double v) {
+    const long long x = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x130, 0xf, 0xf, true);
+    const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(x >> 32), 0x130, 0xf, 0xf, true);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<long long>(static_cast<unsigned>(lo)));
+}
+
 // ---------------------------------------------------------------------------
 // The stencil on one lane's vector. `col` is the first column of the vector;
 // columns 0 and nx-1 (the Dirichlet ring) and padding columns >= nx keep

@@ -55,7 +55,10 @@ struct RegSlot {
                          last_col = 2 * 64 * W + PK_REG_RMAX;
 };
 
-template <typename T, bool HAS_B, bool RB, int RT>
+// ONE: a single column strip (cw == 1): lane 0's W neighbour and lane 63's E
+// neighbour can only belong to ring or padding columns, which keep their
+// values, so the lane shifts need no edge values.
+template <typename T, bool HAS_B, bool RB, int RT, bool ONE>
 __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
     constexpr int W = VecW<T>::W;
     using S = RegSlot<T>;
@@ -126,7 +129,8 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                 T edge[RT];
 #pragma unroll
                 for (int r = 0; r < RT; ++r) edge[r] = T(0);
-                if (lane == 0 && has_left) {
+                if (ONE) {
+                } else if (lane == 0 && has_left) {
                     const T* src = base + static_cast<size_t>(wave - 1) * S::size + S::last_col;
 #pragma unroll
                     for (int r = 0; r < RT; ++r) edge[r] = src[r];
@@ -142,9 +146,14 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                     const int row = row_base + r;
                     if (act & (1u << r)) {  // wave-uniform
                         const Vec<T> nxt = (r + 1 < RT) ? u[r + 1 < RT ? r + 1 : r] : below;
-                        const T e = edge[r];
-                        const T west = from_lower(e, old.v[W - 1]);
-                        const T east = from_upper(e, old.v[0]);
+                        T west, east;
+                        if constexpr (ONE) {
+                            west = from_lower_any(old.v[W - 1]);
+                            east = from_upper_any(old.v[0]);
+                        } else {
+                            west = from_lower(edge[r], old.v[W - 1]);
+                            east = from_upper(edge[r], old.v[0]);
+                        }
                         Vec<T> o;
 #pragma unroll
                         for (int k = 0; k < W; ++k) {
@@ -252,10 +261,17 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
 // Rows per wave are a compile-time count (2 or 4), chosen per engine.
 template <typename T, bool HAS_B, bool RB>
 __device__ __forceinline__ void reg_sweep_task(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
-    if (a.reg_rows == 2)
-        reg_sweep_rows<T, HAS_B, RB, 2>(a, n, cur, bc, lds);
-    else
-        reg_sweep_rows<T, HAS_B, RB, 4>(a, n, cur, bc, lds);
+    if (a.reg_cw == 1) {
+        if (a.reg_rows == 2)
+            reg_sweep_rows<T, HAS_B, RB, 2, true>(a, n, cur, bc, lds);
+        else
+            reg_sweep_rows<T, HAS_B, RB, 4, true>(a, n, cur, bc, lds);
+    } else {
+        if (a.reg_rows == 2)
+            reg_sweep_rows<T, HAS_B, RB, 2, false>(a, n, cur, bc, lds);
+        else
+            reg_sweep_rows<T, HAS_B, RB, 4, false>(a, n, cur, bc, lds);
+    }
 }
 
 // ---------------------------------------------------------------------------
