@@ -722,8 +722,11 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
 #pragma unroll
             for (int j = 1; j <= K; ++j) {
                 const int row = t - dir * j;  // level j row computed at this step
-                Vec<T> o = stencil<T, HAS_B>(win[j - 1][0], win[j - 1][1], win[j - 1][2], bq[j - 1],
-                                             T(0), col, nx);
+                // lanes 0 and 63 are overlap lanes (never stored): their outer
+                // neighbours may be anything, so the shifts need no edge value
+                const Vec<T>& mid = win[j - 1][1];
+                Vec<T> o = stencil_we<T, HAS_B>(win[j - 1][0], mid, win[j - 1][2], bq[j - 1],
+                                                from_lower_any(mid.v[W - 1]), from_upper_any(mid.v[0]), col, nx);
                 if (RB) o = rb_keep(o, win[j - 1][1], row, (h0 + j - 1) & 1);
                 if (row <= 0 || row >= ny - 1) o = win[j - 1][1];  // ring rows (and beyond)
                 if (j < K) {
