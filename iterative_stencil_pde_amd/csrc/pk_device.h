@@ -887,7 +887,10 @@ __device__ __forceinline__ TileMap<T> tile_map(int nv, int lp, int nx) {
 // Rows [lo, hi) of D from S (LDS row stride lp elements; Bt holds b).
 // RB: a red-black half-sweep; node colour from the global row (local row +
 // q_row) and column, updated when it equals `parity`.
-template <typename T, bool HAS_B, bool RB>
+// ONE: rows of one segment (at most 64 vectors): no lane ever needs an edge
+// element from LDS (a row's end lanes border ring or padding columns, which
+// keep their values), so the lane shifts take no edge value.
+template <typename T, bool HAS_B, bool RB, bool ONE>
 __device__ __forceinline__ void resident_rows(const T* S, T* D, const T* Bt, int lo, int hi,
                                               const TileMap<T>& t, int q_row = 0, int parity = 0) {
     constexpr int W = VecW<T>::W;
@@ -917,11 +920,17 @@ __device__ __forceinline__ void resident_rows(const T* S, T* D, const T* Bt, int
             const Vec<T> s = vload(p - lp);
             const Vec<T> n = vload(p + lp);
             const Vec<T> bb = HAS_B ? vload(Bt + o0) : vzero<T>();
-            T ew = T(0), ee = T(0);
-            if (need_w) ew = p[-1];
-            if (need_e) ee = p[W];
-            const T west = from_lower(ew, m.v[W - 1]);
-            const T east = from_upper(ee, m.v[0]);
+            T west, east;
+            if constexpr (ONE) {
+                west = from_lower_any(m.v[W - 1]);
+                east = from_upper_any(m.v[0]);
+            } else {
+                T ew = T(0), ee = T(0);
+                if (need_w) ew = p[-1];
+                if (need_e) ee = p[W];
+                west = from_lower(ew, m.v[W - 1]);
+                east = from_upper(ee, m.v[0]);
+            }
             Vec<T> o;
 #pragma unroll
             for (int k = 0; k < W; ++k) {

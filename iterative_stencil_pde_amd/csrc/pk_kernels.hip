@@ -351,7 +351,10 @@ __device__ __forceinline__ void resident_sweep_task(const pk_kargs& a, int n, in
             const int hi = min(ny - 1, r1 + (sc - s));
             // colour of this half-sweep: half-sweeps done so far in the task, mod 2
             const int parity = (n - remaining + s - 1) & 1;
-            resident_rows<T, HAS_B, RB>(S, D, Bt, lo - e0, hi - e0, tm, e0, parity);
+            if (tm.segs == 1)
+                resident_rows<T, HAS_B, RB, true>(S, D, Bt, lo - e0, hi - e0, tm, e0, parity);
+            else
+                resident_rows<T, HAS_B, RB, false>(S, D, Bt, lo - e0, hi - e0, tm, e0, parity);
             __syncthreads();
             T* t = S;
             S = D;
