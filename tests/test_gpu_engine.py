@@ -163,3 +163,27 @@ def test_launch_mode_rejects_persistent_only_tasks():
         got = e.readback()
         ref, _ = oracle.jacobi(w.u0, 250)
         assert np.array_equal(got, ref)
+
+
+# What the planner picks on MI355X (256 CUs, 160 KiB of LDS per block) for the
+# five workloads; a change here is a change of the measured plan and should be
+# deliberate.
+AUTO_PLANS = {
+    "laplace64": dict(layout=pk.PK_LAYOUT_RESIDENT, grid_blocks=1),
+    "poisson256": dict(layout=pk.PK_LAYOUT_REGISTER, exchange=pk.PK_EXCHANGE_TAGGED, threads=1024),
+    "laplace1024": dict(layout=pk.PK_LAYOUT_REGISTER, exchange=pk.PK_EXCHANGE_TAGGED, threads=1024),
+    "laplace4096": dict(layout=pk.PK_LAYOUT_STREAM, pass_sweeps=8, threads=512, grid_blocks=256),
+    "poisson8192": dict(layout=pk.PK_LAYOUT_STREAM, pass_sweeps=8, threads=512, grid_blocks=256),
+}
+
+
+@pytest.mark.parametrize("name", sorted(AUTO_PLANS))
+def test_auto_plan(name):
+    w = inputs.make(name)
+    with pk.Engine(w.u0, w.f, h=w.h) as e:
+        info = e.info()
+        e.sweep(2)
+    say(f"  {name}: layout={info.layout} G={info.grid_blocks} threads={info.threads} halo={info.halo_depth} "
+        f"exchange={info.exchange} k={info.pass_sweeps}")
+    for key, want in AUTO_PLANS[name].items():
+        assert getattr(info, key) == want, (key, getattr(info, key), want)
