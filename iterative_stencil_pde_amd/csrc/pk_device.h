@@ -300,7 +300,7 @@ struct BarrierCtx {
     uint32_t xmembers;   // XCD barrier: blocks on this XCD
     uint32_t xgroups;    // XCD barrier: XCDs with at least one block
     uint32_t nbr_epoch;  // neighbour exchanges completed (identical in every block)
-    uint32_t tag_epoch;  // tagged exchanges completed (identical in every block)
+    uint64_t tag_epoch;  // tagged exchanges completed (identical in every block)
     uint32_t nbar;       // grid barriers passed (identical in every block)
     // task carry: leader-only state in the block's shared memory (registers
     // live across every pass cost the streaming kernels spills), except the

@@ -187,7 +187,9 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
         const int above = min(mn, r0 - 1);
         const int below = min(mn, ny - 1 - r1);
         if (remaining > 0 && a.exchange == PK_EXCHANGE_TAGGED) {
-            const uint32_t tag = bc.tag_epoch + 1;
+            // the tag of exchange e: never 0 (the buffers start zeroed) and never
+            // equal to the tag of exchange e - 2, the previous use of the buffer
+            const uint32_t tag = static_cast<uint32_t>(bc.tag_epoch % 0xFFFFFFFFull) + 1u;
             uint64_t* tb = a.tag + static_cast<size_t>(bc.tag_epoch & 1u) * ny * a.tag_pitch;
             const int vi = cg * 64 + lane;   // this lane's vector: word vi of each plane
             const int plane = a.tag_pitch / 4;
@@ -229,7 +231,7 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                     __builtin_amdgcn_s_sleep(1);
                 }
             }
-            bc.tag_epoch = tag;
+            bc.tag_epoch += 1;
             continue;  // the field buffers are untouched until the task's last exchange
         }
         {   // publish into the other field buffer
