@@ -616,8 +616,10 @@ __device__ __forceinline__ double stream_unit_residual(const T* __restrict__ src
         }
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
-            const double q = rho2<T, HAS_B>(up, mid, dn[k], bb[k], mh, col, nx);
-            if (act && r + k < r_end) acc += q;
+            if (r + k < r_end) {  // wave-uniform: short bands skip the rows past their end
+                const double q = rho2<T, HAS_B>(up, mid, dn[k], bb[k], mh, col, nx);
+                if (act) acc += q;
+            }
             up = mid;
             mid = dn[k];
             mh = dh[k];
