@@ -44,9 +44,10 @@ def step_tasks(w):
 
 
 def run_steps(e, w, steps: int, timeout_s: float = 600.0):
-    """Submit `steps` passes of the script, keeping the task ring full."""
+    """Submit `steps` passes of the script, keeping the task ring full. Returns
+    the device time of each step (the sum of its tasks' device times, in us)."""
     pending = collections.deque()
-    last = None
+    results = []
     for _ in range(steps):
         for s in step_tasks(w):
             kind = {"sweep": pk.PK_SWEEP, "sweep_rb": pk.PK_SWEEP_RB}.get(s[0], pk.PK_RESIDUAL)
@@ -54,15 +55,16 @@ def run_steps(e, w, steps: int, timeout_s: float = 600.0):
             while True:
                 rc, t = pk.pk_submit_status(e.h, kind, n)
                 if rc == pk.PK_EBUSY:
-                    last = e.wait(pending.popleft(), timeout_s)
+                    results.append(e.wait(pending.popleft(), timeout_s))
                     continue
                 if rc != pk.PK_OK:
                     raise pk.PkError(rc, "pk_submit")
                 pending.append(t)
                 break
     while pending:
-        last = e.wait(pending.popleft(), timeout_s)
-    return last
+        results.append(e.wait(pending.popleft(), timeout_s))
+    per = len(step_tasks(w))
+    return [sum(r.device_us for r in results[i * per:(i + 1) * per]) for i in range(steps)]
 
 
 def algorithmic_bytes(w):
@@ -81,11 +83,12 @@ def measure(w, steps, warmup, **opts):
         info0 = e.info()
         run_steps(e, w, warmup)
         t0 = time.perf_counter()
-        run_steps(e, w, steps)
+        step_us = run_steps(e, w, steps)
         t1 = time.perf_counter()
         if opts.get("mode", pk.PK_PERSISTENT) == pk.PK_PERSISTENT:
             e.wait(e.submit(pk.PK_EXIT))
         info1 = e.info()
+    measure.step_us = step_us  # device time per timed step (persistent mode)
     return t1 - t0, info0, info1
 
 
@@ -329,6 +332,7 @@ def main():
 
     # persistent engine
     dt, info, info_end = measure(w, args.steps, args.warmup, mode=pk.PK_PERSISTENT, **opts)
+    step_us = sorted(measure.step_us)
     value = cells_per_step * args.steps / dt / 1e9
     us_iter = dt / (w.sweeps * args.steps) * 1e6
     kernel_s = info_end.kernel_ms / 1e3
@@ -366,6 +370,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dt / args.steps * 1e3, 4),
+        # each timed step's time on the device clock (its tasks' device times summed)
+        "ms_per_step_device": {"min": round(step_us[0] / 1e3, 4),
+                               "median": round(step_us[len(step_us) // 2] / 1e3, 4)},
         "us_per_iteration": round(us_iter, 4),
         "us_per_iteration_sweep_task": round(us_sweep_only, 4) if us_sweep_only else round(us_iter, 4),
         "higher_is_better": True,
