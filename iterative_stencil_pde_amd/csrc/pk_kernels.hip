@@ -95,17 +95,34 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
             if (HAS_B) bb[r] = ok ? gload(gb + static_cast<size_t>(row) * p + col) : vzero<T>();
         }
     }
+    // this wave's LDS slot in the parity-0 half; the parity-1 half follows
+    T* const slot0 = lds + static_cast<size_t>(wave) * S::size;
+    const size_t half = static_cast<size_t>(nwv) * S::size;
     int par = 0;
     int remaining = n;
     while (remaining > 0) {
         const int sc = period_len(remaining, m);
+        // The rows of sub-sweep s (as in the LDS tile) are [max(1, r0 - (sc - s)),
+        // min(ny - 1, r1 + (sc - s))): a row at distance d above the band takes
+        // part up to sub-sweep sc - d, the row d below its last row up to
+        // sc - 1 - d, the band's rows in all, ring rows in none. Wave-uniform.
+        int last_s[RT];
+        int last_any = 0;
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const int row = row_base + r;
+            int l;
+            if (!wave_live || row < 1 || row >= ny - 1) l = 0;
+            else if (row < r0) l = sc - (r0 - row);
+            else if (row < r1) l = sc;
+            else l = sc - 1 - (row - r1);
+            last_s[r] = __builtin_amdgcn_readfirstlane(l);
+            last_any = max(last_any, last_s[r]);
+        }
         for (int s = 1; s <= sc; ++s) {
-            // rows of this sub-sweep (as in the LDS tile) and, red-black, the colour
-            const int lo = max(1, r0 - (sc - s));
-            const int hi = min(ny - 1, r1 + (sc - s));
+            // red-black: the colour of this sub-sweep
             const int parity = (n - remaining + s - 1) & 1;
-            T* base = lds + static_cast<size_t>(par * nwv) * S::size;
-            T* mine = base + static_cast<size_t>(wave) * S::size;
+            T* mine = par ? slot0 + half : slot0;
             if (wave_live) {
                 vstore(mine + S::top + lane * W, u[0]);
                 vstore(mine + S::bottom + lane * W, u[RT - 1]);
@@ -117,13 +134,20 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                 }
             }
             __syncthreads();
-            // wave-uniform: which of this wave's rows take part (a bit per row)
-            const int first = max(0, lo - row_base), last = min(RT, hi - row_base);
-            const uint32_t act = (wave_live && first < last) ? ((1u << last) - (1u << first)) : 0u;
-            if (act) {
-                const Vec<T> above = rg > 0 ? vload(base + static_cast<size_t>(wave - cw) * S::size + S::bottom + lane * W)
+            // wave-uniform: which of this wave's rows take part; with 4 rows a wave,
+            // a bit mask from this sub-sweep's row range measured faster
+            uint32_t act = 0;
+            if constexpr (RT != 2) {
+                const int lo = max(1, r0 - (sc - s));
+                const int hi = min(ny - 1, r1 + (sc - s));
+                const int first = max(0, lo - row_base), last = min(RT, hi - row_base);
+                act = (wave_live && first < last) ? ((1u << last) - (1u << first)) : 0u;
+            }
+            const auto row_on = [&](int r) { return RT == 2 ? s <= last_s[r] : (act & (1u << r)) != 0u; };
+            if (RT == 2 ? s <= last_any : act != 0u) {
+                const Vec<T> above = rg > 0 ? vload(mine - static_cast<size_t>(cw) * S::size + S::bottom + lane * W)
                                             : vzero<T>();
-                const Vec<T> below = rg + 1 < rw ? vload(base + static_cast<size_t>(wave + cw) * S::size + S::top + lane * W)
+                const Vec<T> below = rg + 1 < rw ? vload(mine + static_cast<size_t>(cw) * S::size + S::top + lane * W)
                                                  : vzero<T>();
                 // outside neighbours of lanes 0 and 63 for every row
                 T edge[RT];
@@ -131,11 +155,11 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                 for (int r = 0; r < RT; ++r) edge[r] = T(0);
                 if (ONE) {
                 } else if (lane == 0 && has_left) {
-                    const T* src = base + static_cast<size_t>(wave - 1) * S::size + S::last_col;
+                    const T* src = mine - S::size + S::last_col;
 #pragma unroll
                     for (int r = 0; r < RT; ++r) edge[r] = src[r];
                 } else if (lane == 63 && has_right) {
-                    const T* src = base + static_cast<size_t>(wave + 1) * S::size + S::first_col;
+                    const T* src = mine + S::size + S::first_col;
 #pragma unroll
                     for (int r = 0; r < RT; ++r) edge[r] = src[r];
                 }
@@ -144,7 +168,7 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                 for (int r = 0; r < RT; ++r) {
                     const Vec<T> old = u[r];
                     const int row = row_base + r;
-                    if (act & (1u << r)) {  // wave-uniform
+                    if (row_on(r)) {  // wave-uniform
                         const Vec<T> nxt = (r + 1 < RT) ? u[r + 1 < RT ? r + 1 : r] : below;
                         T west, east;
                         if constexpr (ONE) {
