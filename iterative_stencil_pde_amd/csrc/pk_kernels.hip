@@ -145,10 +145,12 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
             }
             const auto row_on = [&](int r) { return RT == 2 ? s <= last_s[r] : (act & (1u << r)) != 0u; };
             if (RT == 2 ? s <= last_any : act != 0u) {
-                const Vec<T> above = rg > 0 ? vload(mine - static_cast<size_t>(cw) * S::size + S::bottom + lane * W)
-                                            : vzero<T>();
-                const Vec<T> below = rg + 1 < rw ? vload(mine + static_cast<size_t>(cw) * S::size + S::top + lane * W)
-                                                 : vzero<T>();
+                // The first row of row group 0 and the last of row group rw - 1 never
+                // take part (the tile spans band + 2m rows and a sub-sweep at most
+                // band + 2(m - 1), or they are ring rows), so those groups read their
+                // own slot instead of a missing neighbour's: no branch, never used.
+                const Vec<T> above = vload(mine - (rg > 0 ? static_cast<size_t>(cw) * S::size : 0) + S::bottom + lane * W);
+                const Vec<T> below = vload(mine + (rg + 1 < rw ? static_cast<size_t>(cw) * S::size : 0) + S::top + lane * W);
                 // outside neighbours of lanes 0 and 63 for every row
                 T edge[RT];
 #pragma unroll
