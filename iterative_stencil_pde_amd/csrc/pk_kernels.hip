@@ -119,10 +119,10 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
             last_s[r] = __builtin_amdgcn_readfirstlane(l);
             last_any = max(last_any, last_s[r]);
         }
-        for (int s = 1; s <= sc; ++s) {
+        // sub-sweep s with this wave's LDS slot of its parity
+        const auto sub_sweep = [&](int s, T* mine) {
             // red-black: the colour of this sub-sweep
             const int parity = (n - remaining + s - 1) & 1;
-            T* mine = par ? slot0 + half : slot0;
             if (wave_live) {
                 vstore(mine + S::top + lane * W, u[0]);
                 vstore(mine + S::bottom + lane * W, u[RT - 1]);
@@ -195,8 +195,15 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                     prev = old;
                 }
             }
-            par ^= 1;
+        };
+        // two sub-sweeps an iteration: no slot select or register rotation between them
+        T* const mine0 = par ? slot0 + half : slot0;
+        T* const mine1 = par ? slot0 : slot0 + half;
+        for (int s = 1; s <= sc; s += 2) {
+            sub_sweep(s, mine0);
+            if (s < sc) sub_sweep(s + 1, mine1);
         }
+        par ^= sc & 1;
         remaining -= sc;
         const int mn = period_len(remaining, m);  // the next period, 0 at the end
         // rows to publish: edge rows for the neighbours, or every owned row at the end
