@@ -275,6 +275,50 @@ def test_resident_halo_deeper_than_band(exchange, blocks, halo, tile):
     check_against_oracle(w, got, ref, f"deep-halo/{tile}/{blocks}/{halo}/{exchange}")
 
 
+# The register tile holds band + 2 x halo rows in (threads / 64) / strips row
+# groups of 2 or 4 rows; each case sits at, or one past, the largest depth with
+# 2 rows a wave, or at the largest that fits at all (the last asks for more and
+# gets the deepest that fits). The first and last bands reach the ring.
+REG_CAPACITY = {
+    # id: (ny, nx, dtype, threads, blocks, halo asked, halo given)
+    "256f32-G16-m8-2rows-full": (256, 256, np.float32, 1024, 16, 8, 8),
+    "256f32-G16-m9-4rows": (256, 256, np.float32, 1024, 16, 9, 9),
+    "256f32-G16-m24-4rows-full": (256, 256, np.float32, 1024, 16, 24, 24),
+    "256f32-G16-m30-clamped": (256, 256, np.float32, 1024, 16, 30, 24),
+    "256f32-G64-m14-2rows-full": (256, 256, np.float32, 1024, 64, 14, 14),
+    "256f32-G64-m15-4rows": (256, 256, np.float32, 1024, 64, 15, 15),
+    "256f32-G64-m30-4rows-full": (256, 256, np.float32, 1024, 64, 30, 30),
+    "256f32-t512-G64-m6-2rows-full": (256, 256, np.float32, 512, 64, 6, 6),
+    "256f32-t512-G64-m7-4rows": (256, 256, np.float32, 512, 64, 7, 7),
+    "130x257f32-G16-m4-2strips-2rows-full": (130, 257, np.float32, 1024, 16, 4, 4),
+    "130x257f32-G16-m12-2strips-4rows-full": (130, 257, np.float32, 1024, 16, 12, 12),
+    "256f64-G32-m4-2strips-2rows-full": (256, 256, np.float64, 1024, 32, 4, 4),
+    "256f64-G32-m12-2strips-4rows-full": (256, 256, np.float64, 1024, 32, 12, 12),
+}
+
+
+@pytest.mark.parametrize("exchange", [pk.PK_EXCHANGE_BARRIER, pk.PK_EXCHANGE_TAGGED], ids=["barrier", "tagged"])
+@pytest.mark.parametrize("case", sorted(REG_CAPACITY))
+def test_register_tile_capacity(case, exchange):
+    """Halo depths at the register tile's capacity limits: the edge rows of the
+    first and last row groups never take part in a sub-sweep (their neighbour
+    reads fall on their own slots), and the field stays bitwise equal to the
+    oracle's through tasks that end part-way through a period."""
+    ny, nx, dtype, threads, blocks, halo, given = REG_CAPACITY[case]
+    u, f = _random_case(ny, nx, dtype, True, seed=7 * ny + nx + halo)
+    w = inputs.Workload(f"cap{ny}x{nx}", nx, ny, dtype, 0.01, u, f,
+                        [("residual",), ("sweep", 5), ("sweep", 37), ("residual",), ("sweep", 19),
+                         ("residual",), ("readback",)], "")
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_REGISTER, threads=threads,
+                            max_blocks=blocks, halo_depth=halo, exchange=exchange)
+    info = got["info"]
+    say(f"  grid={info.grid_blocks} threads={info.threads} band={info.band_rows} halo={info.halo_depth}")
+    assert info.layout == pk.PK_LAYOUT_REGISTER and info.grid_blocks == blocks and info.halo_depth == given
+    check_against_oracle(w, got, ref, f"capacity/{case}/{exchange}")
+    assert np.array_equal(got["final"], ref["final"]), case
+
+
 @pytest.mark.parametrize("shape,dtype,poisson,threads,blocks,halo", [
     ((20, 4100), np.float32, False, 1024, 9, 1),  # 1025 vectors a row: more segments than waves
     ((40, 1030), np.float32, True, 256, 12, 1),   # 258 vectors, 4 waves: segments taken in turn
