@@ -51,7 +51,9 @@ void stream_geometry(Plan& p, int nx, int ny, int esize, int min_rows) {
     const int interior = ny - 2;
     const int nw = p.grid * (p.threads / 64);
     int bands = std::max(1, nw / p.strips);
-    bands = std::min(bands, std::max(1, interior / std::max(1, min_rows)));
+    // bands of at most min_rows rows where the waves allow (254 rows make 64 bands
+    // of 4 rather than 51 of 5: the residual's march loads 4 rows a round)
+    bands = std::min(bands, std::max(1, ceil_div(interior, std::max(1, min_rows))));
     p.band_rows = ceil_div(interior, bands);
     p.bands = ceil_div(interior, p.band_rows);
 }
