@@ -13,10 +13,27 @@ using namespace pkd;
 
 namespace {
 
-// Sweeps of the next period of a tile task with `remaining` sweeps left and
-// halo depth m: the remaining sweeps split into the fewest periods of at most m
-// sweeps, as evenly as possible (the same number of exchanges as periods of m,
-// and narrower trapezoids). Every block computes the same sequence.
+// The periods of a tile task of n sweeps with halo depth m: the fewest periods
+// of at most m sweeps (P = ceil(n / m)), as even as possible: the first n mod P
+// have n / P + 1 sweeps, the rest n / P (the same number of exchanges as
+// periods of m, and narrower trapezoids). Every block computes the same
+// sequence; its two divisions happen once a task, not once a period (an integer
+// division is a few dozen instructions, on the scalar unit that the CU's waves
+// share).
+struct Periods {
+    int count, q, r;
+    __device__ __forceinline__ Periods(int n, int m) {
+        count = n > 0 ? (n - 1) / m + 1 : 0;
+        q = count > 0 ? n / count : 0;
+        r = count > 0 ? n - q * count : 0;
+    }
+    // sweeps of period k (0-based), 0 past the last
+    __device__ __forceinline__ int len(int k) const { return k < count ? q + (k < r ? 1 : 0) : 0; }
+};
+
+// The same sequence from the sweeps still to come: the LDS tile's form (its
+// single-block plan measured ~4% slower with the schedule above, although it
+// computes one period a task either way).
 __device__ __forceinline__ int period_len(int remaining, int m) {
     if (remaining <= 0) return 0;
     const int periods = (remaining - 1) / m + 1;
@@ -100,8 +117,10 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
     const size_t half = static_cast<size_t>(nwv) * S::size;
     int par = 0;
     int remaining = n;
+    const Periods periods(n, m);
+    int period = 0;  // the period under way
     while (remaining > 0) {
-        const int sc = period_len(remaining, m);
+        const int sc = periods.len(period);
         // The rows of sub-sweep s (as in the LDS tile) are [max(1, r0 - (sc - s)),
         // min(ny - 1, r1 + (sc - s))): a row at distance d above the band takes
         // part up to sub-sweep sc - d, the row d below its last row up to
@@ -205,7 +224,7 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
         }
         par ^= sc & 1;
         remaining -= sc;
-        const int mn = period_len(remaining, m);  // the next period, 0 at the end
+        const int mn = periods.len(++period);  // the next period, 0 at the end
         // rows to publish: edge rows for the neighbours, or every owned row at the end
         int top_end, bot_begin;
         if (remaining == 0) {
