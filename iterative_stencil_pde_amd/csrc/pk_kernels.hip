@@ -271,8 +271,15 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                                           tag) && ok;
                     }
                     if (__ballot(!ok) == 0) break;
-                    const bool late = wall_clock64() - t0 > a.tag_ticks ||
-                                      __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+                    // a fault elsewhere is read only once the poll has waited far
+                    // longer than an exchange takes (1/65536 of the limit, ~30 us at
+                    // 2 s): read after every miss, it put a second memory round trip
+                    // in front of the next poll
+                    const uint64_t waited = wall_clock64() - t0;
+                    const bool late =
+                        waited > a.tag_ticks ||
+                        (waited > (a.tag_ticks >> 16) &&
+                         __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u);
                     if (late) {  // a fault elsewhere, or a tag that never comes: give up
                         bc.faulted = true;
                         if (lane == 0)
