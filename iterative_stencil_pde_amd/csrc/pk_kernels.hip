@@ -673,17 +673,27 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
         // Fast path: the previous task's last ordered barrier carried this task
         // in (the leader had read it ahead); every block reads the same carry
         // word after that barrier, so all take the same path.
+        // One round of loads: the carry's sequence, kind and count (all written
+        // before the barrier that carried it, so read together and kept only if
+        // the sequence matches) and the fault flag; one after another they were
+        // three memory round trips at every task start.
         if (threadIdx.x == 0) {
             s_carried = 0;
-        }
-        if (may_carry && threadIdx.x == 0) {
-            const pk_carry* c = &a.st->carry[next_seq & 1];
-            const uint64_t cs = __hip_atomic_load(&c->seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_carried = cs == next_seq ? 1 : 0;
-            if (s_carried) {
-                s_kind = __hip_atomic_load(&c->kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                s_n = __hip_atomic_load(&c->n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint64_t cs = 0;
+            int32_t ck = PK_EXIT, cn = 0;
+            if (may_carry) {
+                const pk_carry* c = &a.st->carry[next_seq & 1];
+                cs = __hip_atomic_load(&c->seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ck = __hip_atomic_load(&c->kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                cn = __hip_atomic_load(&c->n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            const uint32_t f = __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (may_carry && cs == next_seq) {
+                s_carried = 1;
+                s_kind = ck;
+                s_n = cn;
                 s_seq = next_seq;
+                s_exit = (bc.faulted || f != 0 || ck == PK_EXIT) ? 1 : 0;
             }
         }
         __syncthreads();
@@ -724,13 +734,11 @@ __global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_
                 s_kind = __hip_atomic_load(&a.st->task_kind, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 s_n = __hip_atomic_load(&a.st->task_n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 s_seq = __hip_atomic_load(&a.st->task_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t f = __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                s_exit = (bc.faulted || f != 0 || s_kind == PK_EXIT) ? 1 : 0;
             }
+            __syncthreads();
         }
-        if (threadIdx.x == 0) {
-            const uint32_t f = __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            s_exit = (bc.faulted || f != 0 || s_kind == PK_EXIT) ? 1 : 0;
-        }
-        __syncthreads();
         const int kind = s_kind, n = s_n;
         const uint64_t seq = s_seq;
         const uint64_t t_begin = leader ? wall_clock64() : 0;
