@@ -220,14 +220,13 @@ TilePlan tile_candidate(int nx, int ny, int esize, bool has_b, int nwv, size_t l
         // the waves go round the CU's 4 SIMDs, so the active row segments of a
         // sub-sweep spread over them (in whole waves of r rows); column groups
         // add an edge exchange
-        // 2-row waves: measured again after the sub-sweep loop lost its per-row
-        // scalar work, their cost grows with the rows themselves, not whole waves
-        // (256^2 Poisson, 64 blocks: m = 12 beats 11, 13 and 14 in every scan;
-        // the slope between the bounds those points set, 0.018 .. 0.038)
+        // Measured again after the sub-sweep loop lost its per-row scalar work:
+        // the cost grows with the rows updated, not in whole waves (256^2 Poisson,
+        // 64 blocks: m = 12 beat 11, 13 and 14 in every scan, which bounds the
+        // 2-row slope to 0.018 .. 0.038; 1024^2 at 256 blocks: m = 6 beat 5,
+        // which rounding to whole 4-row waves had ranked the other way)
         sub_us = [cw](double rows, int r) {
-            const double base = 0.362 + (cw > 1 ? 0.109 : 0.0);
-            if (r == 2) return base + 0.025 * rows * cw / 4.0;
-            return base + 0.0334 * std::ceil(rows / r) * r * cw / 4.0;
+            return 0.362 + (cw > 1 ? 0.109 : 0.0) + (r == 2 ? 0.025 : 0.0334) * rows * cw / 4.0;
         };
     } else {
         const size_t row_bytes = static_cast<size_t>(lp) * esize * (has_b ? 3 : 2);
