@@ -218,12 +218,11 @@ TilePlan tile_candidate(int nx, int ny, int esize, bool has_b, int nwv, size_t l
         if (t.lds > lds_max) return TilePlan{};
         reg_rows = [rw](int ext) { return (ext + rw - 1) / rw <= 2 ? 2 : kRegRows; };
         // the waves go round the CU's 4 SIMDs, so the active row segments of a
-        // sub-sweep spread over them (in whole waves of r rows); column groups
-        // add an edge exchange
-        // Measured again after the sub-sweep loop lost its per-row scalar work:
-        // the cost grows with the rows updated, not in whole waves (256^2 Poisson,
-        // 64 blocks: m = 12 beat 11, 13 and 14 in every scan, which bounds the
-        // 2-row slope to 0.018 .. 0.038; 1024^2 at 256 blocks: m = 6 beat 5,
+        // sub-sweep spread over them; column groups add an edge exchange. The
+        // cost grows with the rows updated, not in whole waves (measured after
+        // the sub-sweep loop lost its per-row scalar work: 256^2 Poisson at 64
+        // blocks, m = 12 beat 11, 13 and 14 in every scan, which bounds the
+        // 2-row slope to 0.018 .. 0.038; 1024^2 at 256 blocks, m = 6 beat 5,
         // which rounding to whole 4-row waves had ranked the other way)
         sub_us = [cw](double rows, int r) {
             return 0.362 + (cw > 1 ? 0.109 : 0.0) + (r == 2 ? 0.025 : 0.0334) * rows * cw / 4.0;
