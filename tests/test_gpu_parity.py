@@ -303,12 +303,13 @@ def test_register_tile_capacity(case, exchange):
     """Halo depths at the register tile's capacity limits: the edge rows of the
     first and last row groups never take part in a sub-sweep (their neighbour
     reads fall on their own slots), and the field stays bitwise equal to the
-    oracle's through tasks that end part-way through a period."""
+    oracle's through tasks that end part-way through a period, red-black
+    iterations among them."""
     ny, nx, dtype, threads, blocks, halo, given = REG_CAPACITY[case]
     u, f = _random_case(ny, nx, dtype, True, seed=7 * ny + nx + halo)
     w = inputs.Workload(f"cap{ny}x{nx}", nx, ny, dtype, 0.01, u, f,
-                        [("residual",), ("sweep", 5), ("sweep", 37), ("residual",), ("sweep", 19),
-                         ("residual",), ("readback",)], "")
+                        [("residual",), ("sweep", 5), ("sweep", 37), ("residual",), ("sweep_rb", 7),
+                         ("sweep", 19), ("residual",), ("readback",)], "")
     ref = run_oracle_script(w)
     got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_REGISTER, threads=threads,
                             max_blocks=blocks, halo_depth=halo, exchange=exchange)
