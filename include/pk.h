@@ -233,15 +233,23 @@ typedef struct pk_info {
 
 typedef struct pk_engine pk_engine;
 
-/* Fill *o with the defaults (PK_F32, h = 0, PK_PERSISTENT, PK_LAYOUT_AUTO, ...). */
+/* Fill *o with the defaults (PK_F32, h = 0, PK_PERSISTENT, PK_LAYOUT_AUTO, ...):
+ * every sizing choice left to the engine, which sizes the grid once from the
+ * occupancy query ("@persistent" page, section "What it promises"). o may be
+ * NULL (no-op). */
 void pk_opts_default(pk_opts* o);
 
-/* Create an engine for an nx x ny field (nx, ny >= 3).
+/* Create an engine for an nx x ny field (nx, ny >= 3): the grid of
+ * "Persistent Kernels", "The problem (another PDE solver)", with h the node
+ * spacing, and two device buffers for Jacobi ("Implementation details and
+ * correctness": the update goes into a separate matrix).
  *   bc  - host array: the outer ring is the fixed Dirichlet data, the interior
  *         is the initial guess; copied into both device buffers.
  *   src - host array of f for -Lap(u) = f, or NULL for Laplace; b = (T)(h*h*f)
  *         is computed on the device once.
- * In PK_PERSISTENT mode the cooperative kernel is launched before returning.
+ * In PK_PERSISTENT mode the cooperative kernel is launched before returning, once,
+ * with a grid sized from the occupancy query ("@persistent" page, "What it
+ * promises"; "Grid-Wide Barriers", "The residency requirement").
  * Errors: PK_EINVAL (sizes, opts, NULL bc or out, h <= 0 when required),
  * PK_ENOMEM, PK_ELAUNCH (grid not co-resident / launch refused), PK_EDEVICE.
  * On error *out is left unchanged and nothing stays allocated. */
@@ -249,7 +257,13 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* o,
               pk_engine** out);
 
 /* Queue a task; tasks run in FIFO order. *ticket (may be NULL) receives the
- * task's sequence number (1, 2, ...). Does not block. A task travels to the
+ * task's sequence number (1, 2, ...). Does not block. The host writes the task
+ * into the next slot of a ring in pinned host memory and the device's single
+ * poller takes it ("Persistent Kernels", "Base implementation" for the
+ * host-to-device task flags, "Thread synchronization" for one poller per
+ * grid, and "Reflections and next steps", point 3, for a done word written only
+ * after the work: here every slot carries a sequence number, so no early
+ * acknowledgement is possible). A task travels to the
  * device as one 64-bit word, so n is at most PK_TASK_N_MAX (2^28 - 1): split
  * longer runs into several SWEEP tasks.
  * Errors: PK_EINVAL (unknown kind, n < 0 or > PK_TASK_N_MAX, persistent-only
@@ -273,7 +287,9 @@ int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket);
 int pk_submit_until(pk_engine* e, int max_sweeps, int check_every, double tol, uint64_t* ticket);
 
 /* Busy-poll (no sleep) until ticket has completed, at most timeout_s seconds
- * (<= 0 => 60 s). r (may be NULL) receives that task's result.
+ * (<= 0 => 60 s). r (may be NULL) receives that task's result. The host spins
+ * on the device's completion word without sleeping ("Persistent Kernels",
+ * "Tuning sleep duration": a sleeping host adds tens of microseconds per task).
  * Errors: PK_EINVAL (ticket never issued), PK_ETIMEDOUT (poisons the engine:
  * a persistent kernel cannot be pre-empted, so only pk_destroy remains, which
  * then leaks rather than free memory the kernel may still use), PK_EDEVICE. */
@@ -282,14 +298,21 @@ int pk_wait(pk_engine* e, uint64_t ticket, double timeout_s, pk_result* r);
 /* Copy the current field (ny x nx, ring included, row-major, the engine's
  * element type) into the caller-owned dst of at least ny*nx*elem bytes.
  * While the persistent kernel runs this is an in-kernel copy task into pinned
- * host memory (no DMA is queued behind the resident kernel).
+ * host memory (no DMA is queued behind the resident kernel): the device hands
+ * results to the host through mapped host memory while it keeps running, as
+ * in the CUDA persistent-thread page, sections "Device Communication" and
+ * "Task Dispatch" (the ping-pong buffer the host reads while the kernel
+ * stays resident).
  * Errors: PK_EINVAL (dst NULL, bytes too small), PK_EBUSY (tasks in flight),
  * PK_ESTATE (poisoned), PK_EDEVICE. */
 int pk_readback(pk_engine* e, void* dst, size_t bytes);
 
 /* PK_LAUNCH engines only: advance the field by n sweeps as n kernel launches
  * with the engine's block count, back to back (sync_each = 0) or with a
- * stream synchronize after each launch (sync_each = 1). *elapsed_us (may be
+ * stream synchronize after each launch (sync_each = 1): the standard-launch
+ * baselines of "Persistent Kernels", sections "Sketching out the experiment"
+ * (same block count for both kernels) and "Comparing the kernels" (queued
+ * launches, and a synchronization after every launch). *elapsed_us (may be
  * NULL) receives the host wall time from the first launch until the last
  * sweep finished. Errors: PK_ESTATE (persistent engine: its kernel holds the
  * CUs, extra launches could not run), PK_EBUSY (tasks in flight), PK_EINVAL. */
@@ -306,15 +329,22 @@ int pk_run_launch_per_iter(pk_engine* e, int n, int sync_each, double* elapsed_u
  * reps < 1), PK_ESTATE (persistent engine, or poisoned), PK_EDEVICE. */
 int pk_run_graph_per_iter(pk_engine* e, int n, int reps, double* elapsed_us);
 
-/* Engine geometry and counters. */
+/* Engine geometry and counters: the grid the occupancy query allowed ("@persistent"
+ * page, "What it promises"), the layout chosen, and the kernel time measured on the
+ * device ("Persistent Kernels", "Sketching out the experiment").
+ * Errors: PK_EINVAL (NULL e or info). */
 int pk_get_info(pk_engine* e, pk_info* info);
 
 /* Stop the kernel (EXIT, bounded wait) and free everything. NULL is a no-op.
- * If the kernel does not leave, device memory is deliberately leaked and
- * PK_ETIMEDOUT returned. */
+ * The kernel leaves only when it reads the EXIT task, so destroy first asks
+ * for it through the ring ("Persistent Kernels", "Base implementation": the
+ * host's stop task ends the persistent loop). If the kernel does not leave,
+ * device memory is deliberately leaked and PK_ETIMEDOUT returned. */
 int pk_destroy(pk_engine* e);
 
-/* Static string for a status code. */
+/* Static string for a status code (never NULL). Errors travel as status codes,
+ * never as an abort of the process (the CUDA persistent-thread page, "Code
+ * Implementation", aborts on any runtime error; a library cannot). */
 const char* pk_strerror(int status);
 
 #ifdef __cplusplus

@@ -35,6 +35,28 @@ def test_header_declares_the_boundary():
     assert sorted(pk.EXPORTED) == names
 
 
+PAGES = ("Persistent Kernels", "Grid-Wide Barriers", "persistent-thread page", "@persistent")
+
+
+def comments_before_declarations():
+    """Map each declared function to the comment block right above its declaration."""
+    text = open(HEADER).read()
+    out = {}
+    for m in re.finditer(r"/\*((?:(?!\*/).)*)\*/\s*(?:(?:const\s+)?[a-z_]+\**\s+)+\**(pk_[a-z_]+)\s*\(",
+                         text, flags=re.S):
+        out[m.group(2)] = m.group(1)
+    return out
+
+
+def test_every_declared_call_cites_a_page():
+    """Each entry point's comment names the page (and section) that defines the
+    operation it performs."""
+    blocks = comments_before_declarations()
+    for name in declared_functions():
+        assert name in blocks, f"{name}: no comment block above its declaration"
+        assert any(p in blocks[name] for p in PAGES), f"{name}: its comment cites no page"
+
+
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.check_output(["nm", "-D", "--defined-only", pk.LIB_PATH], text=True)
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}

@@ -73,8 +73,9 @@ def test_broken_barrier_negative_control():
         results[label] = (ok, stamp)
     for label in ("correct flat", "correct two-level", "correct xcd"):
         assert results[label] == (True, 0), label
-    assert (not results["broken"][0]) or results["broken"][1] > 0, \
-        "the fence-less barrier produced no visible race on this run"
+    # the field gate itself must catch the fence-less barrier; the stamp count is
+    # logged above as further evidence
+    assert not results["broken"][0], "the fence-less barrier left the field within the parity gate"
 
 
 def test_protocol_errors_and_ring():
