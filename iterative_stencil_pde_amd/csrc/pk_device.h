@@ -61,6 +61,34 @@ __device__ __forceinline__ Vec<T> gload(const T* p) {
     return r;
 }
 
+// Wait for this wave's outstanding vector memory operations (vmcnt(0)).
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Buffer access: a resource descriptor (base, size in bytes) in scalar
+// registers, a per-lane byte offset and a wave-uniform byte offset. The lane
+// offset stays in one register for a whole march and the row offset is scalar,
+// so a row load needs no 64-bit address arithmetic and no address register
+// that a later instruction could overwrite while the load is in flight.
+// Descriptor word 3 is the data-format word of the gfx9 family (32-bit format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+template <typename T>
+__device__ __forceinline__ Vec<T> bload(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t row_off) {
+    Vec<T> x;
+    x.v = __builtin_bit_cast(NativeVec<T>, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, row_off, 0));
+    return x;
+}
+
+template <typename T>
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t lane_off, uint32_t row_off,
+                                       const Vec<T>& x) {
+    using U = unsigned int __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(U, x.v), r, lane_off, row_off, 0);
+}
+
 template <typename T>
 __device__ __forceinline__ void gstore(T* p, const Vec<T>& x) {
     *((__attribute__((address_space(1))) NativeVec<T>*)(p)) = x.v;
@@ -364,8 +392,6 @@ __device__ __forceinline__ uint32_t arrive(uint32_t* ctr, bool relaxed) {
                    : __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait for this wave's outstanding vector memory operations (vmcnt(0)).
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // XCD-grouped barrier (PK_BARRIER_XCD). A wave's stores are in its XCD's L2
 // once its vmcnt reaches 0 (the vector L1 is write-through), and an agent-scope
@@ -654,92 +680,209 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
 // K sweeps per pass (temporal blocking in the column march). Level 0 is the
 // field in src; level j row i is the stencil of level j-1 rows i-1, i, i+1.
 // At step t the wave loads level-0 row t and computes level j row t-j for
-// j = 1..K (t+j when marching up), each level keeping its last three rows in
-// registers, and stores level K's row when it lies in the unit's band [r0, r1). The band therefore
-// reads K halo rows above and below, and the field is read and written once
-// per K sweeps. Ring rows keep their value at every level (the middle row of
-// the previous level), ring and padding columns likewise (the stencil's mask).
+// j = 1..K (t+j when marching up); each level keeps its last two rows in
+// registers (the third operand is the row the level below produced at this
+// step), and level K's row is stored when it lies in the unit's band [r0, r1).
+// The band therefore reads K halo rows above and below, and the field is read
+// and written once per K sweeps. Ring rows keep their value at every level (the
+// middle row of the previous level), ring and padding columns likewise (the
+// stencil's mask).
+//
+// Only the rows a stored row depends on are computed: level j needs rows
+// [r0 - (K - j), r1 + (K - j)), which it reaches at step 2j, so during the
+// first 2K steps the levels above step / 2 are skipped (their rows would fall
+// outside that range).
 //
 // Columns: the strip's lanes 0..ov-1 and 64-ov..63 overlap the neighbouring
-// strips and are never stored. Their outer neighbour is not loaded (zero), so
+// strips and are never stored. Their outer neighbours may hold anything, so
 // wrong values spread inward one column per level; after K <= ov * W levels
 // they have not reached a stored lane. A strip stores (64 - 2 ov) * W columns
 // starting at c0 + ov * W. Results equal K single sweeps bit for bit: every
 // stored value is the same expression on the same operands.
+//
+// Ring handling (MODE):
+//   PASS_CHECKED: every level checks whether its row is a ring row (kept) and
+//     every element whether it is a ring or padding column (kept).
+//   PASS_COLS, PASS_INNER: for units whose rows meet a ring row only during
+//     the first 2K steps of the march (the first band marches down from the top
+//     ring, the last band up from the bottom ring, and no band ends within K rows
+//     of the far ring). The ring-row check runs only in those steps, as a
+//     branch-free blend; PASS_INNER also leaves out the column check, for units
+//     whose columns [c0, c0 + 64 W) are all interior.
+//
+// Memory: rows go in chunks of CH, loaded one chunk ahead of their use. With
+// DEFER, a chunk's level-K rows are stored at the start of the next chunk
+// (before its loads): faster where stores are a large share of the traffic
+// (fp64, or with b); otherwise each row is stored as soon as it is computed.
 // ---------------------------------------------------------------------------
-template <typename T, bool HAS_B, int K, int DIR, bool RB>
+enum { PASS_CHECKED = 0, PASS_COLS = 1, PASS_INNER = 2 };
+
+template <typename T, bool HAS_B, bool COLS>
+__device__ __forceinline__ Vec<T> pass_stencil(const Vec<T>& s, const Vec<T>& m, const Vec<T>& n,
+                                               const Vec<T>& b, int col, int nx) {
+    constexpr int W = VecW<T>::W;
+    // lanes 0 and 63 are overlap lanes (never stored): their outer neighbours
+    // may be anything, so the shifts need no edge value
+    const T west = from_lower_any(m.v[W - 1]), east = from_upper_any(m.v[0]);
+    if constexpr (COLS) return stencil_we<T, HAS_B>(s, m, n, b, west, east, col, nx);
+    Vec<T> o;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const T w = (k == 0) ? west : m.v[k - 1];
+        const T e = (k == W - 1) ? east : m.v[k + 1];
+        T t = (w + e) + (s.v[k] + n.v[k]);
+        if (HAS_B) t = t + b.v[k];
+        o.v[k] = T(0.25) * t;
+    }
+    return o;
+}
+
+// keep_val where mask is all ones, else new_val, element by element
+template <typename T>
+__device__ __forceinline__ Vec<T> vblend(uint32_t mask, const Vec<T>& keep_val, const Vec<T>& new_val) {
+    Vec<T> r;
+#pragma unroll
+    for (int k = 0; k < VecW<T>::W; ++k) r.v[k] = blend(mask, keep_val.v[k], new_val.v[k]);
+    return r;
+}
+
+template <bool V>
+struct HeadSteps {
+    static constexpr bool value = V;
+};
+
+template <typename T, bool HAS_B, int K, int DIR, bool RB, int MODE>
 __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* __restrict__ dst,
                                                  const T* __restrict__ bsrc, int nx, int ny,
                                                  int pitch, int c0, int ov, int r0, int r1, int h0) {
     constexpr int dir = DIR;
     constexpr int W = VecW<T>::W;
-    // rows of loads issued ahead; fewer for deep passes (registers hold K windows)
-    constexpr int CH = (HAS_B || K >= 3) ? 2 : 4;
+    constexpr int CH = (HAS_B || K >= 3) ? 2 : 4;  // rows per chunk
+    constexpr bool DEFER = HAS_B || sizeof(T) == 8;
+    constexpr bool COLS = MODE != PASS_INNER;
+    static_assert((2 * K) % CH == 0, "the first 2K steps are whole chunks");
     const int lane = threadIdx.x & 63;
     const int col = c0 + lane * W;
     const bool act = col >= 0 && col < nx;
     const bool store_lane = act && lane >= ov && lane < 64 - ov;
+    // Loads are unconditional, at addresses clamped into the unit's rows and the
+    // row's vectors: rows outside the field read a ring row, lanes outside it a
+    // vector of the same row. Neither value reaches a stored element: ring rows
+    // keep their value at every level, rows beyond them feed only ring rows, and
+    // a lane outside the field borders a ring column, which keeps its value.
+    // The buffer descriptors cover rows [w0, w1), every row the unit reads or
+    // writes (the planner keeps them within 4 GiB).
+    const int w0 = max(0, r0 - K), w1 = min(ny, r1 + K);
     const size_t p = static_cast<size_t>(pitch);
+    const uint32_t row_bytes = static_cast<uint32_t>(p * sizeof(T));
+    const uint32_t win_bytes = static_cast<uint32_t>(w1 - w0) * row_bytes;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + static_cast<size_t>(w0) * p, win_bytes);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + static_cast<size_t>(w0) * p, win_bytes);
+    const __amdgpu_buffer_rsrc_t rbs = make_rsrc(HAS_B ? bsrc + static_cast<size_t>(w0) * p : src, win_bytes);
+    const uint32_t lbyte = static_cast<uint32_t>(min(max(col, 0), pitch - W)) * sizeof(T);
+    const uint32_t sbyte = static_cast<uint32_t>(max(col, 0)) * sizeof(T);  // stored lanes have col >= 0
+    const int b_lo = max(w0, 1), b_hi = min(w1, ny - 1) - 1;  // b rows: interior rows of the window
 
-    Vec<T> win[K][3];  // win[j] = level j rows (x-2, x-1, x), x the last row pushed
-    Vec<T> bq[K];      // bq[j] = b row of the level j+1 row computed at step t
+    Vec<T> ra[K], rm[K];  // level j rows x-1 and x, x the last row it received
+    Vec<T> bq[K];         // bq[j] = b row of the level j+1 row computed at this step
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-        win[j][0] = win[j][1] = win[j][2] = vzero<T>();
+        ra[j] = rm[j] = vzero<T>();
         bq[j] = vzero<T>();
     }
-    // dir = +1 marches down from r0 - K, dir = -1 marches up from r1 - 1 + K;
-    // neighbouring bands march in opposite directions, so the halo rows they
-    // share are read at about the same time (and hit in the XCD's L2)
+    // dir = +1 marches down from r0 - K, dir = -1 marches up from r1 - 1 + K
     const int nsteps = (r1 - r0) + 2 * K;
     const int t_first = dir > 0 ? r0 - K : r1 - 1 + K;
-    for (int q0 = 0; q0 < nsteps; q0 += CH) {
-        Vec<T> ld[CH];
-        Vec<T> lb[CH];
+    const auto load_chunk = [&](int q, Vec<T>* u, Vec<T>* b) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int t = t_first + dir * (q0 + c);
-            const bool live = q0 + c < nsteps;
-            ld[c] = (act && live && t >= 0 && t < ny) ? gload(src + static_cast<size_t>(t) * p + col)
-                                                      : vzero<T>();
-            if (HAS_B) {
-                const int rb = t - dir;
-                lb[c] = (act && live && rb >= 1 && rb <= ny - 2)
-                            ? gload(bsrc + static_cast<size_t>(rb) * p + col) : vzero<T>();
-            } else {
-                lb[c] = vzero<T>();
-            }
+            const int t = t_first + dir * (q + c);
+            u[c] = bload<T>(rs, lbyte, static_cast<uint32_t>(min(max(t, w0), w1 - 1) - w0) * row_bytes);
+            if (HAS_B)
+                b[c] = bload<T>(rbs, lbyte, static_cast<uint32_t>(min(max(t - dir, b_lo), b_hi) - w0) * row_bytes);
+            else
+                b[c] = vzero<T>();
         }
+    };
+    // level K row of step q, stored if it lies in the band
+    const auto store_row = [&](int q, const Vec<T>& x) {
+        const int row = t_first + dir * q - dir * K;
+        if (row >= r0 && row < r1) {  // wave-uniform
+            const uint32_t roff = static_cast<uint32_t>(row - w0) * row_bytes;
+            if (store_lane) bstore<T>(rd, sbyte, roff, x);
+        }
+    };
+    Vec<T> out[CH];  // DEFER: a chunk's level-K rows, stored at the start of the next chunk
+    // One step: level-0 row u (and its b row). In the first 2K steps (head) only
+    // levels j <= q / 2 are computed: a higher level's row at this step lies
+    // outside the rows any stored row depends on.
+    const auto step = [&](int q, const Vec<T>& u, const Vec<T>& b, auto head_c) -> Vec<T> {
+        constexpr bool head = decltype(head_c)::value;
+        const int t = t_first + dir * q;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            if (q0 + c >= nsteps) break;  // wave-uniform
-            const int t = t_first + dir * (q0 + c);
-            // level 0 receives row t
-            win[0][0] = win[0][1];
-            win[0][1] = win[0][2];
-            win[0][2] = ld[c];
+        for (int j = K - 1; j > 0; --j) bq[j] = bq[j - 1];
+        bq[0] = b;
+        Vec<T> inc = u;  // row t of level 0, then level j's new row
 #pragma unroll
-            for (int j = K - 1; j > 0; --j) bq[j] = bq[j - 1];
-            bq[0] = lb[c];
-#pragma unroll
-            for (int j = 1; j <= K; ++j) {
+        for (int j = 1; j <= K; ++j) {
+            const Vec<T> mid = rm[j - 1];
+            if (!head || 2 * j <= q) {  // wave-uniform
                 const int row = t - dir * j;  // level j row computed at this step
-                // lanes 0 and 63 are overlap lanes (never stored): their outer
-                // neighbours may be anything, so the shifts need no edge value
-                const Vec<T>& mid = win[j - 1][1];
-                Vec<T> o = stencil_we<T, HAS_B>(win[j - 1][0], mid, win[j - 1][2], bq[j - 1],
-                                                from_lower_any(mid.v[W - 1]), from_upper_any(mid.v[0]), col, nx);
-                if (RB) o = rb_keep(o, win[j - 1][1], row, (h0 + j - 1) & 1);
-                if (row <= 0 || row >= ny - 1) o = win[j - 1][1];  // ring rows (and beyond)
-                if (j < K) {
-                    win[j][0] = win[j][1];
-                    win[j][1] = win[j][2];
-                    win[j][2] = o;
-                } else if (store_lane && row >= r0 && row < r1) {
-                    gstore(dst + static_cast<size_t>(row) * p + col, o);
+                // level j-1 rows row-1, row, row+1 (dir = -1: row+1, row, row-1)
+                Vec<T> o = pass_stencil<T, HAS_B, COLS>(ra[j - 1], mid, inc, bq[j - 1], col, nx);
+                if (RB) o = rb_keep(o, mid, row, (h0 + j - 1) & 1);
+                const bool ring = row <= 0 || row >= ny - 1;  // ring rows (and beyond) keep their value
+                if (MODE == PASS_CHECKED) {
+                    if (ring) o = mid;
+                } else if (head) {
+                    o = vblend(lane_mask(ring), mid, o);
                 }
+                ra[j - 1] = mid;
+                rm[j - 1] = inc;
+                inc = o;
+            } else {  // a row outside every stored row's reach: shift only
+                ra[j - 1] = mid;
+                rm[j - 1] = inc;
             }
         }
+        return inc;
+    };
+    const auto run = [&](int q_begin, int q_end, auto head_c) {
+        Vec<T> ld[CH], lb[CH];  // the chunk being computed
+        load_chunk(q_begin, ld, lb);
+        // nothing may be in flight when a loop is entered: the compiler's wait
+        // analysis merges the loop's entry with its back edge, and loads pending
+        // at entry would make it wait for every prefetch right after issuing it
+        wait_vm();
+        for (int q0 = q_begin; q0 < q_end; q0 += CH) {
+            if (DEFER && q0 > 0) {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) store_row(q0 - CH + c, out[c]);
+            }
+            Vec<T> nld[CH], nlb[CH];
+            // always issued (past the end it reads clamped rows that nothing uses)
+            load_chunk(q0 + CH, nld, nlb);
+            // whole chunks: a step past the last computes rows beyond the band's
+            // halo, which are never stored
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const Vec<T> x = step(q0 + c, ld[c], lb[c], head_c);
+                if (DEFER) out[c] = x;
+                else store_row(q0 + c, x);
+            }
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                ld[c] = nld[c];
+                lb[c] = nlb[c];
+            }
+        }
+    };
+    run(0, 2 * K, HeadSteps<true>{});
+    run(2 * K, nsteps, HeadSteps<false>{});
+    if (DEFER) {
+        const int q_last = 2 * K + ((nsteps - 2 * K - 1) / CH) * CH;  // the last chunk computed
+#pragma unroll
+        for (int c = 0; c < CH; ++c) store_row(q_last + c, out[c]);
     }
 }
 
@@ -761,12 +904,29 @@ __device__ __forceinline__ void stream_pass_k(const pk_kargs& a, const T* __rest
         const int r0 = 1 + band * a.pband_rows;
         const int r1 = min(a.ny - 1, r0 + a.pband_rows);
         if (r0 >= r1) continue;
-        if (band & 1)
-            stream_pass_unit<T, HAS_B, K, -1, RB>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W,
-                                                  ov, r0, r1, h0);
-        else
-            stream_pass_unit<T, HAS_B, K, 1, RB>(src, dst, bsrc, a.nx, a.ny, a.pitch, strip * stride - ov * W,
-                                                 ov, r0, r1, h0);
+        const int c0 = strip * stride - ov * W;
+        // the first band marches down from the top ring, the last up from the
+        // bottom ring, the others alternate, so that neighbouring bands read the
+        // halo rows they share at about the same time (and hit in the XCD's L2)
+        const int dir = band == 0 ? 1 : (band == a.pbands - 1 ? -1 : ((band & 1) ? -1 : 1));
+        // the march meets a ring row only in its first 2K steps unless the band
+        // ends within K rows of the far ring (a single band, or a short last band)
+        const bool rows_late = dir > 0 ? r1 + K > a.ny : r0 < K;
+        const bool cols = c0 < 1 || c0 + 64 * W > a.nx - 1;
+        const int nx = a.nx, ny = a.ny, pt = a.pitch;
+        if constexpr (RB) {
+            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, true, PASS_CHECKED>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            else stream_pass_unit<T, HAS_B, K, -1, true, PASS_CHECKED>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+        } else if (rows_late) {
+            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_CHECKED>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_CHECKED>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+        } else if (cols) {
+            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_COLS>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_COLS>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+        } else {
+            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_INNER>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_INNER>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+        }
     }
 }
 

@@ -358,9 +358,14 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     }
     if (!tiled) {
         p.layout = PK_LAYOUT_STREAM;
-        // the persistent streaming kernel runs blocks of at most 512 threads (its
-        // passes keep up to 8 levels of the march in registers)
-        if (e->mode == PK_PERSISTENT) p.threads = std::min(p.threads, 512);
+        // the persistent streaming kernel's blocks are as large as its register
+        // budget allows (its passes keep up to 8 levels of the march in registers)
+        if (e->mode == PK_PERSISTENT) {
+            hipFuncAttributes fa{};
+            if (hipFuncGetAttributes(&fa, pkk_persistent_fn(e->dtype, e->has_b, PK_LAYOUT_STREAM)) != hipSuccess)
+                return PK_EDEVICE;
+            p.threads = std::min(p.threads, fa.maxThreadsPerBlock / 64 * 64);
+        }
         const int wpb = p.threads / 64;
         // enough blocks for one wave per unit of >= 4 rows, at most one block per CU
         const int strips = ceil_div(e->nx, 64 * W);
@@ -388,6 +393,11 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         int bands = std::max(1, nw / strips_k);
         bands = std::min(bands, std::max(1, interior / (4 * k)));
         p.pband_rows = o.band_rows > 0 ? std::min(o.band_rows, interior) : ceil_div(interior, bands);
+        // a pass addresses a unit's rows (band + 2k halo rows) through 32-bit byte
+        // offsets: shorter bands for very wide rows, and refuse what cannot fit
+        const uint64_t lim = 0xFFFFFFFFull / e->pitch_bytes;
+        if (lim < static_cast<uint64_t>(2 * k + 1)) return PK_EINVAL;
+        p.pband_rows = static_cast<int>(std::min<uint64_t>(p.pband_rows, lim - 2 * k));
         p.pbands = ceil_div(interior, p.pband_rows);
     }
 

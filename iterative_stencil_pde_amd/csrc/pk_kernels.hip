@@ -603,13 +603,16 @@ __device__ __forceinline__ double residual_round(const pk_kargs& a, int cur, Bar
 
 // The streaming kernel's passes keep up to 8 levels of the march in registers:
 // blocks of at most 512 threads give it 256 VGPRs per lane.
-template <int LAYOUT>
+// (Two waves per SIMD already keep its vector unit busy: 768-thread blocks, which
+// the fp32 Laplace passes would fit, measured slower, 6.5 against 5.3 us per
+// 4096^2 sweep, with shorter bands and more halo rows.)
+template <typename T, bool HAS_B, int LAYOUT>
 struct PkMaxThreads {
     static constexpr int value = LAYOUT == PK_LAYOUT_STREAM ? 512 : 1024;
 };
 
 template <typename T, bool HAS_B, int LAYOUT>
-__global__ void __launch_bounds__(PkMaxThreads<LAYOUT>::value) pk_persistent(pk_kargs a) {
+__global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_persistent(pk_kargs a) {
     extern __shared__ __align__(16) unsigned char pk_lds[];
     __shared__ double s_red[16];
     __shared__ int s_kind, s_n, s_exit, s_carried, s_every;
