@@ -105,6 +105,11 @@ extern "C" {
                       /*   sweeps_done counts iterations.                           */
 #define PK_SWEEP_UNTIL 7 /* Jacobi sweeps until the residual reaches a tolerance:   */
                       /*   submitted with pk_submit_until (see there), not pk_submit */
+#define PK_BLOCKSYNC 8 /* n rounds of the block-level step of a tile sub-sweep and   */
+                      /*   nothing else (persistent only; timing): each wave writes  */
+                      /*   LDS, the block barrier, each wave reads a neighbour's     */
+                      /*   value. Its time per round is the synchronization floor of */
+                      /*   one sub-sweep                                             */
 
 /* ---- option flags ------------------------------------------------------- */
 /* Debug only: the grid barrier drops its release/acquire ordering (relaxed

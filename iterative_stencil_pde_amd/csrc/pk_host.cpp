@@ -661,13 +661,14 @@ int pk_submit(pk_engine* e, pk_task t, uint64_t* ticket) {
     if (!e) return PK_EINVAL;
     if (e->state != RUNNING) return PK_ESTATE;
     const bool known = t.kind == PK_SWEEP || t.kind == PK_SWEEP_RB || t.kind == PK_RESIDUAL ||
-                       t.kind == PK_EXIT || t.kind == PK_BARRIER || t.kind == PK_STAMP;
+                       t.kind == PK_EXIT || t.kind == PK_BARRIER || t.kind == PK_STAMP ||
+                       t.kind == PK_BLOCKSYNC;
     if (!known || t.n < 0 || t.n > PK_TASK_N_MAX) return PK_EINVAL;
     // red-black runs 2n half-sweeps
     if (t.kind == PK_SWEEP_RB && t.n > PK_TASK_N_MAX / 2)
         return PK_EINVAL;
     if (e->mode == PK_LAUNCH) {
-        if (t.kind == PK_BARRIER || t.kind == PK_STAMP) return PK_EINVAL;
+        if (t.kind == PK_BARRIER || t.kind == PK_STAMP || t.kind == PK_BLOCKSYNC) return PK_EINVAL;
         const uint64_t seq = e->lresults.size() + 1;
         hipEvent_t& ev = e->ev_ticket[seq % PK_RING];
         if (seq > PK_RING) {  // the slot's previous ticket must be finished

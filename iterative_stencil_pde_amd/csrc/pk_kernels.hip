@@ -833,6 +833,18 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
             for (int s = 0; s < n; ++s) grid_barrier(bc);
         } else if (kind == PK_STAMP) {
             errs = stamp_task(a, n, stamp_round, bc, s_red);
+        } else if (kind == PK_BLOCKSYNC) {
+            // the block-level step of every tile sub-sweep and nothing else: each
+            // wave writes to LDS, the block meets, each wave reads its neighbour's
+            // value (slots alternate by round, as the tiles' exchange slots do)
+            const int wv = wave_id();
+            double v = static_cast<double>(wv);
+            for (int r = 0; r < n; ++r) {
+                if ((threadIdx.x & 63) == 0) s_red[(r & 1) * 8 + (wv & 7)] = v;
+                __syncthreads();
+                v += s_red[(r & 1) * 8 + ((wv + 1) & 7)];
+            }
+            if (v < 0.0) errs = 1;  // never: keeps the loop's result in use
         } else {
             status = PK_EINVAL;
         }

@@ -21,3 +21,4 @@ hipError_t pkk_launch_residual(int dtype, bool has_b, const pk_kargs& a, int thr
 // b = (T)((h*h) * f) on a pitched ny x pitch array.
 hipError_t pkk_launch_scale_source(int dtype, const void* f, void* b, int nx, int ny, int pitch,
                                    double hh, hipStream_t s);
+

@@ -27,6 +27,7 @@ PK_F32, PK_F64 = 0, 1
 PK_PERSISTENT, PK_LAUNCH = 0, 1
 PK_LAYOUT_AUTO, PK_LAYOUT_STREAM, PK_LAYOUT_RESIDENT, PK_LAYOUT_REGISTER = 0, 1, 2, 3
 PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP, PK_SWEEP_RB, PK_SWEEP_UNTIL = 1, 2, 3, 4, 5, 6, 7
+PK_BLOCKSYNC = 8
 PK_DBG_BROKEN_BARRIER = 0x1
 PK_TASK_N_MAX = 0x0FFFFFFF
 PK_BARRIER_AUTO, PK_BARRIER_FLAT, PK_BARRIER_TWO_LEVEL, PK_BARRIER_XCD = 0, 1, 2, 3
