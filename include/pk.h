@@ -334,6 +334,35 @@ int pk_run_launch_per_iter(pk_engine* e, int n, int sync_each, double* elapsed_u
  * reps < 1), PK_ESTATE (persistent engine, or poisoned), PK_EDEVICE. */
 int pk_run_graph_per_iter(pk_engine* e, int n, int reps, double* elapsed_us);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): n Jacobi sweeps and,
+ * if residual is not NULL, the residual R of the result, on the caller's own
+ * device buffers, with the kernels, grid and results (bit for bit) of a
+ * PK_LAUNCH engine created with default options running the tasks SWEEP n and
+ * RESIDUAL. Allocates nothing and never synchronizes: the launches are queued
+ * on `stream` (NULL: the null stream) and the call returns.
+ *   dtype       PK_F32 or PK_F64 (element type T below)
+ *   nx, ny      field size (>= 3); pitch: row stride in elements, at least nx
+ *               rounded up to 16 bytes, rows 16-byte aligned
+ *   u0, u1      device arrays of ny x pitch T, 16-byte aligned. u0 holds the
+ *               field (the outer ring is the Dirichlet data); u1 must hold the
+ *               same ring, its interior is overwritten. Sweep k reads u[k % 2]
+ *               and writes u[(k + 1) % 2]: the result is in u0 for even n, in
+ *               u1 for odd n
+ *   b           NULL (Laplace), or a device array like u0 holding the scaled
+ *               source (T)((h*h) * f) (only interior nodes are read)
+ *   residual    NULL, or a device-accessible double (device memory or mapped
+ *               pinned host memory) that receives R of the final field
+ * Scratch: one partial sum per block of the residual, in a fixed array of the
+ * library (PK_NOALLOC_MAX_BLOCKS = 1024 doubles) per GPU. Calls that overlap
+ * on one GPU (other streams, other host threads) race on it; each call writes
+ * every partial it reads, so nothing carries over from an earlier call.
+ * Errors: PK_EINVAL (sizes, pitch, alignment, n < 0, u0 == u1, or a plan whose
+ * block count exceeds the scratch), PK_ELAUNCH (kernel not resident),
+ * PK_EDEVICE (HIP error while queueing). */
+int pk_sweep_noalloc(int dtype, int nx, int ny, int pitch, void* u0, void* u1, const void* b, int n,
+                     double* residual, void* stream);
+
 /* Engine geometry and counters: the grid the occupancy query allowed ("@persistent"
  * page, "What it promises"), the layout chosen, and the kernel time measured on the
  * device ("Persistent Kernels", "Sketching out the experiment").

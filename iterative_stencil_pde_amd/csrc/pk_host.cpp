@@ -919,6 +919,70 @@ int pk_run_graph_per_iter(pk_engine* e, int n, int reps, double* elapsed_us) {
     return PK_OK;
 }
 
+int pk_sweep_noalloc(int dtype, int nx, int ny, int pitch, void* u0, void* u1, const void* b, int n,
+                     double* residual, void* stream) {
+    if (dtype != PK_F32 && dtype != PK_F64) return PK_EINVAL;
+    const int esize = dtype == PK_F64 ? 8 : 4;
+    const int W = 16 / esize;
+    if (nx < 3 || ny < 3 || n < 0 || !u0 || !u1 || u0 == u1) return PK_EINVAL;
+    // rows are read and written as whole 16-byte vectors
+    if (pitch < (nx + W - 1) / W * W || (static_cast<int64_t>(pitch) * esize) % 16 != 0) return PK_EINVAL;
+    if (static_cast<int64_t>(nx) * esize > (int64_t(1) << 30)) return PK_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(u0) | reinterpret_cast<uintptr_t>(u1) | reinterpret_cast<uintptr_t>(b)) % 16)
+        return PK_EINVAL;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PK_EDEVICE;
+    double* part = nullptr;
+    if (pkk_noalloc_scratch(dev, &part) != hipSuccess) return PK_EDEVICE;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PK_EDEVICE;
+    // the plan of a PK_LAUNCH engine with default options (same grid, same
+    // geometry, so the same results bit for bit); nothing here allocates
+    pk_engine e;
+    e.nx = nx;
+    e.ny = ny;
+    e.dtype = dtype;
+    e.esize = esize;
+    e.mode = PK_LAUNCH;
+    e.has_b = b != nullptr;
+    e.cus = prop.multiProcessorCount;
+    e.pitch = pitch;
+    e.pitch_bytes = static_cast<size_t>(pitch) * esize;
+    pk_opts o;
+    pk_opts_default(&o);
+    o.dtype = dtype;
+    o.mode = PK_LAUNCH;
+    const int rc = plan_engine(&e, o, prop);
+    if (rc != PK_OK) return rc;
+    if (e.plan.grid > PK_NOALLOC_MAX_BLOCKS) return PK_EINVAL;  // more partials than the scratch holds
+    pk_kargs a{};
+    a.u[0] = u0;
+    a.u[1] = u1;
+    a.b = b;
+    a.nx = nx;
+    a.ny = ny;
+    a.pitch = pitch;
+    a.strips = e.plan.strips;
+    a.bands = e.plan.bands;
+    a.band_rows = e.plan.band_rows;
+    a.grid = e.plan.grid;
+    a.xcd_remap = e.plan.xcd_remap;
+    a.pass_sweeps = 1;
+    a.partials = part;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t he = hipSuccess;
+    int cur = 0;
+    for (int k = 0; k < n && he == hipSuccess; ++k, cur ^= 1)
+        he = pkk_launch_sweep(dtype, e.has_b, a, e.plan.threads, cur, -1, st);
+    if (he == hipSuccess && residual)
+        he = pkk_launch_residual(dtype, e.has_b, a, e.plan.threads, cur, residual, st);
+    if (he != hipSuccess) {
+        debug_msg("pk_sweep_noalloc", he);
+        return PK_EDEVICE;
+    }
+    return PK_OK;
+}
+
 int pk_get_info(pk_engine* e, pk_info* info) {
     if (!e || !info) return PK_EINVAL;
     std::memset(info, 0, sizeof(*info));

@@ -976,3 +976,32 @@ hipError_t pkk_launch_scale_source(int dtype, const void* f, void* b, int nx, in
                            static_cast<const float*>(f), static_cast<float*>(b), nx, ny, pitch, hh);
     return hipGetLastError();
 }
+
+// ---- scratch of the entry point that allocates nothing ------------------------
+// pk_sweep_noalloc runs the launch-per-sweep kernels on the caller's buffers;
+// their only scratch, one residual partial per block, lives in this array (one
+// copy per GPU, held until the process ends). Host code never passes the
+// array's name to a kernel: it looks the array's address up once per device
+// (hipGetSymbolAddress, with that device current) and passes that address.
+static __device__ __align__(256) double scratch[PK_NOALLOC_MAX_BLOCKS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+double* g_scratch_addr[kMaxDevices] = {};  // per device, looked up on first use
+}  // namespace
+
+hipError_t pkk_noalloc_scratch(int dev, double** out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    double* p = __atomic_load_n(&g_scratch_addr[dev], __ATOMIC_ACQUIRE);
+    if (!p) {
+        // the caller has made `dev` current; two threads racing here store the
+        // same address
+        void* addr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        p = static_cast<double*>(addr);
+        __atomic_store_n(&g_scratch_addr[dev], p, __ATOMIC_RELEASE);
+    }
+    *out = p;
+    return hipSuccess;
+}

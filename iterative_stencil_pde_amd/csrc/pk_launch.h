@@ -22,3 +22,8 @@ hipError_t pkk_launch_residual(int dtype, bool has_b, const pk_kargs& a, int thr
 hipError_t pkk_launch_scale_source(int dtype, const void* f, void* b, int nx, int ny, int pitch,
                                    double hh, hipStream_t s);
 
+// Blocks the scratch of pk_sweep_noalloc holds residual partials for.
+#define PK_NOALLOC_MAX_BLOCKS 1024
+// Device address of that scratch on device `dev` (which must be current); looked
+// up once per device and kept.
+hipError_t pkk_noalloc_scratch(int dev, double** out);

@@ -35,7 +35,8 @@ PK_EXCHANGE_AUTO, PK_EXCHANGE_BARRIER, PK_EXCHANGE_NEIGHBOR, PK_EXCHANGE_TAGGED 
 
 EXPORTED = ["pk_opts_default", "pk_create", "pk_submit", "pk_submit_until", "pk_wait", "pk_readback",
             "pk_run_launch_per_iter", "pk_run_graph_per_iter", "pk_get_info", "pk_destroy",
-            "pk_strerror"]
+            "pk_strerror", "pk_sweep_noalloc"]
+PK_NOALLOC_MAX_BLOCKS = 1024
 
 
 class pk_opts(ctypes.Structure):
@@ -111,6 +112,8 @@ def load(path: str = LIB_PATH):
     lib.pk_destroy.argtypes = [vp]
     lib.pk_strerror.restype = ctypes.c_char_p
     lib.pk_strerror.argtypes = [ip]
+    lib.pk_sweep_noalloc.restype = ip
+    lib.pk_sweep_noalloc.argtypes = [ip, ip, ip, ip, vp, vp, vp, ip, vp, vp]
     _lib = lib
     return lib
 
@@ -214,6 +217,13 @@ def pk_get_info(eng: int) -> pk_info:
 def pk_destroy(eng: int) -> None:
     if eng:
         _check(load().pk_destroy(eng), "pk_destroy")
+
+
+def pk_sweep_noalloc(dtype: int, nx: int, ny: int, pitch: int, u0: int, u1: int, b: int | None,
+                     n: int, residual: int | None = None, stream: int | None = None) -> int:
+    """Device pointers as integers (e.g. a torch tensor's data_ptr()); returns the
+    status code (0 = queued). Nothing is allocated and nothing synchronizes."""
+    return load().pk_sweep_noalloc(dtype, nx, ny, pitch, u0, u1, b, n, residual, stream)
 
 
 class Engine:
