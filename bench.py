@@ -26,6 +26,7 @@ import argparse
 import collections
 import copy
 import csv
+import ctypes
 import glob
 import hashlib
 import json
@@ -55,6 +56,36 @@ EXCHANGES = {0: None, 1: "barrier", 2: "neighbor", 3: "tagged"}
 def say(msg: str):
     """Progress on stderr (stdout carries only the JSON line)."""
     print(msg, file=sys.stderr, flush=True)
+
+
+class Runtime:
+    """The HIP runtime the engine library itself loaded, for plumbing only: a device
+    copy of known size (to calibrate byte counters) and releasing the device."""
+
+    def __init__(self):
+        pk.load()
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+        self.rt.hipFree.argtypes = [ctypes.c_void_p]
+        self.rt.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+
+    def calibration_copy(self, mib: int):
+        """One device-to-device copy of mib MiB (the runtime's copy kernel)."""
+        n = mib * (1 << 20)
+        a, b = ctypes.c_void_p(), ctypes.c_void_p()
+        assert self.rt.hipMalloc(ctypes.byref(a), n) == 0 and self.rt.hipMalloc(ctypes.byref(b), n) == 0
+        assert self.rt.hipMemcpy(b, a, n, 3) == 0  # hipMemcpyDeviceToDevice
+        assert self.rt.hipDeviceSynchronize() == 0
+        self.rt.hipFree(a)
+        self.rt.hipFree(b)
+
+    def release(self):
+        """Free every device resource of this process now, while the process (and
+        any profiler attached to it) is still whole, instead of in exit-time
+        teardown. Only once no engine is left: a resident persistent kernel would
+        make the synchronize wait for it."""
+        self.rt.hipDeviceSynchronize()
+        self.rt.hipDeviceReset()
 
 
 # ---- running task scripts ---------------------------------------------------
@@ -465,8 +496,8 @@ def main():
                     help="store the traffic of two rocprofv3 counter runs of this workload "
                          "(made with --main-only --calibrate-copy MIB) and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="first run a torch device-to-device copy of MIB MiB (a plain copy "
-                         "kernel of known size, to scale HBM byte counters)")
+                    help="first run a device-to-device copy of MIB MiB (a plain copy kernel "
+                         "of known size, to scale HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -489,24 +520,25 @@ def main():
     traffic_key = w.name.split("_")[0]
 
     if args.fold_traffic:
-        # the launch of a --main-only run: its algorithmic bytes with the default plan
-        with pk.Engine(w.u0, w.f, h=w.h, **opts) as e:
-            k = e.info().pass_sweeps
+        # the launch of a --main-only run of a streaming workload: its algorithmic
+        # bytes with the passes it ran (the planner's default depth unless given)
+        k = args.pass_sweeps or pk.PK_MAX_PASS
         per_step = algorithmic_bytes(w, k)[1]
         pure = algorithmic_bytes(sweeps_only(w), k)[1]
         fold_traffic(args.fold_traffic[0], args.fold_traffic[1], traffic_key,
                      (args.steps + args.warmup) * per_step + args.steps * pure, args.calibrate_copy or 1024)
         return
 
+    rt = Runtime()
+    try:
+        run(args, w, opts, traffic_key, rt)
+    finally:
+        rt.release()
+
+
+def run(args, w, opts, traffic_key, rt):
     if args.calibrate_copy:
-        import torch  # before the engine library: one HIP runtime in the process
-        n = args.calibrate_copy * (1 << 20) // 4
-        x = torch.ones(n, dtype=torch.float32, device="cuda")
-        y = torch.empty_like(x)
-        y.copy_(x)
-        torch.cuda.synchronize()
-        del x, y
-        torch.cuda.empty_cache()
+        rt.calibration_copy(args.calibrate_copy)
 
     cells_per_step = w.interior_cells * w.sweeps
     say(f"[bench] {w.name}: persistent, {args.warmup} + {args.steps} steps")

@@ -710,12 +710,45 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
 //     branch-free blend; PASS_INNER also leaves out the column check, for units
 //     whose columns [c0, c0 + 64 W) are all interior.
 //
+// RES: the pass also sums rho^2 of its result (the residual of the field it
+// stores, as a RESIDUAL task would compute it, element by element the same
+// expression): a level K+1 that computes rho of level K's rows instead of a
+// stencil, accumulated in double per lane over the band's rows and the strip's
+// stored lanes, so every interior node counts once. The unit then reaches K+1
+// halo rows and needs K+1 overlap columns.
+//
 // Memory: rows go in chunks of CH, loaded one chunk ahead of their use. With
 // DEFER, a chunk's level-K rows are stored at the start of the next chunk
 // (before its loads): faster where stores are a large share of the traffic
 // (fp64, or with b); otherwise each row is stored as soon as it is computed.
 // ---------------------------------------------------------------------------
 enum { PASS_CHECKED = 0, PASS_COLS = 1, PASS_INNER = 2 };
+
+// rho^2 of one vector summed in double over its interior elements, from the
+// vector (m), its row neighbours (s, n), its W/E neighbours by DPP and b
+// (overlap lanes are not summed, so their outer neighbours may be anything)
+template <typename T, bool HAS_B, bool COLS>
+__device__ __forceinline__ double pass_rho2(const Vec<T>& s, const Vec<T>& m, const Vec<T>& n,
+                                            const Vec<T>& b, int col, int nx) {
+    constexpr int W = VecW<T>::W;
+    const T west = from_lower_any(m.v[W - 1]), east = from_upper_any(m.v[0]);
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const double w = static_cast<double>((k == 0) ? west : m.v[k - 1]);
+        const double e = static_cast<double>((k == W - 1) ? east : m.v[k + 1]);
+        double t = (w + e) + (static_cast<double>(s.v[k]) + static_cast<double>(n.v[k]));
+        if (HAS_B) t = t + static_cast<double>(b.v[k]);
+        const double r = t - 4.0 * static_cast<double>(m.v[k]);
+        if constexpr (COLS) {
+            const int c = col + k;
+            acc += (c == 0 || c >= nx - 1) ? 0.0 : r * r;
+        } else {
+            acc += r * r;
+        }
+    }
+    return acc;
+}
 
 template <typename T, bool HAS_B, bool COLS>
 __device__ __forceinline__ Vec<T> pass_stencil(const Vec<T>& s, const Vec<T>& m, const Vec<T>& n,
@@ -751,16 +784,17 @@ struct HeadSteps {
     static constexpr bool value = V;
 };
 
-template <typename T, bool HAS_B, int K, int DIR, bool RB, int MODE>
-__device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* __restrict__ dst,
-                                                 const T* __restrict__ bsrc, int nx, int ny,
-                                                 int pitch, int c0, int ov, int r0, int r1, int h0) {
+template <typename T, bool HAS_B, int K, int DIR, bool RB, int MODE, bool RES>
+__device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T* __restrict__ dst,
+                                                   const T* __restrict__ bsrc, int nx, int ny,
+                                                   int pitch, int c0, int ov, int r0, int r1, int h0) {
     constexpr int dir = DIR;
     constexpr int W = VecW<T>::W;
-    constexpr int CH = (HAS_B || K >= 3) ? 2 : 4;  // rows per chunk
+    constexpr int L = K + (RES ? 1 : 0);  // levels of the march (the last one rho with RES)
+    constexpr int CH = (HAS_B || L >= 3) ? 2 : 4;  // rows per chunk
     constexpr bool DEFER = HAS_B || sizeof(T) == 8;
     constexpr bool COLS = MODE != PASS_INNER;
-    static_assert((2 * K) % CH == 0, "the first 2K steps are whole chunks");
+    static_assert((2 * L) % CH == 0, "the first 2L steps are whole chunks");
     const int lane = threadIdx.x & 63;
     const int col = c0 + lane * W;
     const bool act = col >= 0 && col < nx;
@@ -772,7 +806,7 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
     // a lane outside the field borders a ring column, which keeps its value.
     // The buffer descriptors cover rows [w0, w1), every row the unit reads or
     // writes (the planner keeps them within 4 GiB).
-    const int w0 = max(0, r0 - K), w1 = min(ny, r1 + K);
+    const int w0 = max(0, r0 - L), w1 = min(ny, r1 + L);
     const size_t p = static_cast<size_t>(pitch);
     const uint32_t row_bytes = static_cast<uint32_t>(p * sizeof(T));
     const uint32_t win_bytes = static_cast<uint32_t>(w1 - w0) * row_bytes;
@@ -783,16 +817,17 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
     const uint32_t sbyte = static_cast<uint32_t>(max(col, 0)) * sizeof(T);  // stored lanes have col >= 0
     const int b_lo = max(w0, 1), b_hi = min(w1, ny - 1) - 1;  // b rows: interior rows of the window
 
-    Vec<T> ra[K], rm[K];  // level j rows x-1 and x, x the last row it received
-    Vec<T> bq[K];         // bq[j] = b row of the level j+1 row computed at this step
+    Vec<T> ra[L], rm[L];  // level j rows x-1 and x, x the last row it received
+    Vec<T> bq[L];         // bq[j] = b row of the level j+1 row computed at this step
+    double acc = 0.0;     // RES: this lane's rho^2
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
+    for (int j = 0; j < L; ++j) {
         ra[j] = rm[j] = vzero<T>();
         bq[j] = vzero<T>();
     }
-    // dir = +1 marches down from r0 - K, dir = -1 marches up from r1 - 1 + K
-    const int nsteps = (r1 - r0) + 2 * K;
-    const int t_first = dir > 0 ? r0 - K : r1 - 1 + K;
+    // dir = +1 marches down from r0 - L, dir = -1 marches up from r1 - 1 + L
+    const int nsteps = (r1 - r0) + 2 * L;
+    const int t_first = dir > 0 ? r0 - L : r1 - 1 + L;
     const auto load_chunk = [&](int q, Vec<T>* u, Vec<T>* b) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
@@ -813,19 +848,30 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
         }
     };
     Vec<T> out[CH];  // DEFER: a chunk's level-K rows, stored at the start of the next chunk
-    // One step: level-0 row u (and its b row). In the first 2K steps (head) only
-    // levels j <= q / 2 are computed: a higher level's row at this step lies
-    // outside the rows any stored row depends on.
+    // One step: level-0 row u (and its b row); returns level K's row. In the first
+    // 2L steps (head) only levels j <= q / 2 are computed: a higher level's row at
+    // this step lies outside the rows any stored row (or summed rho) depends on.
     const auto step = [&](int q, const Vec<T>& u, const Vec<T>& b, auto head_c) -> Vec<T> {
         constexpr bool head = decltype(head_c)::value;
         const int t = t_first + dir * q;
 #pragma unroll
-        for (int j = K - 1; j > 0; --j) bq[j] = bq[j - 1];
+        for (int j = L - 1; j > 0; --j) bq[j] = bq[j - 1];
         bq[0] = b;
         Vec<T> inc = u;  // row t of level 0, then level j's new row
+        Vec<T> outK = u;
 #pragma unroll
-        for (int j = 1; j <= K; ++j) {
+        for (int j = 1; j <= L; ++j) {
             const Vec<T> mid = rm[j - 1];
+            if (RES && j == L) {  // rho of level K's row t - dir L, if it is a band row
+                const int row = t - dir * j;
+                if ((!head || 2 * j <= q) && row >= r0 && row < r1) {  // wave-uniform
+                    const double r2 = pass_rho2<T, HAS_B, COLS>(ra[j - 1], mid, inc, bq[j - 1], col, nx);
+                    if (store_lane) acc += r2;
+                }
+                ra[j - 1] = mid;
+                rm[j - 1] = inc;
+                continue;
+            }
             if (!head || 2 * j <= q) {  // wave-uniform
                 const int row = t - dir * j;  // level j row computed at this step
                 // level j-1 rows row-1, row, row+1 (dir = -1: row+1, row, row-1)
@@ -844,8 +890,9 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
                 ra[j - 1] = mid;
                 rm[j - 1] = inc;
             }
+            if (j == K) outK = inc;
         }
-        return inc;
+        return outK;
     };
     const auto run = [&](int q_begin, int q_end, auto head_c) {
         Vec<T> ld[CH], lb[CH];  // the chunk being computed
@@ -877,28 +924,32 @@ __device__ __forceinline__ void stream_pass_unit(const T* __restrict__ src, T* _
             }
         }
     };
-    run(0, 2 * K, HeadSteps<true>{});
-    run(2 * K, nsteps, HeadSteps<false>{});
+    run(0, 2 * L, HeadSteps<true>{});
+    run(2 * L, nsteps, HeadSteps<false>{});
     if (DEFER) {
-        const int q_last = 2 * K + ((nsteps - 2 * K - 1) / CH) * CH;  // the last chunk computed
+        const int q_last = 2 * L + ((nsteps - 2 * L - 1) / CH) * CH;  // the last chunk computed
 #pragma unroll
         for (int c = 0; c < CH; ++c) store_row(q_last + c, out[c]);
     }
+    return acc;
 }
 
 // One pass of k sweeps (1 <= k <= PK_MAX_PASS) over all units, src -> dst.
 // h0 >= 0: the k levels are red-black half-sweeps, level j of colour (h0+j-1) mod 2.
-template <typename T, bool HAS_B, int K, bool RB>
-__device__ __forceinline__ void stream_pass_k(const pk_kargs& a, const T* __restrict__ src,
-                                              T* __restrict__ dst, int h0) {
+// RES: also this lane's rho^2 of the result (returned; 0 otherwise).
+template <typename T, bool HAS_B, int K, bool RB, bool RES>
+__device__ __forceinline__ double stream_pass_k(const pk_kargs& a, const T* __restrict__ src,
+                                                T* __restrict__ dst, int h0) {
     constexpr int W = VecW<T>::W;
-    const int ov = (K + W - 1) / W;
+    constexpr int L = K + (RES ? 1 : 0);
+    const int ov = (L + W - 1) / W;
     const int stride = (64 - 2 * ov) * W;  // stored columns per strip
     const int strips = (a.nx + stride - 1) / stride;
     const int gw = unit_wave(a);
     const int nw = a.grid * (static_cast<int>(blockDim.x) >> 6);
     const int units = strips * a.pbands;
     const T* bsrc = static_cast<const T*>(a.b);
+    double acc = 0.0;
     for (int u = gw; u < units; u += nw) {
         const int strip = u % strips, band = u / strips;
         const int r0 = 1 + band * a.pband_rows;
@@ -909,55 +960,74 @@ __device__ __forceinline__ void stream_pass_k(const pk_kargs& a, const T* __rest
         // bottom ring, the others alternate, so that neighbouring bands read the
         // halo rows they share at about the same time (and hit in the XCD's L2)
         const int dir = band == 0 ? 1 : (band == a.pbands - 1 ? -1 : ((band & 1) ? -1 : 1));
-        // the march meets a ring row only in its first 2K steps unless the band
-        // ends within K rows of the far ring (a single band, or a short last band)
-        const bool rows_late = dir > 0 ? r1 + K > a.ny : r0 < K;
+        // the march meets a ring row only in its first 2L steps unless the band
+        // ends within L rows of the far ring (a single band, or a short last band)
+        const bool rows_late = dir > 0 ? r1 + L > a.ny : r0 < L;
         const bool cols = c0 < 1 || c0 + 64 * W > a.nx - 1;
         const int nx = a.nx, ny = a.ny, pt = a.pitch;
-        if constexpr (RB) {
-            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, true, PASS_CHECKED>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-            else stream_pass_unit<T, HAS_B, K, -1, true, PASS_CHECKED>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+        // red-black passes, the last pass of a task (RES) and passes of fewer than
+        // PK_MAX_PASS sweeps (a task's passes are all PK_MAX_PASS deep but its
+        // last) take the checked march
+        if constexpr (RB || RES || K != PK_MAX_PASS) {
+            if (dir > 0) acc += stream_pass_unit<T, HAS_B, K, 1, RB, PASS_CHECKED, RES>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            else acc += stream_pass_unit<T, HAS_B, K, -1, RB, PASS_CHECKED, RES>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
         } else if (rows_late) {
-            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_CHECKED>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_CHECKED>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_CHECKED, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_CHECKED, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
         } else if (cols) {
-            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_COLS>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_COLS>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_COLS, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_COLS, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
         } else {
-            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_INNER>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_INNER>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_INNER, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_INNER, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
         }
     }
+    return acc;
 }
 
+// One pass of k sweeps; res (Jacobi only): also returns this lane's rho^2 of
+// the result (the residual march of the last pass of a task).
 template <typename T, bool HAS_B>
-__device__ __forceinline__ void stream_pass(const pk_kargs& a, const T* __restrict__ src,
-                                            T* __restrict__ dst, int k, int h0 = -1) {
+__device__ __forceinline__ double stream_pass(const pk_kargs& a, const T* __restrict__ src,
+                                              T* __restrict__ dst, int k, int h0, bool res) {
     // red-black passes are their own instances: the colour mask stays out of the
     // Jacobi march
     if (h0 >= 0) {
         switch (k) {
-            case 2: stream_pass_k<T, HAS_B, 2, true>(a, src, dst, h0); break;
-            case 3: stream_pass_k<T, HAS_B, 3, true>(a, src, dst, h0); break;
-            case 4: stream_pass_k<T, HAS_B, 4, true>(a, src, dst, h0); break;
-            case 5: stream_pass_k<T, HAS_B, 5, true>(a, src, dst, h0); break;
-            case 6: stream_pass_k<T, HAS_B, 6, true>(a, src, dst, h0); break;
-            case 7: stream_pass_k<T, HAS_B, 7, true>(a, src, dst, h0); break;
-            case 8: stream_pass_k<T, HAS_B, 8, true>(a, src, dst, h0); break;
+            case 2: stream_pass_k<T, HAS_B, 2, true, false>(a, src, dst, h0); break;
+            case 3: stream_pass_k<T, HAS_B, 3, true, false>(a, src, dst, h0); break;
+            case 4: stream_pass_k<T, HAS_B, 4, true, false>(a, src, dst, h0); break;
+            case 5: stream_pass_k<T, HAS_B, 5, true, false>(a, src, dst, h0); break;
+            case 6: stream_pass_k<T, HAS_B, 6, true, false>(a, src, dst, h0); break;
+            case 7: stream_pass_k<T, HAS_B, 7, true, false>(a, src, dst, h0); break;
+            case 8: stream_pass_k<T, HAS_B, 8, true, false>(a, src, dst, h0); break;
             default: stream_sweep<T, HAS_B>(a, src, dst, h0); break;
         }
-        return;
+        return 0.0;
+    }
+    if (res) {
+        switch (k) {
+            case 1: return stream_pass_k<T, HAS_B, 1, false, true>(a, src, dst, h0);
+            case 2: return stream_pass_k<T, HAS_B, 2, false, true>(a, src, dst, h0);
+            case 3: return stream_pass_k<T, HAS_B, 3, false, true>(a, src, dst, h0);
+            case 4: return stream_pass_k<T, HAS_B, 4, false, true>(a, src, dst, h0);
+            case 5: return stream_pass_k<T, HAS_B, 5, false, true>(a, src, dst, h0);
+            case 6: return stream_pass_k<T, HAS_B, 6, false, true>(a, src, dst, h0);
+            case 7: return stream_pass_k<T, HAS_B, 7, false, true>(a, src, dst, h0);
+            default: return stream_pass_k<T, HAS_B, 8, false, true>(a, src, dst, h0);
+        }
     }
     switch (k) {
-        case 2: stream_pass_k<T, HAS_B, 2, false>(a, src, dst, h0); break;
-        case 3: stream_pass_k<T, HAS_B, 3, false>(a, src, dst, h0); break;
-        case 4: stream_pass_k<T, HAS_B, 4, false>(a, src, dst, h0); break;
-        case 5: stream_pass_k<T, HAS_B, 5, false>(a, src, dst, h0); break;
-        case 6: stream_pass_k<T, HAS_B, 6, false>(a, src, dst, h0); break;
-        case 7: stream_pass_k<T, HAS_B, 7, false>(a, src, dst, h0); break;
-        case 8: stream_pass_k<T, HAS_B, 8, false>(a, src, dst, h0); break;
+        case 2: stream_pass_k<T, HAS_B, 2, false, false>(a, src, dst, h0); break;
+        case 3: stream_pass_k<T, HAS_B, 3, false, false>(a, src, dst, h0); break;
+        case 4: stream_pass_k<T, HAS_B, 4, false, false>(a, src, dst, h0); break;
+        case 5: stream_pass_k<T, HAS_B, 5, false, false>(a, src, dst, h0); break;
+        case 6: stream_pass_k<T, HAS_B, 6, false, false>(a, src, dst, h0); break;
+        case 7: stream_pass_k<T, HAS_B, 7, false, false>(a, src, dst, h0); break;
+        case 8: stream_pass_k<T, HAS_B, 8, false, false>(a, src, dst, h0); break;
         default: stream_sweep<T, HAS_B>(a, src, dst, -1); break;
     }
+    return 0.0;
 }
 
 // Per-block sum of rho^2 over the same units; valid in thread 0.

@@ -550,9 +550,18 @@ __device__ __forceinline__ int64_t stamp_task(const pk_kargs& a, int n, uint32_t
 // n Jacobi sweeps of the field in u[cur] in the engine's layout (cur flips).
 // n sub-sweeps in the engine's layout: Jacobi sweeps, or (rb) red-black
 // half-sweeps, red first.
+// Residual state shared by the sweeping tasks (identical in every block): the
+// round count picks the half of `partials` a round uses; `ready` says that the
+// last streaming pass already wrote this round's partials (of the field as it
+// is now), so the next residual only sums them.
+struct ResidualState {
+    uint32_t round;
+    bool ready;
+};
+
 template <typename T, bool HAS_B, int LAYOUT>
 __device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, int& cur, BarrierCtx& bc,
-                                            T* lds) {
+                                            T* lds, ResidualState& rs, double* s_red) {
     if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
         if (rb)
             resident_sweep_task<T, HAS_B, true>(a, n, cur, bc, lds);
@@ -566,13 +575,24 @@ __device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, i
     } else {
         for (int s = 0; s < n;) {
             const int k = min(a.pass_sweeps, n - s);
-            stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), static_cast<T*>(a.u[cur ^ 1]), k,
-                                  rb ? (s & 1) : -1);
-            grid_barrier(bc, bc.broken);
+            // the last Jacobi pass of a task also sums rho^2 of its result, so a
+            // RESIDUAL that follows need not read the field again ("Grid-Wide
+            // Barriers", "What the barrier buys": the convergence check as a
+            // reduction at the barrier); not under the negative control
+            const bool res = s + k >= n && !rb && !bc.broken;
+            const double acc = stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]),
+                                                     static_cast<T*>(a.u[cur ^ 1]), k, rb ? (s & 1) : -1, res);
+            if (res) {
+                const double p = block_sum(acc, s_red);
+                if (threadIdx.x == 0) a.partials[static_cast<size_t>(rs.round & 1u) * a.grid + blockIdx.x] = p;
+            }
+            grid_barrier(bc, bc.broken);  // also orders the partials before any read
             cur ^= 1;
             s += k;
+            rs.ready = res;
         }
     }
+    if (rb && n > 0) rs.ready = false;  // the field changed, no partials of it
 }
 
 // One residual round: each block's partial goes to the half of `partials` of
@@ -582,14 +602,19 @@ __device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, i
 // block writes round r + 2 only after passing round r + 1's barrier, which every
 // reader of round r reaches only after its reads. Returns R in every thread of
 // a block that asked (0 elsewhere).
+// When the last streaming pass already wrote this round's partials (rs.ready),
+// the round only sums them: that pass's grid barrier ordered them.
 template <typename T, bool HAS_B>
 __device__ __forceinline__ double residual_round(const pk_kargs& a, int cur, BarrierCtx& bc,
-                                                 uint32_t& round, double* s_red, bool all) {
-    double* part = a.partials + static_cast<size_t>(round & 1u) * a.grid;
-    round += 1;
-    const double p = stream_residual_block<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), s_red);
-    if (threadIdx.x == 0) part[blockIdx.x] = p;
-    grid_barrier(bc);
+                                                 ResidualState& rs, double* s_red, bool all) {
+    double* part = a.partials + static_cast<size_t>(rs.round & 1u) * a.grid;
+    rs.round += 1;
+    if (!rs.ready) {
+        const double p = stream_residual_block<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), s_red);
+        if (threadIdx.x == 0) part[blockIdx.x] = p;
+        grid_barrier(bc);
+    }
+    rs.ready = false;
     double r = 0.0;
     if (all || blockIdx.x == 0) {
         const double tot = sum_partials(part, a.grid);
@@ -668,7 +693,7 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
     int64_t sweeps = 0;
     uint64_t next_seq = 1;
     bool may_carry = false;  // the last task passed an ordered barrier (uniform)
-    uint32_t res_round = 0;  // residual rounds so far (uniform): partials half
+    ResidualState rs{0u, false};  // residual rounds so far (uniform) and ready partials
     uint32_t stamp_round = 0;
     pk_mailbox* mail = a.mail;
 
@@ -813,7 +838,7 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
                 int done = 0;
                 for (;;) {  // the same decisions in every block
                     if (check) {
-                        res = residual_round<T, HAS_B>(a, cur, bc, res_round, s_red, until);
+                        res = residual_round<T, HAS_B>(a, cur, bc, rs, s_red, until);
                         if (res <= tol) break;
                     }
                     if (done >= budget) break;
@@ -821,7 +846,8 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
                     // red-black: k iterations = 2k half-sweeps, each computed into
                     // the other buffer with the other colour copied (the in-place
                     // result: a node never reads its own colour)
-                    sweeps_task<T, HAS_B, LAYOUT>(a, rb ? 2 * k : k, rb, cur, bc, reinterpret_cast<T*>(pk_lds));
+                    sweeps_task<T, HAS_B, LAYOUT>(a, rb ? 2 * k : k, rb, cur, bc, reinterpret_cast<T*>(pk_lds),
+                                                  rs, s_red);
                     done += k;
                 }
                 sweeps += done;
