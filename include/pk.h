@@ -117,6 +117,13 @@ extern "C" {
  * only the visibility of other blocks' writes is no longer guaranteed, so the
  * field is expected to diverge from the oracle. A negative control.          */
 #define PK_DBG_BROKEN_BARRIER 0x1u
+/* Debug only: thread 0 of every block records device wall-clock events (task
+ * begin and end, arrival at and departure from each grid barrier or neighbour
+ * sync, the start of each tile period, wave 0's tagged-halo polls) in a ring of
+ * its own, read with pk_trace_read after the kernel has left: where a task's
+ * time goes, computing or waiting for the slowest block ("Grid-Wide Barriers and
+ * Persistent Work Queues", "What the barrier buys"). Persistent mode only. */
+#define PK_DBG_TRACE 0x2u
 
 /* Grid barrier construction (both are an arrival counter plus a generation
  * word with release/acquire ordering).
@@ -234,6 +241,9 @@ typedef struct pk_info {
     int64_t tasks_carried;   /* PERSISTENT: tasks that started without a poll and a      */
                              /* broadcast barrier: the previous task's barrier carried */
                              /* them (the host had queued them ahead)                   */
+    int wall_clock_khz;      /* rate of the device wall clock that task times and the   */
+                             /* trace count in                                           */
+    int trace_capacity;      /* PK_DBG_TRACE: events each block's ring holds; else 0   */
 } pk_info;
 
 typedef struct pk_engine pk_engine;
@@ -368,6 +378,22 @@ int pk_sweep_noalloc(int dtype, int nx, int ny, int pitch, void* u0, void* u1, c
  * device ("Persistent Kernels", "Sketching out the experiment").
  * Errors: PK_EINVAL (NULL e or info). */
 int pk_get_info(pk_engine* e, pk_info* info);
+
+/* PK_DBG_TRACE engines, once the persistent kernel has left (after PK_EXIT):
+ * copy the device trace into dst. Layout, per block in block order: a uint64
+ * count of the events the block recorded, then trace_capacity records of
+ * {uint64 time (device wall clock, pk_info.wall_clock_khz), uint32 kind,
+ * uint32 aux}; event e sits in record e % trace_capacity, so when count exceeds
+ * the capacity the ring holds the latest events. Kinds: 1 task begin, 2 task end
+ * (aux = task kind), 3 arrival at and 4 departure from a grid barrier (aux 0)
+ * or neighbour sync (aux 1), 5 and 6 wave 0 starts and ends polling tagged halo
+ * words, 7 a tile period starts (aux = its sweeps). *needed (may be NULL)
+ * receives the bytes; dst NULL only asks for them. The measurement behind
+ * "Grid-Wide Barriers and Persistent Work Queues", "What the barrier buys"
+ * (every block waits for the slowest). Errors: PK_ESTATE (no trace, launch
+ * mode), PK_EBUSY (the kernel is still running), PK_EINVAL (bytes too small),
+ * PK_EDEVICE. */
+int pk_trace_read(pk_engine* e, void* dst, size_t bytes, size_t* needed);
 
 /* Stop the kernel (EXIT, bounded wait) and free everything. NULL is a no-op.
  * The kernel leaves only when it reads the EXIT task, so destroy first asks

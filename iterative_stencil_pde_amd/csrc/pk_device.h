@@ -336,7 +336,22 @@ struct BarrierCtx {
     // flight while the task runs
     struct CarryState* carry;
     uint64_t carry_word;
+    // device trace (thread 0's view): this block's ring, or null when off
+    unsigned char* trace;
+    uint64_t tcount;
 };
+
+// Appends one event to the block's trace ring (thread 0 only; a no-op when the
+// trace is off).
+__device__ __forceinline__ void trace_event(BarrierCtx& bc, uint32_t kind, uint32_t aux = 0) {
+    if (!bc.trace || threadIdx.x != 0) return;
+    pk_trace_rec* r = reinterpret_cast<pk_trace_rec*>(bc.trace + 8) + (bc.tcount % PK_TRACE_CAP);
+    r->t = wall_clock64();
+    r->kind = kind;
+    r->aux = aux;
+    bc.tcount += 1;
+    *reinterpret_cast<uint64_t*>(bc.trace) = bc.tcount;
+}
 
 // Task carry state of the leader (block 0, thread 0), in shared memory: the
 // task read ahead once at task start (seq), when (t0), and whether it still
@@ -412,6 +427,7 @@ __device__ __forceinline__ void xcd_barrier(BarrierCtx& bc) {
     if (threadIdx.x == 0) carry_at_barrier(bc);
     wait_vm();
     __syncthreads();
+    trace_event(bc, PK_TR_SYNC_ARRIVE, 0);
     if (threadIdx.x == 0) {
         const uint32_t target = bc.epoch + 1;
         pk_dev_state* st = bc.st;
@@ -434,6 +450,7 @@ __device__ __forceinline__ void xcd_barrier(BarrierCtx& bc) {
         if (!released) spin_until(bc, &st->xgrp_gen[g].v, target);
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
+    trace_event(bc, PK_TR_SYNC_LEAVE, 0);
     bc.epoch += 1;
     __syncthreads();
 }
@@ -448,6 +465,7 @@ __device__ __forceinline__ void neighbor_sync(BarrierCtx& bc, uint32_t* nbr, int
     wait_vm();
     __syncthreads();
     const uint32_t target = bc.nbr_epoch + 1;
+    trace_event(bc, PK_TR_SYNC_ARRIVE, 1);
     if (threadIdx.x == 0 && !bc.faulted) {
         __hip_atomic_store(nbr + static_cast<size_t>(lb) * PK_NBR_WORDS, target, __ATOMIC_RELEASE,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -459,6 +477,7 @@ __device__ __forceinline__ void neighbor_sync(BarrierCtx& bc, uint32_t* nbr, int
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
+    trace_event(bc, PK_TR_SYNC_LEAVE, 1);
     bc.nbr_epoch = target;
     __syncthreads();
 }
@@ -471,6 +490,7 @@ __device__ __forceinline__ void grid_barrier(BarrierCtx& bc, bool relaxed = fals
     }
     if (threadIdx.x == 0 && !relaxed) carry_at_barrier(bc);
     __syncthreads();
+    trace_event(bc, PK_TR_SYNC_ARRIVE, 0);
     if (threadIdx.x == 0 && bc.grid > 1) {
         const uint32_t target = bc.epoch + 1;
         pk_dev_state* st = bc.st;
@@ -503,6 +523,7 @@ __device__ __forceinline__ void grid_barrier(BarrierCtx& bc, bool relaxed = fals
         }
         if (!relaxed) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
+    trace_event(bc, PK_TR_SYNC_LEAVE, 0);
     bc.epoch += 1;
     __syncthreads();
 }

@@ -77,6 +77,7 @@ struct pk_engine {
     uint32_t* d_stamp = nullptr;
     uint32_t* d_nbr = nullptr;
     uint64_t* d_tag = nullptr;  // tagged halo words (PK_EXCHANGE_TAGGED only)
+    unsigned char* d_trace = nullptr;  // PK_DBG_TRACE: grid x PK_TRACE_BLOCK_BYTES
     pk_mailbox* h_mail = nullptr;
     pk_mailbox* d_mail = nullptr;
     void* h_staging = nullptr;
@@ -129,6 +130,7 @@ void release(pk_engine* e) {
     if (e->d_stamp) (void)hipFree(e->d_stamp);
     if (e->d_nbr) (void)hipFree(e->d_nbr);
     if (e->d_tag) (void)hipFree(e->d_tag);
+    if (e->d_trace) (void)hipFree(e->d_trace);
     if (e->h_mail) (void)hipHostFree(e->h_mail);
     if (e->h_staging) (void)hipHostFree(e->h_staging);
     if (e->h_lres) (void)hipHostFree(e->h_lres);
@@ -462,6 +464,7 @@ void fill_kargs(pk_engine* e) {
     a.exchange = p.exchange;
     a.tag = e->d_tag;
     a.tag_pitch = 4 * (e->pitch * e->esize / 16);
+    a.trace = e->d_trace;
 }
 
 bool poll_exited(void* ctx) {
@@ -507,7 +510,8 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     if (o.threads != 0 && (o.threads < 64 || o.threads > 1024 || o.threads % 64 != 0)) return PK_EINVAL;
     if (o.max_blocks < 0 || o.halo_depth < 0 || o.idle_timeout_s < 0) return PK_EINVAL;
     if (o.pass_sweeps < 0 || o.pass_sweeps > PK_MAX_PASS || o.band_rows < 0) return PK_EINVAL;
-    if (o.flags & ~PK_DBG_BROKEN_BARRIER) return PK_EINVAL;
+    if (o.flags & ~(PK_DBG_BROKEN_BARRIER | PK_DBG_TRACE)) return PK_EINVAL;
+    if ((o.flags & PK_DBG_TRACE) && o.mode != PK_PERSISTENT) return PK_EINVAL;
     if (o.barrier < PK_BARRIER_AUTO || o.barrier > PK_BARRIER_XCD) return PK_EINVAL;
     // the negative control relaxes the flat/two-level barriers; the XCD barrier keeps
     // separate counters, so the two are not combined
@@ -602,6 +606,11 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
         const size_t tag_bytes = sizeof(uint64_t) * 2 * static_cast<size_t>(ny) * 4 * (e->pitch * e->esize / 16);
         PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_tag), tag_bytes));
         PK_TRY(hipMemsetAsync(e->d_tag, 0, tag_bytes, e->stream));
+    }
+    if (e->flags & PK_DBG_TRACE) {
+        const size_t tb = static_cast<size_t>(PK_TRACE_BLOCK_BYTES) * e->plan.grid;
+        PK_TRY(hipMalloc(reinterpret_cast<void**>(&e->d_trace), tb));
+        PK_TRY(hipMemsetAsync(e->d_trace, 0, tb, e->stream));
     }
     PK_TRY(hipHostMalloc(reinterpret_cast<void**>(&e->h_mail), sizeof(pk_mailbox),
                          hipHostMallocCoherent | hipHostMallocMapped));
@@ -1006,6 +1015,8 @@ int pk_get_info(pk_engine* e, pk_info* info) {
     info->pass_sweeps = e->plan.pass_sweeps;
     info->exchange = e->plan.exchange;
     info->kernel_launches = e->launches;
+    info->wall_clock_khz = e->wclk_khz;
+    info->trace_capacity = e->d_trace ? PK_TRACE_CAP : 0;
     if (e->mode == PK_PERSISTENT) {
         info->sweeps_done = e->ring.sweeps_seen();
         info->tasks_done = static_cast<int64_t>(e->ring.done_seen());
@@ -1022,6 +1033,20 @@ int pk_get_info(pk_engine* e, pk_info* info) {
         info->kernel_ms = e->last_batch_ms;
     }
     return PK_OK;
+}
+
+int pk_trace_read(pk_engine* e, void* dst, size_t bytes, size_t* needed) {
+    if (!e) return PK_EINVAL;
+    if (!e->d_trace) return PK_ESTATE;
+    const size_t need = static_cast<size_t>(PK_TRACE_BLOCK_BYTES) * e->plan.grid;
+    if (needed) *needed = need;
+    if (!dst) return PK_OK;
+    if (bytes < need) return PK_EINVAL;
+    if (!__atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE)) return PK_EBUSY;
+    if (hipEventSynchronize(e->ev_end) != hipSuccess) return PK_EDEVICE;  // the kernel has drained
+    hipError_t he = hipMemcpyAsync(dst, e->d_trace, need, hipMemcpyDeviceToHost, e->stream);
+    if (he == hipSuccess) he = hipStreamSynchronize(e->stream);
+    return map_err(he);
 }
 
 int pk_destroy(pk_engine* e) {

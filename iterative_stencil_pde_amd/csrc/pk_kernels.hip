@@ -121,6 +121,7 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
     int period = 0;  // the period under way
     while (remaining > 0) {
         const int sc = periods.len(period);
+        trace_event(bc, PK_TR_PERIOD, static_cast<uint32_t>(sc));
         // The rows of sub-sweep s (as in the LDS tile) are [max(1, r0 - (sc - s)),
         // min(ny - 1, r1 + (sc - s))): a row at distance d above the band takes
         // part up to sub-sweep sc - d, the row d below its last row up to
@@ -258,6 +259,7 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                 if ((row >= r0 - above && row < r0) || (row >= r1 && row < r1 + below)) need |= 1u << r;
             }
             if (!wave_live) need = 0;
+            if (wave == 0 && need) trace_event(bc, PK_TR_TAG_WAIT, static_cast<uint32_t>(bc.tag_epoch));
             if (need && !bc.faulted) {
                 // load every halo word of the wave until all carry this exchange's tag
                 // (straight into the rows: their old values are not needed again)
@@ -290,6 +292,7 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                     __builtin_amdgcn_s_sleep(1);
                 }
             }
+            if (wave == 0 && need) trace_event(bc, PK_TR_TAG_DONE, static_cast<uint32_t>(bc.tag_epoch));
             bc.tag_epoch += 1;
             continue;  // the field buffers are untouched until the task's last exchange
         }
@@ -404,6 +407,7 @@ __device__ __forceinline__ void resident_sweep_task(const pk_kargs& a, int n, in
     int remaining = n;
     while (remaining > 0) {
         const int sc = period_len(remaining, m);
+        trace_event(bc, PK_TR_PERIOD, static_cast<uint32_t>(sc));
         for (int s = 1; s <= sc; ++s) {
             // rows of this sub-sweep: the owned band widened by the sub-sweeps
             // still to come, within the interior (a halo deeper than the
@@ -669,6 +673,8 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
     __syncthreads();
     bc.carry = &s_carry;
     bc.carry_word = 0;
+    bc.trace = a.trace ? a.trace + static_cast<size_t>(blockIdx.x) * PK_TRACE_BLOCK_BYTES : nullptr;
+    bc.tcount = 0;
     if (a.barrier_kind == PK_BARRIER_XCD && a.grid > 1 && !bc.broken) {
         // count the blocks on each XCD (one flat barrier, generation 1), then
         // switch to the XCD barrier, whose counters start from zero
@@ -783,6 +789,7 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
                                               __HIP_MEMORY_SCOPE_SYSTEM);
         }
 
+        trace_event(bc, PK_TR_TASK_BEGIN, static_cast<uint32_t>(kind));
         if (s_exit) {
             if (leader) {
                 const uint32_t f = __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -880,6 +887,7 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
         // path, the broadcast barrier of this task, i.e. after every block read
         // carry[(seq - 1) & 1], the same word. A task without a barrier carries
         // nothing, so the next one starts the ordinary way.
+        trace_event(bc, PK_TR_TASK_END, static_cast<uint32_t>(kind));
         if (leader) s_carry.pending = 0;  // never publish it outside its task
         may_carry = !bc.broken && bc.nbar != nbar0;
         if (leader) {

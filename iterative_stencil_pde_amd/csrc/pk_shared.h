@@ -20,6 +20,27 @@
 // Internal task kinds (the public ones are in pk.h); kinds fit in 4 bits.
 #define PK_TASK_READBACK 15
 
+// Device trace (PK_DBG_TRACE): thread 0 of every block appends events to a
+// ring of PK_TRACE_CAP records of its own; the count of events ever written
+// (which may exceed the capacity: the ring then holds the latest) precedes them.
+#define PK_TRACE_CAP 8192
+enum PkTraceKind : uint32_t {
+    PK_TR_TASK_BEGIN = 1,   // aux = task kind
+    PK_TR_TASK_END = 2,     // aux = task kind
+    PK_TR_SYNC_ARRIVE = 3,  // a grid barrier (aux 0) or neighbour sync (aux 1): the block's work is done
+    PK_TR_SYNC_LEAVE = 4,   // every block it waits for has arrived
+    PK_TR_TAG_WAIT = 5,     // wave 0 starts polling its tagged halo words
+    PK_TR_TAG_DONE = 6,     // they all carry the current exchange number
+    PK_TR_PERIOD = 7,       // a tile period (up to halo_depth sub-sweeps) starts; aux = its sweeps
+};
+struct pk_trace_rec {
+    uint64_t t;  // device wall clock
+    uint32_t kind;
+    uint32_t aux;
+};
+// bytes of one block's trace: its event count, then its ring
+#define PK_TRACE_BLOCK_BYTES (8u + PK_TRACE_CAP * 16u)
+
 // Device fault codes (pk_dev_state::fault).
 #define PK_FAULT_BARRIER_TIMEOUT 1u
 #define PK_FAULT_IDLE_TIMEOUT 2u
@@ -151,4 +172,5 @@ struct pk_kargs {
     uint64_t* tag;         // tagged halo words: 2 parities x ny rows x tag_pitch words
     int tag_pitch;         // words per row: 4 planes of one word per 16-byte vector
     uint64_t tag_ticks;    // longest wait for a tagged halo word (device clock ticks)
+    unsigned char* trace;  // PK_DBG_TRACE: grid x PK_TRACE_BLOCK_BYTES, or null
 };

@@ -28,7 +28,7 @@ PK_PERSISTENT, PK_LAUNCH = 0, 1
 PK_LAYOUT_AUTO, PK_LAYOUT_STREAM, PK_LAYOUT_RESIDENT, PK_LAYOUT_REGISTER = 0, 1, 2, 3
 PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP, PK_SWEEP_RB, PK_SWEEP_UNTIL = 1, 2, 3, 4, 5, 6, 7
 PK_BLOCKSYNC = 8
-PK_DBG_BROKEN_BARRIER = 0x1
+PK_DBG_BROKEN_BARRIER, PK_DBG_TRACE = 0x1, 0x2
 PK_TASK_N_MAX = 0x0FFFFFFF
 PK_MAX_PASS = 8  # deepest streaming pass (sweeps kept on chip), the planner's default
 PK_BARRIER_AUTO, PK_BARRIER_FLAT, PK_BARRIER_TWO_LEVEL, PK_BARRIER_XCD = 0, 1, 2, 3
@@ -36,7 +36,7 @@ PK_EXCHANGE_AUTO, PK_EXCHANGE_BARRIER, PK_EXCHANGE_NEIGHBOR, PK_EXCHANGE_TAGGED 
 
 EXPORTED = ["pk_opts_default", "pk_create", "pk_submit", "pk_submit_until", "pk_wait", "pk_readback",
             "pk_run_launch_per_iter", "pk_run_graph_per_iter", "pk_get_info", "pk_destroy",
-            "pk_strerror", "pk_sweep_noalloc"]
+            "pk_strerror", "pk_sweep_noalloc", "pk_trace_read"]
 PK_NOALLOC_MAX_BLOCKS = 1024
 
 
@@ -70,7 +70,8 @@ class pk_info(ctypes.Structure):
                 ("exchange", ctypes.c_int), ("lds_bytes", ctypes.c_size_t),
                 ("kernel_ms", ctypes.c_double), ("sweeps_done", ctypes.c_int64),
                 ("tasks_done", ctypes.c_int64), ("kernel_launches", ctypes.c_int64),
-                ("tasks_carried", ctypes.c_int64)]
+                ("tasks_carried", ctypes.c_int64), ("wall_clock_khz", ctypes.c_int),
+                ("trace_capacity", ctypes.c_int)]
 
 
 class PkError(RuntimeError):
@@ -113,6 +114,8 @@ def load(path: str = LIB_PATH):
     lib.pk_destroy.argtypes = [vp]
     lib.pk_strerror.restype = ctypes.c_char_p
     lib.pk_strerror.argtypes = [ip]
+    lib.pk_trace_read.restype = ip
+    lib.pk_trace_read.argtypes = [vp, vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
     lib.pk_sweep_noalloc.restype = ip
     lib.pk_sweep_noalloc.argtypes = [ip, ip, ip, ip, vp, vp, vp, ip, vp, vp]
     _lib = lib
@@ -227,6 +230,16 @@ def pk_sweep_noalloc(dtype: int, nx: int, ny: int, pitch: int, u0: int, u1: int,
     return load().pk_sweep_noalloc(dtype, nx, ny, pitch, u0, u1, b, n, residual, stream)
 
 
+def pk_trace_read(eng: int) -> bytes:
+    """The device trace of a PK_DBG_TRACE engine whose kernel has left (raw bytes;
+    ``iterative_stencil_pde_amd.trace`` decodes them)."""
+    need = ctypes.c_size_t()
+    _check(load().pk_trace_read(eng, None, 0, ctypes.byref(need)), "pk_trace_read")
+    buf = ctypes.create_string_buffer(need.value)
+    _check(load().pk_trace_read(eng, buf, need.value, None), "pk_trace_read")
+    return buf.raw
+
+
 class Engine:
     """Owning wrapper: ``with Engine(bc, f, mode=...) as e: e.sweep(100); ...``."""
 
@@ -256,6 +269,9 @@ class Engine:
 
     def residual(self) -> float:
         return self.run(PK_RESIDUAL).residual
+
+    def trace(self) -> bytes:
+        return pk_trace_read(self.h)
 
     def readback(self) -> np.ndarray:
         out = np.empty(self.shape, dtype=self.dtype)

@@ -188,3 +188,52 @@ def test_auto_plan(name):
         f"exchange={info.exchange} k={info.pass_sweeps}")
     for key, want in AUTO_PLANS[name].items():
         assert getattr(info, key) == want, (key, getattr(info, key), want)
+
+
+@pytest.mark.parametrize("name,layout", [("laplace1024", pk.PK_LAYOUT_STREAM), ("poisson256", pk.PK_LAYOUT_AUTO)])
+def test_device_trace(name, layout):
+    """PK_DBG_TRACE: every block records its tasks and each synchronization it takes
+    part in; the field is unchanged by tracing; the trace is readable only after
+    the kernel has left."""
+    from iterative_stencil_pde_amd import trace
+    w = inputs.make(name)
+    with pk.Engine(w.u0, w.f, h=w.h, layout=layout, flags=pk.PK_DBG_TRACE) as e:
+        info = e.info()
+        assert info.trace_capacity > 0 and info.wall_clock_khz > 0
+        e.sweep(40)
+        with pytest.raises(pk.PkError) as ex:
+            e.trace()
+        assert ex.value.status == pk.PK_EBUSY
+        got = e.readback()
+        e.wait(e.submit(pk.PK_EXIT))
+        raw = e.trace()
+    ref, _ = oracle.jacobi(w.u0, 40, f=w.f, h=w.h)
+    assert np.array_equal(got, ref)
+    blocks = trace.decode(raw, info.grid_blocks, info.trace_capacity)
+    assert len(blocks) == info.grid_blocks
+    for ev in blocks:
+        kinds = [int(k) for k in ev["kind"]]
+        t = np.asarray(ev["t"], dtype=np.int64)
+        assert np.all(np.diff(t) >= 0)  # one block's clock never runs back
+        assert kinds.count(trace.TASK_BEGIN) == kinds.count(trace.TASK_END) + 1  # EXIT has no end
+        assert kinds.count(trace.SYNC_ARRIVE) == kinds.count(trace.SYNC_LEAVE)
+    counts = {len(ev) for ev in blocks}
+    syncs = {[int(k) for k in ev["kind"]].count(trace.SYNC_ARRIVE) for ev in blocks}
+    assert len(syncs) == 1  # every block takes part in every synchronization
+    if info.layout == pk.PK_LAYOUT_STREAM:
+        # per pass one grid barrier (40 sweeps in passes of k), plus the task broadcasts
+        passes = -(-40 // info.pass_sweeps)
+        assert syncs.pop() >= passes
+    s = trace.summarize(raw, info.grid_blocks, info.trace_capacity, info.wall_clock_khz)
+    say(f"  {name}: layout={info.layout} events/block={sorted(counts)[:3]} work={s['work'].get('mean')} "
+        f"wait={s['sync_wait'].get('mean')} tag={s['tag_wait'].get('mean')} period={s['period'].get('mean')}")
+    assert s["work"]["count"] > 0
+
+
+def test_trace_needs_the_flag():
+    w = inputs.laplace_harmonic(64, 0)
+    with pk.Engine(w.u0, None) as e:
+        e.sweep(2)
+        with pytest.raises(pk.PkError) as ex:
+            e.trace()
+        assert ex.value.status == pk.PK_ESTATE
