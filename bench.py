@@ -43,7 +43,8 @@ sys.path.insert(0, ROOT)
 from iterative_stencil_pde_amd import inputs, pk  # noqa: E402
 
 PROFILES = os.path.join(ROOT, "profiles")
-DEVICE_SOURCES = ["pk_device.h", "pk_kernels.hip", "pk_shared.h"]
+DEVICE_SOURCES = ["pk_device.h", "pk_persistent.h", "pk_kernels.hip", "pk_kern_stream.hip", "pk_kern_resident.hip",
+                  "pk_kern_register_f32.hip", "pk_kern_register_f64.hip", "pk_shared.h"]
 METRIC = ("µs/iteration + Gcell-updates/s (persistent vs per-launch); "
           "HBM GB/s % of peak")
 HBM_PEAK_GBS = 8000.0

@@ -324,9 +324,9 @@ struct BarrierCtx {
     bool two_level;      // per-XCD-group counters under a top counter
     bool xcd;            // groups by hardware XCD, cache maintenance once per XCD
     bool faulted;        // thread 0's view; broadcast at task boundaries
-    uint32_t xg;         // XCD barrier: this block's XCD
-    uint32_t xmembers;   // XCD barrier: blocks on this XCD
-    uint32_t xgroups;    // XCD barrier: XCDs with at least one block
+    // XCD barrier: thread 0's view of its groups, in the block's shared memory
+    // (values live across every task would otherwise hold vector registers)
+    struct XcdState* xs;
     uint32_t nbr_epoch;  // neighbour exchanges completed (identical in every block)
     uint64_t tag_epoch;  // tagged exchanges completed (identical in every block)
     uint32_t nbar;       // grid barriers passed (identical in every block)
@@ -336,21 +336,39 @@ struct BarrierCtx {
     // flight while the task runs
     struct CarryState* carry;
     uint64_t carry_word;
-    // device trace (thread 0's view): this block's ring, or null when off
-    unsigned char* trace;
-    uint64_t tcount;
+    // device trace (thread 0's view), in the block's shared memory: the state
+    // is touched only when an event is recorded, so it takes no registers
+    struct TraceState* trace;
+};
+
+// XCD barrier groups as thread 0 sees them: this block's XCD, the blocks on it,
+// and the XCDs with at least one block.
+struct XcdState {
+    uint32_t g;
+    uint32_t members;
+    uint32_t groups;
+};
+
+// This block's trace ring (null when the trace is off) and its event count.
+struct TraceState {
+    unsigned char* ring;
+    uint64_t count;
 };
 
 // Appends one event to the block's trace ring (thread 0 only; a no-op when the
 // trace is off).
 __device__ __forceinline__ void trace_event(BarrierCtx& bc, uint32_t kind, uint32_t aux = 0) {
-    if (!bc.trace || threadIdx.x != 0) return;
-    pk_trace_rec* r = reinterpret_cast<pk_trace_rec*>(bc.trace + 8) + (bc.tcount % PK_TRACE_CAP);
+    if (threadIdx.x != 0) return;
+    TraceState* ts = bc.trace;
+    if (!ts->ring) return;
+    // field by field: merged into one 16-byte store, the record's registers were
+    // kept (and spilled) across the tile loops
+    volatile pk_trace_rec* r = reinterpret_cast<pk_trace_rec*>(ts->ring + 8) + (ts->count % PK_TRACE_CAP);
     r->t = wall_clock64();
     r->kind = kind;
     r->aux = aux;
-    bc.tcount += 1;
-    *reinterpret_cast<uint64_t*>(bc.trace) = bc.tcount;
+    ts->count += 1;
+    *reinterpret_cast<volatile uint64_t*>(ts->ring) = ts->count;
 }
 
 // Task carry state of the leader (block 0, thread 0), in shared memory: the
@@ -361,6 +379,7 @@ struct CarryState {
     uint64_t t0;
     uint64_t age;
     int pending;
+    uint64_t t_task;  // start of the task under way (its done record's t_begin)
 };
 
 // Leader only, before it arrives at an ordered grid barrier: if the task read
@@ -431,15 +450,15 @@ __device__ __forceinline__ void xcd_barrier(BarrierCtx& bc) {
     if (threadIdx.x == 0) {
         const uint32_t target = bc.epoch + 1;
         pk_dev_state* st = bc.st;
-        const uint32_t g = bc.xg;
+        const uint32_t g = bc.xs->g;
         const uint32_t old = __hip_atomic_fetch_add(&st->xgrp_count[g].v, 1u, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         bool released = false;
-        if (old == target * bc.xmembers - 1u) {
+        if (old == target * bc.xs->members - 1u) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
             const uint32_t old2 = __hip_atomic_fetch_add(&st->xtop_count, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
-            if (old2 == target * bc.xgroups - 1u) {
+            if (old2 == target * bc.xs->groups - 1u) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
                 for (uint32_t k = 0; k < 8; ++k)
                     __hip_atomic_store(&st->xgrp_gen[k].v, target, __ATOMIC_RELAXED,
@@ -536,6 +555,16 @@ __device__ __forceinline__ void grid_barrier(BarrierCtx& bc, bool relaxed = fals
 // driven by it into vector registers under exec masks.
 __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+}
+
+// threadIdx.x as a value the compiler must read afresh where it is used: the
+// per-lane addresses of the rarely run tasks (readback, stamp rounds) are then
+// formed inside those tasks, not hoisted out of the task loop and kept, or
+// spilled, across every other task.
+__device__ __forceinline__ int thread_id_here() {
+    int t = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(t));
+    return t;
 }
 
 __device__ __forceinline__ int logical_block(int remap, int grid) {

@@ -364,7 +364,7 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         // budget allows (its passes keep up to 8 levels of the march in registers)
         if (e->mode == PK_PERSISTENT) {
             hipFuncAttributes fa{};
-            if (hipFuncGetAttributes(&fa, pkk_persistent_fn(e->dtype, e->has_b, PK_LAYOUT_STREAM)) != hipSuccess)
+            if (hipFuncGetAttributes(&fa, pkk_persistent_fn(e->dtype, e->has_b, PK_LAYOUT_STREAM, 0, false)) != hipSuccess)
                 return PK_EDEVICE;
             p.threads = std::min(p.threads, fa.maxThreadsPerBlock / 64 * 64);
         }
@@ -404,7 +404,7 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     }
 
     // occupancy of the kernel that will be resident, at its LDS footprint
-    const void* fn = e->mode == PK_PERSISTENT ? pkk_persistent_fn(e->dtype, e->has_b, p.layout)
+    const void* fn = e->mode == PK_PERSISTENT ? pkk_persistent_fn(e->dtype, e->has_b, p.layout, p.reg_rows, (e->flags & PK_DBG_TRACE) != 0)
                                               : pkk_sweep_fn(e->dtype, e->has_b);
     if (p.lds_bytes > 0)
         (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -646,7 +646,8 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     e->ring.attach(e->h_mail);
 
     if (e->mode == PK_PERSISTENT) {
-        const void* fn = pkk_persistent_fn(e->dtype, e->has_b, e->plan.layout);
+        const void* fn = pkk_persistent_fn(e->dtype, e->has_b, e->plan.layout, e->plan.reg_rows,
+                                           (e->flags & PK_DBG_TRACE) != 0);
         void* args[] = {&e->ka};
         PK_TRY(hipEventRecord(e->ev_start, e->stream));
         he = hipLaunchCooperativeKernel(fn, dim3(e->plan.grid), dim3(e->plan.threads), args,

@@ -5,8 +5,15 @@
 
 #include "pk_shared.h"
 
-// Kernel symbol of the persistent kernel for an element type / source / layout.
-const void* pkk_persistent_fn(int dtype, bool has_b, int layout);
+// Kernel symbol of the persistent kernel for an element type / source / layout;
+// rows: rows per wave of the register layout (2 or 4, else ignored); trace: the
+// instance with the tile layouts' in-loop events (PK_DBG_TRACE).
+const void* pkk_persistent_fn(int dtype, bool has_b, int layout, int rows, bool trace);
+// The same, per layout (one translation unit each).
+const void* pkk_stream_fn(int dtype, bool has_b);
+const void* pkk_resident_fn(int dtype, bool has_b, bool trace);
+const void* pkk_register_fn_f32(bool has_b, int rows, bool trace);
+const void* pkk_register_fn_f64(bool has_b, int rows, bool trace);
 // Kernel symbol of the one-sweep kernel (for the occupancy query).
 const void* pkk_sweep_fn(int dtype, bool has_b);
 

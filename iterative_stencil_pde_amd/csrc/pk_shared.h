@@ -109,26 +109,30 @@ struct alignas(PK_LINE) pk_carry {
 };
 
 struct pk_dev_state {
-    alignas(PK_LINE) uint32_t bar_count;   // arrivals, monotonically increasing
-    alignas(PK_LINE) uint32_t bar_gen;     // completed barrier generations
-    // two-level barrier: one arrival counter and one generation word per XCD
-    // group (block b belongs to group b mod 8), and a top-level counter
-    pk_word256 grp_count[8];
-    pk_word256 grp_gen[8];
-    alignas(256) uint32_t top_count;
-    // XCD barrier: groups are the XCDs the blocks actually run on (hardware
-    // XCC id), with one L2 write-back and one L2 invalidate per XCD
-    pk_word256 xmembers[8];
-    pk_word256 xgrp_count[8];
-    pk_word256 xgrp_gen[8];
-    alignas(256) uint32_t xtop_count;
-    alignas(256) uint32_t xtop_gen;
+    // The words every task touches come first, within the 4 KiB that a global
+    // instruction reaches from a scalar base with its immediate offset: no
+    // per-word 64-bit address has to be kept in vector registers.
     alignas(PK_LINE) uint64_t task_seq;    // task broadcast (written by the leader)
     int32_t task_kind;
     int32_t task_n;
     pk_carry carry[2];
     alignas(PK_LINE) uint32_t fault;       // device-side fault, read by every block
     alignas(PK_LINE) uint64_t stamp_errors;
+    alignas(PK_LINE) uint32_t bar_count;   // arrivals, monotonically increasing
+    alignas(PK_LINE) uint32_t bar_gen;     // completed barrier generations
+    alignas(256) uint32_t top_count;
+    alignas(256) uint32_t xtop_count;
+    alignas(256) uint32_t xtop_gen;
+    // two-level barrier: one arrival counter and one generation word per XCD
+    // group (block b belongs to group b mod 8), and the top-level counter above
+    pk_word256 grp_count[8];
+    pk_word256 grp_gen[8];
+    // XCD barrier: groups are the XCDs the blocks actually run on (hardware
+    // XCC id), with one L2 write-back and one L2 invalidate per XCD, and the
+    // top-level counter and generation above
+    pk_word256 xmembers[8];
+    pk_word256 xgrp_count[8];
+    pk_word256 xgrp_gen[8];
 };
 
 // Kernel arguments (passed by value).
