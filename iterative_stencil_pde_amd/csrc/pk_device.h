@@ -289,6 +289,26 @@ __device__ __forceinline__ double rho2(const Vec<T>& s, const Vec<T>& m, const V
     return acc;
 }
 
+// A store kept on its own: a relaxed atomic store is neither merged with the
+// stores beside it into one wide store (whose register tuple the compiler then
+// keeps live, and spills, across the task loop) nor made to wait for its own
+// completion, as a volatile store is. For records written field by field by one
+// thread (task completions, trace events); what orders them is the release
+// that publishes the record.
+template <typename V>
+struct Same {
+    using type = V;
+};
+template <typename V>
+__device__ __forceinline__ void put(V* p, typename Same<V>::type v, int scope = __HIP_MEMORY_SCOPE_SYSTEM) {
+    if constexpr (sizeof(V) == 8)
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                           scope);
+    else
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                           scope);
+}
+
 // ---------------------------------------------------------------------------
 // Grid-wide barrier: an arrival counter plus a generation word
 // ("Grid-Wide Barriers and Persistent Work Queues", "The barrier is a counter
@@ -361,14 +381,14 @@ __device__ __forceinline__ void trace_event(BarrierCtx& bc, uint32_t kind, uint3
     if (threadIdx.x != 0) return;
     TraceState* ts = bc.trace;
     if (!ts->ring) return;
-    // field by field: merged into one 16-byte store, the record's registers were
-    // kept (and spilled) across the tile loops
-    volatile pk_trace_rec* r = reinterpret_cast<pk_trace_rec*>(ts->ring + 8) + (ts->count % PK_TRACE_CAP);
-    r->t = wall_clock64();
-    r->kind = kind;
-    r->aux = aux;
+    // field by field (put): merged into one 16-byte store, the record's registers
+    // were kept, and spilled, across the tile loops
+    pk_trace_rec* r = reinterpret_cast<pk_trace_rec*>(ts->ring + 8) + (ts->count % PK_TRACE_CAP);
+    put(&r->t, wall_clock64(), __HIP_MEMORY_SCOPE_AGENT);
+    put(&r->kind, kind, __HIP_MEMORY_SCOPE_AGENT);
+    put(&r->aux, aux, __HIP_MEMORY_SCOPE_AGENT);
     ts->count += 1;
-    *reinterpret_cast<volatile uint64_t*>(ts->ring) = ts->count;
+    put(reinterpret_cast<uint64_t*>(ts->ring), ts->count, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Task carry state of the leader (block 0, thread 0), in shared memory: the

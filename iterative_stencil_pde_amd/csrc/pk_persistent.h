@@ -538,6 +538,23 @@ __device__ __forceinline__ int64_t stamp_task(const pk_kargs& a, int n, uint32_t
     return total;
 }
 
+// A task's completion record, field by field (the leader only; the release
+// store of done_seq that follows publishes it to the host).
+__device__ __forceinline__ void write_done(pk_done_rec* d, uint64_t seq, int kind, int status, double residual,
+                                           int64_t sweeps, uint64_t t_begin, uint64_t t_end, int64_t errors,
+                                           int cur, int carried) {
+    put(&d->kind, kind);
+    put(&d->status, status);
+    put(&d->residual, residual);
+    put(&d->sweeps_done, sweeps);
+    put(&d->t_begin, t_begin);
+    put(&d->t_end, t_end);
+    put(&d->errors, errors);
+    put(&d->cur, cur);
+    put(&d->carried, carried);
+    put(&d->seq, seq);
+}
+
 // ---------------------------------------------------------------------------
 // The persistent kernel: launched once, loops over host tasks until EXIT.
 // Block 0 lane 0 is the only thread that touches the host mailbox: it polls
@@ -808,17 +825,8 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
                 const uint32_t f = __hip_atomic_load(&a.st->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const uint32_t code = (f != 0) ? f : (bc.faulted ? PK_FAULT_BARRIER_TIMEOUT : 0u);
                 if (kind == PK_EXIT && code == 0) {
-                    volatile pk_done_rec* d = &mail->done[seq % PK_RING];
-                    d->kind = PK_EXIT;
-                    d->status = PK_OK;
-                    d->residual = 0.0;
-                    d->sweeps_done = sweeps;
-                    d->t_begin = s_carry.t_task;
-                    d->t_end = s_carry.t_task;
-                    d->errors = 0;
-                    d->cur = cur;
-                    d->carried = s_carried;
-                    d->seq = seq;
+                    write_done(&mail->done[seq % PK_RING], seq, PK_EXIT, PK_OK, 0.0, sweeps, s_carry.t_task,
+                               s_carry.t_task, 0, cur, s_carried);
                     __hip_atomic_store(&mail->done_seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
                 }
                 __hip_atomic_store(&mail->fault, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -904,17 +912,8 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
         if (leader) s_carry.pending = 0;  // never publish it outside its task
         may_carry = !bc.broken && bc.nbar != nbar0;
         if (leader) {
-            volatile pk_done_rec* d = &mail->done[seq % PK_RING];
-            d->kind = kind;
-            d->status = bc.faulted ? PK_EDEVICE : status;
-            d->residual = res;
-            d->sweeps_done = sweeps;
-            d->t_begin = s_carry.t_task;
-            d->t_end = wall_clock64();
-            d->errors = errs;
-            d->cur = cur;
-            d->carried = s_carried;
-            d->seq = seq;
+            write_done(&mail->done[seq % PK_RING], seq, kind, bc.faulted ? PK_EDEVICE : status, res, sweeps,
+                       s_carry.t_task, wall_clock64(), errs, cur, s_carried);
             __hip_atomic_store(&mail->done_seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
         }
         next_seq = seq + 1;
