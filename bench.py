@@ -43,8 +43,9 @@ sys.path.insert(0, ROOT)
 from iterative_stencil_pde_amd import inputs, pk  # noqa: E402
 
 PROFILES = os.path.join(ROOT, "profiles")
-DEVICE_SOURCES = ["pk_device.h", "pk_persistent.h", "pk_kernels.hip", "pk_kern_stream.hip", "pk_kern_resident.hip",
-                  "pk_kern_register_f32.hip", "pk_kern_register_f64.hip", "pk_shared.h"]
+DEVICE_SOURCES = ["pk_device.h", "pk_persistent.h", "pk_kernels.hip", "pk_kern_stream_f32.hip",
+                  "pk_kern_stream_f64.hip", "pk_kern_resident.hip", "pk_kern_register_f32.hip",
+                  "pk_kern_register_f64.hip", "pk_shared.h"]
 METRIC = ("µs/iteration + Gcell-updates/s (persistent vs per-launch); "
           "HBM GB/s % of peak")
 HBM_PEAK_GBS = 8000.0
@@ -195,17 +196,53 @@ def per_unit_bytes(w):
             w.interior_cells * es * (1 + (1 if has_b else 0)))
 
 
+SHALLOW_PASS = 8  # the deepest pass that also sums the residual, and red-black passes
+
+
+def pass_depths(n, depth, rb=False):
+    """The passes a streaming task of n sweeps (red-black: half-sweeps) runs at the
+    engine's depth, as the kernel splits it: depth-deep passes, a depth it does not
+    carry (9..11) as 8, and a last Jacobi pass of at most 8 (it also sums the
+    residual: a 12-sweep tail runs as 4 + 8)."""
+    out = []
+    while n > 0:
+        k = min(depth, n)
+        if k > SHALLOW_PASS and (rb or k != pk.PK_MAX_PASS):
+            k = SHALLOW_PASS
+        if k == n and k > SHALLOW_PASS:
+            k = n - SHALLOW_PASS
+        out.append(k)
+        n -= k
+    return out
+
+
+def default_depth(w):
+    """The planner's pass depth: 12 where the streamed arrays (u, u', b) exceed the
+    256 MiB Infinity Cache, else 8."""
+    es = np.dtype(w.dtype).itemsize
+    pitch_bytes = -(-w.nx * es // 256) * 256
+    streamed = pitch_bytes * w.ny * (3 if w.f is not None else 2)
+    return pk.PK_MAX_PASS if streamed > MALL_BYTES else SHALLOW_PASS
+
+
 def script_counts(w, pass_sweeps):
-    """(sweeps, passes, residuals) of one step: a SWEEP task of n sweeps runs in
-    ceil(n / k) passes of at most k sweeps (k = 1: one pass per sweep)."""
+    """(sweeps, passes, residual reads) of one step of a persistent streaming
+    engine: each SWEEP task runs the passes of pass_depths (k = 1: one pass per
+    sweep); a RESIDUAL right after a Jacobi SWEEP task of n > 0 sweeps reads
+    nothing (its partials were summed by that task's last pass), any other reads
+    u and b."""
     sweeps = passes = residuals = 0
+    fused = False
     for s in step_tasks(w):
         if s[0] == "residual":
-            residuals += 1
+            residuals += 0 if fused else 1
+            fused = False
         else:
-            n = s[1] * (2 if s[0] == "sweep_rb" else 1)  # red-black: two half-sweeps
+            rb = s[0] == "sweep_rb"
+            n = s[1] * (2 if rb else 1)  # red-black: two half-sweeps
             sweeps += s[1]
-            passes += -(-n // max(1, pass_sweeps))
+            passes += len(pass_depths(n, max(1, pass_sweeps), rb))
+            fused = not rb and n > 0 and pass_sweeps > 1
     return sweeps, passes, residuals
 
 
@@ -337,7 +374,8 @@ def roofline_stream(w, r, steps, warmup, traffic_key):
         "kernel_ms": round(end.kernel_ms, 3),
         "launches": 1,
         "pass_sweeps": k,
-        "algorithmic_unit": "one pass of k sweeps: u read and written once, b read once; a residual reads u and b",
+        "algorithmic_unit": "one pass of up to k sweeps: u read and written once, b read once; a residual "
+                            "not summed by the pass before it reads u and b",
         "algorithmic_bytes_per_launch": launch_alg,
         "counter_GBps": round(traffic / kernel_s / 1e9, 2) if traffic else None,
         "counter_frac": round(traffic / kernel_s / 1e9 / HBM_PEAK_GBS, 4) if traffic else None,
@@ -523,7 +561,7 @@ def main():
     if args.fold_traffic:
         # the launch of a --main-only run of a streaming workload: its algorithmic
         # bytes with the passes it ran (the planner's default depth unless given)
-        k = args.pass_sweeps or pk.PK_MAX_PASS
+        k = args.pass_sweeps or default_depth(w)
         per_step = algorithmic_bytes(w, k)[1]
         pure = algorithmic_bytes(sweeps_only(w), k)[1]
         fold_traffic(args.fold_traffic[0], args.fold_traffic[1], traffic_key,

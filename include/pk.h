@@ -192,10 +192,13 @@ typedef struct pk_opts {
     double idle_timeout_s; /* the persistent kernel leaves by itself after this     */
                            /* long without a task; 0 => 120 s                       */
     int barrier;           /* PK_BARRIER_*                                           */
-    int pass_sweeps;       /* STREAM: sweeps per pass, 1..8: each wave carries k     */
-                           /* levels of its band in registers, so the field crosses */
-                           /* HBM and the grid barrier once per k sweeps; 0 = 8    */
-                           /* (pk_info reports it)                                  */
+    int pass_sweeps;       /* STREAM: sweeps per pass, 1..8 or 12 (else            */
+                           /* PK_EINVAL): each wave carries k levels of its band in */
+                           /* registers, so the field crosses HBM and the grid      */
+                           /* barrier once per k sweeps; 0 = 12 where u, u' and b   */
+                           /* exceed the 256 MiB Infinity Cache, else 8 (pk_info    */
+                           /* reports it). A task's last pass is at most 8 deep     */
+                           /* (12 -> 4 + 8), as are red-black passes                */
     int band_rows;         /* STREAM passes: rows per band (a unit is a band x one  */
                            /* strip, one per wave); 0 = automatic                   */
     int exchange;          /* RESIDENT, REGISTER: PK_EXCHANGE_*                      */

@@ -33,8 +33,8 @@ HIP_FLAGS = [
 
 # the device code: launch-per-sweep and setup kernels, and the persistent kernel's
 # instances, one translation unit per layout (compiled in parallel)
-DEVICE_SOURCES = ["pk_kernels.hip", "pk_kern_stream.hip", "pk_kern_resident.hip",
-                  "pk_kern_register_f32.hip", "pk_kern_register_f64.hip"]
+DEVICE_SOURCES = ["pk_kernels.hip", "pk_kern_stream_f32.hip", "pk_kern_stream_f64.hip",
+                  "pk_kern_resident.hip", "pk_kern_register_f32.hip", "pk_kern_register_f64.hip"]
 SOURCES = [*DEVICE_SOURCES, "pk_host.cpp"]
 # the compiler's per-kernel resource report of the last build (VGPRs, SGPRs,
 # scratch bytes per lane), with a hash of the sources it was made from

@@ -862,7 +862,7 @@ __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T*
     constexpr int W = VecW<T>::W;
     constexpr int L = K + (RES ? 1 : 0);  // levels of the march (the last one rho with RES)
     constexpr int CH = (HAS_B || L >= 3) ? 2 : 4;  // rows per chunk
-    constexpr bool DEFER = HAS_B || sizeof(T) == 8;
+    constexpr bool DEFER = sizeof(T) == 8 || (HAS_B && L <= PK_SHALLOW_PASS + 1);
     constexpr bool COLS = MODE != PASS_INNER;
     static_assert((2 * L) % CH == 0, "the first 2L steps are whole chunks");
     const int lane = threadIdx.x & 63;
@@ -1004,7 +1004,7 @@ __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T*
     return acc;
 }
 
-// One pass of k sweeps (1 <= k <= PK_MAX_PASS) over all units, src -> dst.
+// One pass of k sweeps (a depth PK_PASS_DEPTH_OK accepts) over all units, src -> dst.
 // h0 >= 0: the k levels are red-black half-sweeps, level j of colour (h0+j-1) mod 2.
 // RES: also this lane's rho^2 of the result (returned; 0 otherwise).
 template <typename T, bool HAS_B, int K, bool RB, bool RES>
@@ -1036,9 +1036,9 @@ __device__ __forceinline__ double stream_pass_k(const pk_kargs& a, const T* __re
         const bool cols = c0 < 1 || c0 + 64 * W > a.nx - 1;
         const int nx = a.nx, ny = a.ny, pt = a.pitch;
         // red-black passes, the last pass of a task (RES) and passes of fewer than
-        // PK_MAX_PASS sweeps (a task's passes are all PK_MAX_PASS deep but its
-        // last) take the checked march
-        if constexpr (RB || RES || K != PK_MAX_PASS) {
+        // PK_SHALLOW_PASS sweeps (a task's passes are all as deep as the engine's
+        // depth but its last one or two) take the checked march
+        if constexpr (RB || RES || K < PK_SHALLOW_PASS) {
             if (dir > 0) acc += stream_pass_unit<T, HAS_B, K, 1, RB, PASS_CHECKED, RES>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
             else acc += stream_pass_unit<T, HAS_B, K, -1, RB, PASS_CHECKED, RES>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
         } else if (rows_late) {
@@ -1095,6 +1095,7 @@ __device__ __forceinline__ double stream_pass(const pk_kargs& a, const T* __rest
         case 6: stream_pass_k<T, HAS_B, 6, false, false>(a, src, dst, h0); break;
         case 7: stream_pass_k<T, HAS_B, 7, false, false>(a, src, dst, h0); break;
         case 8: stream_pass_k<T, HAS_B, 8, false, false>(a, src, dst, h0); break;
+        case PK_MAX_PASS: stream_pass_k<T, HAS_B, PK_MAX_PASS, false, false>(a, src, dst, h0); break;
         default: stream_sweep<T, HAS_B>(a, src, dst, -1); break;
     }
     return 0.0;

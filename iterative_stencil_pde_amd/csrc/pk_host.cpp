@@ -186,6 +186,7 @@ double exchange_estimate_us(int exchange, int g, double kb, int dist, bool regis
 
 constexpr int kRegRows = 4;  // rows per wave held in registers (PK_REG_RMAX)
 constexpr int kMaxHalo = 64;  // deepest LDS-tile halo the planner considers
+constexpr uint64_t kInfinityCacheBytes = 256ull << 20;  // the MI355X's last-level cache
 
 // One candidate block count g for the LDS (register == false) or register tile.
 // `exchanges` lists the exchange kinds to consider (LDS tile only).
@@ -382,11 +383,19 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
                         : (p.grid >= 16 ? PK_BARRIER_TWO_LEVEL : PK_BARRIER_FLAT));
     stream_geometry(p, e->nx, e->ny, e->esize, 4);
     // passes of k sweeps (stream layout, persistent only): about one unit per
-    // wave, bands at least 4 k rows tall (each band re-reads 2 k halo rows)
-    // default: the deepest pass the kernel carries (8 levels)
+    // wave, bands at least 4 k rows tall (each band re-reads 2 k halo rows).
+    // Default depth: a deeper pass reads and writes the field fewer times per
+    // sweep but recomputes more overlap rows and columns, so it pays where the
+    // pass is bound by memory traffic, i.e. where the arrays it streams (u, u'
+    // and b) do not fit the 256 MiB Infinity Cache (8192^2 fp64 Poisson: 41.7 us
+    // per sweep at 8, 31.9 at 12); where they fit, the pass is bound by vector
+    // issue and 8 is fastest (4096^2 fp32: 4.54 us at 8, 5.28 at 12).
     p.pass_sweeps = 1;
-    if (e->mode == PK_PERSISTENT && p.layout == PK_LAYOUT_STREAM)
-        p.pass_sweeps = o.pass_sweeps > 0 ? o.pass_sweeps : PK_MAX_PASS;
+    if (e->mode == PK_PERSISTENT && p.layout == PK_LAYOUT_STREAM) {
+        const uint64_t streamed = static_cast<uint64_t>(e->pitch_bytes) * e->ny * (e->has_b ? 3 : 2);
+        const int depth = streamed > kInfinityCacheBytes ? PK_MAX_PASS : PK_SHALLOW_PASS;
+        p.pass_sweeps = o.pass_sweeps > 0 ? o.pass_sweeps : depth;
+    }
     {
         const int k = p.pass_sweeps;
         const int ov = (k + W - 1) / W;
@@ -395,11 +404,12 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         int bands = std::max(1, nw / strips_k);
         bands = std::min(bands, std::max(1, interior / (4 * k)));
         p.pband_rows = o.band_rows > 0 ? std::min(o.band_rows, interior) : ceil_div(interior, bands);
-        // a pass addresses a unit's rows (band + 2k halo rows) through 32-bit byte
-        // offsets: shorter bands for very wide rows, and refuse what cannot fit
+        // a pass addresses a unit's rows (band + 2L halo rows, L <= k + 1 levels:
+        // a task's last pass also sums the residual) through 32-bit byte offsets:
+        // shorter bands for very wide rows, and refuse what cannot fit
         const uint64_t lim = 0xFFFFFFFFull / e->pitch_bytes;
-        if (lim < static_cast<uint64_t>(2 * k + 1)) return PK_EINVAL;
-        p.pband_rows = static_cast<int>(std::min<uint64_t>(p.pband_rows, lim - 2 * k));
+        if (lim < static_cast<uint64_t>(2 * (k + 1) + 1)) return PK_EINVAL;
+        p.pband_rows = static_cast<int>(std::min<uint64_t>(p.pband_rows, lim - 2 * (k + 1)));
         p.pbands = ceil_div(interior, p.pband_rows);
     }
 
@@ -509,7 +519,8 @@ int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* op
     if (o.layout < PK_LAYOUT_AUTO || o.layout > PK_LAYOUT_REGISTER) return PK_EINVAL;
     if (o.threads != 0 && (o.threads < 64 || o.threads > 1024 || o.threads % 64 != 0)) return PK_EINVAL;
     if (o.max_blocks < 0 || o.halo_depth < 0 || o.idle_timeout_s < 0) return PK_EINVAL;
-    if (o.pass_sweeps < 0 || o.pass_sweeps > PK_MAX_PASS || o.band_rows < 0) return PK_EINVAL;
+    if (o.pass_sweeps < 0 || (o.pass_sweeps > 0 && !PK_PASS_DEPTH_OK(o.pass_sweeps)) || o.band_rows < 0)
+        return PK_EINVAL;
     if (o.flags & ~(PK_DBG_BROKEN_BARRIER | PK_DBG_TRACE)) return PK_EINVAL;
     if ((o.flags & PK_DBG_TRACE) && o.mode != PK_PERSISTENT) return PK_EINVAL;
     if (o.barrier < PK_BARRIER_AUTO || o.barrier > PK_BARRIER_XCD) return PK_EINVAL;

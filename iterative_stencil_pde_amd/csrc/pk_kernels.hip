@@ -59,7 +59,7 @@ const void* pkk_persistent_fn(int dtype, bool has_b, int layout, int rows, bool 
     if (layout == PK_LAYOUT_RESIDENT) return pkk_resident_fn(dtype, has_b, trace);
     // the streaming layout has no events inside its passes: one instance serves
     // traced and untraced engines
-    return pkk_stream_fn(dtype, has_b);
+    return dtype == PK_F64 ? pkk_stream_fn_f64(has_b) : pkk_stream_fn_f32(has_b);
 }
 
 const void* pkk_sweep_fn(int dtype, bool has_b) {

@@ -10,7 +10,8 @@
 // instance with the tile layouts' in-loop events (PK_DBG_TRACE).
 const void* pkk_persistent_fn(int dtype, bool has_b, int layout, int rows, bool trace);
 // The same, per layout (one translation unit each).
-const void* pkk_stream_fn(int dtype, bool has_b);
+const void* pkk_stream_fn_f32(bool has_b);
+const void* pkk_stream_fn_f64(bool has_b);
 const void* pkk_resident_fn(int dtype, bool has_b, bool trace);
 const void* pkk_register_fn_f32(bool has_b, int rows, bool trace);
 const void* pkk_register_fn_f64(bool has_b, int rows, bool trace);

@@ -1,7 +1,7 @@
 // The persistent kernel of the Jacobi engine for gfx950, as a template. Each
 // layout's instances are compiled in a translation unit of their own
-// (pk_kern_stream.hip, pk_kern_resident.hip, pk_kern_register_f32.hip,
-// pk_kern_register_f64.hip), which builds them in parallel and lets each
+// (pk_kern_stream_f32.hip, pk_kern_stream_f64.hip, pk_kern_resident.hip,
+// pk_kern_register_f32.hip, pk_kern_register_f64.hip), which builds them in parallel and lets each
 // instance carry only its own layout's code.
 #pragma once
 
@@ -574,6 +574,19 @@ struct ResidualState {
     bool ready;
 };
 
+// Depth of the next streaming pass with `left` sweeps (or red-black
+// half-sweeps) to go: the engine's depth, or `left` when fewer. A depth the
+// kernel does not carry (9..11) runs 8 first. A task's last Jacobi pass also
+// sums the residual with one level more, so it is at most PK_SHALLOW_PASS deep:
+// a 12-sweep tail runs as 4 + 8. Red-black passes are at most PK_SHALLOW_PASS
+// deep. Every block computes the same sequence.
+__device__ __forceinline__ int pass_depth(int depth, int left, bool rb) {
+    int k = min(depth, left);
+    if (k > PK_SHALLOW_PASS && (rb || !PK_PASS_DEPTH_OK(k))) k = PK_SHALLOW_PASS;
+    if (k == left && k > PK_SHALLOW_PASS) k = left - PK_SHALLOW_PASS;
+    return k;
+}
+
 // n sub-sweeps of the field in u[cur] in the engine's layout (cur flips):
 // Jacobi sweeps, or (rb) red-black half-sweeps, red first.
 template <typename T, bool HAS_B, int LAYOUT, int RT, bool TRACE>
@@ -591,7 +604,7 @@ __device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, i
             reg_sweep_task<T, HAS_B, false, RT, TRACE>(a, n, cur, bc, lds);
     } else {
         for (int s = 0; s < n;) {
-            const int k = min(a.pass_sweeps, n - s);
+            const int k = pass_depth(a.pass_sweeps, n - s, rb);
             // the last Jacobi pass of a task also sums rho^2 of its result, so a
             // RESIDUAL that follows need not read the field again ("Grid-Wide
             // Barriers", "What the barrier buys": the convergence check as a

@@ -14,7 +14,12 @@
 #include <stdint.h>
 
 #define PK_RING 64u
-#define PK_MAX_PASS 8
+// Streaming pass depths (sweeps per pass) the kernel carries: 1..8 and 12.
+// Passes that also sum the residual, and red-black passes, are at most
+// PK_SHALLOW_PASS deep.
+#define PK_MAX_PASS 12
+#define PK_SHALLOW_PASS 8
+#define PK_PASS_DEPTH_OK(k) ((k) >= 1 && ((k) <= PK_SHALLOW_PASS || (k) == PK_MAX_PASS))
 #define PK_LINE 128
 
 // Internal task kinds (the public ones are in pk.h); kinds fit in 4 bits.

@@ -30,7 +30,7 @@ PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP, PK_SWEEP_RB, PK_SWEEP_UNTI
 PK_BLOCKSYNC = 8
 PK_DBG_BROKEN_BARRIER, PK_DBG_TRACE = 0x1, 0x2
 PK_TASK_N_MAX = 0x0FFFFFFF
-PK_MAX_PASS = 8  # deepest streaming pass (sweeps kept on chip), the planner's default
+PK_MAX_PASS = 12  # deepest streaming pass (sweeps kept on chip); passes of 1..8 and 12
 PK_BARRIER_AUTO, PK_BARRIER_FLAT, PK_BARRIER_TWO_LEVEL, PK_BARRIER_XCD = 0, 1, 2, 3
 PK_EXCHANGE_AUTO, PK_EXCHANGE_BARRIER, PK_EXCHANGE_NEIGHBOR, PK_EXCHANGE_TAGGED = 0, 1, 2, 3
 

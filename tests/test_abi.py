@@ -122,6 +122,9 @@ def test_create_rejects_bad_arguments_before_touching_a_device(lib):
     assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
     bad = pk.pk_opts_default(exchange=4)
     assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
+    for k in (-1, 9, 10, 11, 13, 16):  # pass depths the kernel does not carry
+        bad = pk.pk_opts_default(pass_sweeps=k)
+        assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL
     for x in (pk.PK_EXCHANGE_NEIGHBOR, pk.PK_EXCHANGE_TAGGED):  # the negative control keeps barriers
         bad = pk.pk_opts_default(exchange=x, flags=pk.PK_DBG_BROKEN_BARRIER)
         assert lib.pk_create(8, 8, bc.ctypes.data, None, ctypes.byref(bad), ctypes.byref(h)) == pk.PK_EINVAL

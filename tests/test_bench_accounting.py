@@ -1,0 +1,65 @@
+"""The byte accounting of bench.py's roofline mirrors how the persistent kernel
+splits a streaming task into passes (deep passes, the shallow last pass that also
+sums the residual, red-black passes) and which RESIDUAL tasks read the field.
+Expected values are worked out by hand from that rule. No GPU needed."""
+
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("n,depth,rb,want", [
+    (50, 12, False, [12, 12, 12, 12, 2]),
+    (12, 12, False, [4, 8]),
+    (23, 12, False, [12, 8, 3]),
+    (24, 12, False, [12, 4, 8]),
+    (10, 12, False, [8, 2]),
+    (8, 12, False, [8]),
+    (7, 12, False, [7]),
+    (14, 12, True, [8, 6]),
+    (50, 8, False, [8, 8, 8, 8, 8, 8, 2]),
+    (5, 1, False, [1, 1, 1, 1, 1]),
+    (0, 12, False, []),
+])
+def test_pass_depths(n, depth, rb, want):
+    got = bench.pass_depths(n, depth, rb)
+    assert got == want
+    assert sum(got) == n
+    assert all(k in (1, 2, 3, 4, 5, 6, 7, 8, 12) for k in got)
+    if got:
+        assert got[-1] <= bench.SHALLOW_PASS
+
+
+def _shape_only(nx, ny, dtype, poisson, script=()):
+    """What the accounting reads of a workload: shape, type, source, script."""
+    return types.SimpleNamespace(nx=nx, ny=ny, dtype=dtype, f=(object() if poisson else None),
+                                 script=list(script))
+
+
+def test_default_depth_follows_the_infinity_cache():
+    # 8192^2 fp64 Poisson streams 3 x 512 MiB: deep passes; 4096^2 fp32 Laplace
+    # streams 2 x 64 MiB, which the 256 MiB cache holds
+    assert bench.default_depth(_shape_only(8192, 8192, np.float64, True)) == 12
+    assert bench.default_depth(_shape_only(4096, 4096, np.float32, False)) == 8
+    assert bench.default_depth(_shape_only(6000, 6000, np.float32, True)) == 12  # 3 x 137 MiB
+
+
+def test_script_counts_fused_residuals():
+    # the 8192^2 script: RESIDUAL; 10 x (SWEEP 50, RESIDUAL): only the first
+    # residual reads the field, the others were summed by the pass before them
+    script = [("residual",)] + [("sweep", 50), ("residual",)] * 10 + [("readback",)]
+    w = _shape_only(8192, 8192, np.float64, True, script)
+    assert bench.script_counts(w, 12) == (500, 50, 1)
+    assert bench.script_counts(w, 8) == (500, 70, 1)
+    # one pass per sweep (launch-style plans) fuses nothing
+    assert bench.script_counts(w, 1) == (500, 500, 11)
+    # red-black tasks and empty sweeps leave the next residual to read the field
+    w = _shape_only(64, 64, np.float32, False,
+                    [("sweep", 9), ("residual",), ("sweep_rb", 3), ("residual",), ("sweep", 0), ("residual",)])
+    assert bench.script_counts(w, 8) == (12, 2 + 1, 2)

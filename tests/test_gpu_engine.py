@@ -174,7 +174,7 @@ AUTO_PLANS = {
     "poisson256": dict(layout=pk.PK_LAYOUT_REGISTER, exchange=pk.PK_EXCHANGE_TAGGED, threads=1024),
     "laplace1024": dict(layout=pk.PK_LAYOUT_REGISTER, exchange=pk.PK_EXCHANGE_TAGGED, threads=1024),
     "laplace4096": dict(layout=pk.PK_LAYOUT_STREAM, pass_sweeps=8, threads=512, grid_blocks=256),
-    "poisson8192": dict(layout=pk.PK_LAYOUT_STREAM, pass_sweeps=8, threads=512, grid_blocks=256),
+    "poisson8192": dict(layout=pk.PK_LAYOUT_STREAM, pass_sweeps=12, threads=512, grid_blocks=256),
 }
 
 

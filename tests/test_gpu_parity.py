@@ -152,7 +152,7 @@ def test_xcd_barrier_full_size(name, sweeps):
     check_against_oracle(w, got, ref, f"{name}/xcd")
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7, 8, 12])
 @pytest.mark.parametrize("poisson", [False, True], ids=["laplace", "poisson"])
 @pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
 @pytest.mark.parametrize("shape", [(3, 3), (5, 300), (300, 5), (67, 131), (130, 257), (33, 1030),
@@ -171,9 +171,34 @@ def test_stream_passes_of_k_sweeps(shape, dtype, poisson, k):
     check_against_oracle(w, got, ref, f"pass{k}/{ny}x{nx}/{np.dtype(dtype).name}")
 
 
+DEEP_SCRIPT = [("sweep", 12), ("residual",), ("sweep", 23), ("residual",), ("sweep", 24), ("residual",),
+               ("sweep", 10), ("sweep", 35), ("residual",), ("sweep_rb", 7), ("residual",), ("sweep", 13),
+               ("readback",)]
+
+
+@pytest.mark.parametrize("poisson", [False, True], ids=["laplace", "poisson"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("shape", [(5, 300), (67, 131), (130, 257), (33, 1030), (61, 4100)],
+                         ids=lambda s: f"{s[0]}x{s[1]}")
+def test_deep_pass_splitting(shape, dtype, poisson):
+    """Depth-12 passes: tasks of 12 (run as 4 + 8, the last pass summing the
+    residual), 23 (12 + 8 + 3), 24 (12 + 4 + 8), 10 (8 + 2), 35 and 13 sweeps, and
+    red-black iterations (passes of at most 8 half-sweeps) between them, against
+    the oracle."""
+    ny, nx = shape
+    u, f = _random_case(ny, nx, dtype, poisson, seed=11 * ny + nx)
+    w = inputs.Workload(f"deep{ny}x{nx}", nx, ny, dtype, 0.013, u, f, list(DEEP_SCRIPT), "")
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=12)
+    assert got["info"].pass_sweeps == 12
+    check_against_oracle(w, got, ref, f"deep/{ny}x{nx}/{np.dtype(dtype).name}")
+
+
 @pytest.mark.parametrize("name,sweeps,k", [("laplace4096", 41, 4), ("laplace4096", 23, 3), ("laplace4096", 37, 8),
                                            ("poisson8192", 5, 2), ("poisson8192", 7, 3), ("poisson8192", 9, 4),
-                                           ("poisson8192", 13, 8), ("poisson8192", 11, 6)])
+                                           ("poisson8192", 13, 8), ("poisson8192", 11, 6),
+                                           ("poisson8192", 50, 12), ("poisson8192", 12, 12),
+                                           ("laplace4096", 29, 12)])
 def test_stream_passes_full_size(name, sweeps, k):
     w = inputs.make(name)
     w.script = [("sweep", sweeps), ("residual",), ("readback",)]
@@ -698,7 +723,7 @@ FUSED_SCRIPT = [("residual",), ("sweep", 1), ("residual",), ("sweep", 8), ("resi
                 ("sweep", 0), ("residual",), ("readback",)]
 
 
-@pytest.mark.parametrize("k", [1, 2, 3, 8])
+@pytest.mark.parametrize("k", [1, 2, 3, 8, 12])
 @pytest.mark.parametrize("shape,dtype,poisson", [((67, 131), np.float64, True), ((257, 255), np.float32, True),
                                                  ((130, 257), np.float32, False), ((33, 1030), np.float64, False),
                                                  ((5, 300), np.float32, True)],
