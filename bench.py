@@ -348,8 +348,9 @@ def persistent_run(w, steps, warmup, opts, pure=True):
 
 def roofline_stream(w, r, steps, warmup, traffic_key):
     """HBM roofline of a persistent streaming launch. The unit is one pass over the
-    field (k sweeps kept on chip): its algorithmic bytes read u and b once and write
-    u once; a residual reads u and b. The counter bytes (stored, same device code)
+    field (up to k sweeps kept on chip): its algorithmic bytes read u and b once and
+    write u once; a residual that the pass before it did not sum reads u and b. The
+    counter bytes (stored, same device code)
     add what the kernel really moves (halo rows, overlap lanes, polling words; Infinity
     Cache hits count)."""
     info, end = r["info"], r["end"]
