@@ -773,12 +773,21 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
 // Ring handling (MODE):
 //   PASS_CHECKED: every level checks whether its row is a ring row (kept) and
 //     every element whether it is a ring or padding column (kept).
-//   PASS_COLS, PASS_INNER: for units whose rows meet a ring row only during
-//     the first 2K steps of the march (the first band marches down from the top
-//     ring, the last band up from the bottom ring, and no band ends within K rows
-//     of the far ring). The ring-row check runs only in those steps, as a
-//     branch-free blend; PASS_INNER also leaves out the column check, for units
-//     whose columns [c0, c0 + 64 W) are all interior.
+//   PASS_COLS, PASS_EDGE, PASS_INNER: for units whose rows meet a ring row only
+//     during the first 2K steps of the march (the first band marches down from
+//     the top ring, the last band up from the bottom ring, and no band ends
+//     within K rows of the far ring). The ring-row check runs only in those
+//     steps, as a branch-free blend. PASS_INNER also leaves out the column
+//     check, for units whose columns [c0, c0 + 64 W) are all interior.
+//     PASS_EDGE_LO / PASS_EDGE_HI, for a Laplace unit that holds one of the two
+//     ring columns when nx is a multiple of W: column 0 is then element 0 of its lane
+//     and column nx - 1 element W - 1 of its lane, and no stored lane holds a
+//     padding column, so the march keeps just that one element (one per-lane
+//     blend a level) instead of checking every element: padding and outside
+//     columns feed only the ring columns, which are kept.
+//     (The edge strips' waves finish last and hold the pass's barrier: with
+//     them on the INNER march's cost, 4096^2 ran 14% faster; with one blend a
+//     level, 4.48 -> 4.22 us per sweep.)
 //
 // RES: the pass also sums rho^2 of its result (the residual of the field it
 // stores, as a RESIDUAL task would compute it, element by element the same
@@ -792,7 +801,7 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
 // (before its loads): faster where stores are a large share of the traffic
 // (fp64, or with b); otherwise each row is stored as soon as it is computed.
 // ---------------------------------------------------------------------------
-enum { PASS_CHECKED = 0, PASS_COLS = 1, PASS_INNER = 2 };
+enum { PASS_CHECKED = 0, PASS_COLS = 1, PASS_INNER = 2, PASS_EDGE_LO = 3, PASS_EDGE_HI = 4 };
 
 // rho^2 of one vector summed in double over its interior elements, from the
 // vector (m), its row neighbours (s, n), its W/E neighbours by DPP and b
@@ -854,6 +863,12 @@ struct HeadSteps {
     static constexpr bool value = V;
 };
 
+// A step's slot in a level's three-row ring (the step number mod 3).
+template <int P>
+struct RingSlot {
+    static constexpr int value = P;
+};
+
 template <typename T, bool HAS_B, int K, int DIR, bool RB, int MODE, bool RES>
 __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T* __restrict__ dst,
                                                    const T* __restrict__ bsrc, int nx, int ny,
@@ -861,10 +876,16 @@ __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T*
     constexpr int dir = DIR;
     constexpr int W = VecW<T>::W;
     constexpr int L = K + (RES ? 1 : 0);  // levels of the march (the last one rho with RES)
-    constexpr int CH = (HAS_B || L >= 3) ? 2 : 4;  // rows per chunk
+    // ROT: each level keeps its last three rows in a ring indexed by the step
+    // number mod 3, and the march takes three rows a chunk, so every ring slot is
+    // known at compile time and no row moves from one register to another (the
+    // two-row form copies every level's rows at every step). One row more per
+    // level: only where no b delay line shares the register file.
+    constexpr bool ROT = !HAS_B;
+    constexpr int CH = ROT ? 3 : ((HAS_B || L >= 3) ? 2 : 4);  // rows per chunk
+    constexpr int HEAD = (2 * L + CH - 1) / CH * CH;  // steps taken with the head's level checks
     constexpr bool DEFER = sizeof(T) == 8 || (HAS_B && L <= PK_SHALLOW_PASS + 1);
-    constexpr bool COLS = MODE != PASS_INNER;
-    static_assert((2 * L) % CH == 0, "the first 2L steps are whole chunks");
+    constexpr bool COLS = MODE == PASS_CHECKED || MODE == PASS_COLS;  // every element checked
     const int lane = threadIdx.x & 63;
     const int col = c0 + lane * W;
     const bool act = col >= 0 && col < nx;
@@ -883,16 +904,26 @@ __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T*
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + static_cast<size_t>(w0) * p, win_bytes);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + static_cast<size_t>(w0) * p, win_bytes);
     const __amdgpu_buffer_rsrc_t rbs = make_rsrc(HAS_B ? bsrc + static_cast<size_t>(w0) * p : src, win_bytes);
+    // PASS_EDGE_LO: the lane holding column 0 (element 0); PASS_EDGE_HI: the lane
+    // holding column nx - 1 (element W - 1)
+    const uint32_t ring_lane = lane_mask(MODE == PASS_EDGE_LO ? col == 0 : col + W - 1 == nx - 1);
     const uint32_t lbyte = static_cast<uint32_t>(min(max(col, 0), pitch - W)) * sizeof(T);
     const uint32_t sbyte = static_cast<uint32_t>(max(col, 0)) * sizeof(T);  // stored lanes have col >= 0
     const int b_lo = max(w0, 1), b_hi = min(w1, ny - 1) - 1;  // b rows: interior rows of the window
 
-    Vec<T> ra[L], rm[L];  // level j rows x-1 and x, x the last row it received
+    // two-row form: level j rows x-1 and x, x the last row it received;
+    // ROT: level j's rows of the last three steps, the row of step q in slot q mod 3
+    Vec<T> ra[ROT ? 1 : L], rm[ROT ? 1 : L];
+    Vec<T> hr[ROT ? L : 1][3];
     Vec<T> bq[L];         // bq[j] = b row of the level j+1 row computed at this step
     double acc = 0.0;     // RES: this lane's rho^2
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-        ra[j] = rm[j] = vzero<T>();
+        if constexpr (ROT) {
+            hr[j][0] = hr[j][1] = hr[j][2] = vzero<T>();
+        } else {
+            ra[j] = rm[j] = vzero<T>();
+        }
         bq[j] = vzero<T>();
     }
     // dir = +1 marches down from r0 - L, dir = -1 marches up from r1 - 1 + L
@@ -921,8 +952,10 @@ __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T*
     // One step: level-0 row u (and its b row); returns level K's row. In the first
     // 2L steps (head) only levels j <= q / 2 are computed: a higher level's row at
     // this step lies outside the rows any stored row (or summed rho) depends on.
-    const auto step = [&](int q, const Vec<T>& u, const Vec<T>& b, auto head_c) -> Vec<T> {
+    // slot_c (ROT): q mod 3.
+    const auto step = [&](int q, const Vec<T>& u, const Vec<T>& b, auto head_c, auto slot_c) -> Vec<T> {
         constexpr bool head = decltype(head_c)::value;
+        constexpr int P = decltype(slot_c)::value;
         const int t = t_first + dir * q;
 #pragma unroll
         for (int j = L - 1; j > 0; --j) bq[j] = bq[j - 1];
@@ -931,21 +964,32 @@ __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T*
         Vec<T> outK = u;
 #pragma unroll
         for (int j = 1; j <= L; ++j) {
-            const Vec<T> mid = rm[j - 1];
+            // level j-1's rows of steps t-2 and t-1 (inc is its row of step t)
+            const Vec<T> up = ROT ? hr[ROT ? j - 1 : 0][(P + 1) % 3] : ra[ROT ? 0 : j - 1];
+            const Vec<T> mid = ROT ? hr[ROT ? j - 1 : 0][(P + 2) % 3] : rm[ROT ? 0 : j - 1];
+            const auto keep = [&](const Vec<T>& x) {  // level j-1 moves on by one row
+                if constexpr (ROT) {
+                    hr[j - 1][P] = x;
+                } else {
+                    ra[j - 1] = mid;
+                    rm[j - 1] = x;
+                }
+            };
             if (RES && j == L) {  // rho of level K's row t - dir L, if it is a band row
                 const int row = t - dir * j;
                 if ((!head || 2 * j <= q) && row >= r0 && row < r1) {  // wave-uniform
-                    const double r2 = pass_rho2<T, HAS_B, COLS>(ra[j - 1], mid, inc, bq[j - 1], col, nx);
+                    const double r2 = pass_rho2<T, HAS_B, COLS>(up, mid, inc, bq[j - 1], col, nx);
                     if (store_lane) acc += r2;
                 }
-                ra[j - 1] = mid;
-                rm[j - 1] = inc;
+                keep(inc);
                 continue;
             }
             if (!head || 2 * j <= q) {  // wave-uniform
                 const int row = t - dir * j;  // level j row computed at this step
                 // level j-1 rows row-1, row, row+1 (dir = -1: row+1, row, row-1)
-                Vec<T> o = pass_stencil<T, HAS_B, COLS>(ra[j - 1], mid, inc, bq[j - 1], col, nx);
+                Vec<T> o = pass_stencil<T, HAS_B, COLS>(up, mid, inc, bq[j - 1], col, nx);
+                if constexpr (MODE == PASS_EDGE_LO) o.v[0] = blend(ring_lane, mid.v[0], o.v[0]);
+                if constexpr (MODE == PASS_EDGE_HI) o.v[W - 1] = blend(ring_lane, mid.v[W - 1], o.v[W - 1]);
                 if (RB) o = rb_keep(o, mid, row, (h0 + j - 1) & 1);
                 const bool ring = row <= 0 || row >= ny - 1;  // ring rows (and beyond) keep their value
                 if (MODE == PASS_CHECKED) {
@@ -953,12 +997,10 @@ __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T*
                 } else if (head) {
                     o = vblend(lane_mask(ring), mid, o);
                 }
-                ra[j - 1] = mid;
-                rm[j - 1] = inc;
+                keep(inc);
                 inc = o;
             } else {  // a row outside every stored row's reach: shift only
-                ra[j - 1] = mid;
-                rm[j - 1] = inc;
+                keep(inc);
             }
             if (j == K) outK = inc;
         }
@@ -981,11 +1023,23 @@ __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T*
             load_chunk(q0 + CH, nld, nlb);
             // whole chunks: a step past the last computes rows beyond the band's
             // halo, which are never stored
+            if constexpr (ROT) {  // q0 is a multiple of 3: the ring slots are 0, 1, 2
+                const Vec<T> x0 = step(q0, ld[0], lb[0], head_c, RingSlot<0>{});
+                if (DEFER) out[0] = x0;
+                else store_row(q0, x0);
+                const Vec<T> x1 = step(q0 + 1, ld[1], lb[1], head_c, RingSlot<1>{});
+                if (DEFER) out[1] = x1;
+                else store_row(q0 + 1, x1);
+                const Vec<T> x2 = step(q0 + 2, ld[2], lb[2], head_c, RingSlot<2>{});
+                if (DEFER) out[2] = x2;
+                else store_row(q0 + 2, x2);
+            } else {
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const Vec<T> x = step(q0 + c, ld[c], lb[c], head_c);
-                if (DEFER) out[c] = x;
-                else store_row(q0 + c, x);
+                for (int c = 0; c < CH; ++c) {
+                    const Vec<T> x = step(q0 + c, ld[c], lb[c], head_c, RingSlot<0>{});
+                    if (DEFER) out[c] = x;
+                    else store_row(q0 + c, x);
+                }
             }
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
@@ -994,10 +1048,11 @@ __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T*
             }
         }
     };
-    run(0, 2 * L, HeadSteps<true>{});
-    run(2 * L, nsteps, HeadSteps<false>{});
+    run(0, HEAD, HeadSteps<true>{});
+    run(HEAD, nsteps, HeadSteps<false>{});
     if (DEFER) {
-        const int q_last = 2 * L + ((nsteps - 2 * L - 1) / CH) * CH;  // the last chunk computed
+        // the last chunk computed
+        const int q_last = nsteps > HEAD ? HEAD + ((nsteps - HEAD - 1) / CH) * CH : HEAD - CH;
 #pragma unroll
         for (int c = 0; c < CH; ++c) store_row(q_last + c, out[c]);
     }
@@ -1033,7 +1088,7 @@ __device__ __forceinline__ double stream_pass_k(const pk_kargs& a, const T* __re
         // the march meets a ring row only in its first 2L steps unless the band
         // ends within L rows of the far ring (a single band, or a short last band)
         const bool rows_late = dir > 0 ? r1 + L > a.ny : r0 < L;
-        const bool cols = c0 < 1 || c0 + 64 * W > a.nx - 1;
+        const bool lo = c0 < 1, hi = c0 + 64 * W > a.nx - 1;  // the unit holds ring column 0 / nx - 1
         const int nx = a.nx, ny = a.ny, pt = a.pitch;
         // red-black passes, the last pass of a task (RES) and passes of fewer than
         // PK_SHALLOW_PASS sweeps (a task's passes are all as deep as the engine's
@@ -1044,7 +1099,15 @@ __device__ __forceinline__ double stream_pass_k(const pk_kargs& a, const T* __re
         } else if (rows_late) {
             if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_CHECKED, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
             else stream_pass_unit<T, HAS_B, K, -1, false, PASS_CHECKED, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-        } else if (cols) {
+        } else if (!HAS_B && lo != hi && nx % W == 0) {  // (with b the register file is full at depth 12)
+            if (lo) {
+                if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_EDGE_LO, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+                else stream_pass_unit<T, HAS_B, K, -1, false, PASS_EDGE_LO, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            } else {
+                if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_EDGE_HI, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+                else stream_pass_unit<T, HAS_B, K, -1, false, PASS_EDGE_HI, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            }
+        } else if (lo || hi) {
             if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_COLS, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
             else stream_pass_unit<T, HAS_B, K, -1, false, PASS_COLS, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
         } else {
