@@ -362,7 +362,7 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     if (!tiled) {
         p.layout = PK_LAYOUT_STREAM;
         // the persistent streaming kernel's blocks are as large as its register
-        // budget allows (its passes keep up to 8 levels of the march in registers)
+        // budget allows (its passes keep up to 12 levels of the march in registers)
         if (e->mode == PK_PERSISTENT) {
             hipFuncAttributes fa{};
             if (hipFuncGetAttributes(&fa, pkk_persistent_fn(e->dtype, e->has_b, PK_LAYOUT_STREAM, 0, false)) != hipSuccess)

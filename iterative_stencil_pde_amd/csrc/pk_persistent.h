@@ -79,7 +79,12 @@ struct RegSlot {
 // ONE: a single column strip (cw == 1): lane 0's W neighbour and lane 63's E
 // neighbour can only belong to ring or padding columns, which keep their
 // values, so the lane shifts need no edge values.
-template <typename T, bool HAS_B, bool RB, int RT, bool ONE, bool TRACE>
+// ALN: nx is a multiple of the vector width, so column 0 is element 0 of its
+// lane, column nx - 1 element W - 1 of its lane, and every other lane holds
+// interior columns or padding only; padding lanes are never published, so their
+// values do not matter and only those two elements need keeping (two blends a
+// row instead of W).
+template <typename T, bool HAS_B, bool RB, int RT, bool ONE, bool ALN, bool TRACE>
 __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
     constexpr int W = VecW<T>::W;
     using S = RegSlot<T>;
@@ -100,9 +105,11 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
     const int row_base = e0 + rg * RT;
     const size_t p = static_cast<size_t>(a.pitch);
     const bool has_left = cg > 0, has_right = cg + 1 < cw;  // wave-uniform
-    uint32_t keep[W];  // ring and padding columns keep their value
+    uint32_t keep[W];  // ring (and, unless ALN, padding) columns keep their value
 #pragma unroll
-    for (int k = 0; k < W; ++k) keep[k] = lane_mask((col + k == 0) || (col + k >= nx - 1));
+    for (int k = 0; k < W; ++k)
+        keep[k] = ALN ? lane_mask((k == 0 && col == 0) || (k == W - 1 && col + k == nx - 1))
+                      : lane_mask((col + k == 0) || (col + k >= nx - 1));
 
     Vec<T> u[RT], bb[RT];
     {
@@ -211,7 +218,10 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
                             const T ea = (k == W - 1) ? east : old.v[k + 1];
                             T x = (w + ea) + (prev.v[k] + nxt.v[k]);
                             if (HAS_B) x = x + bb[r].v[k];
-                            o.v[k] = blend(keep[k], old.v[k], T(0.25) * x);
+                            if (!ALN || k == 0 || k == W - 1)
+                                o.v[k] = blend(keep[k], old.v[k], T(0.25) * x);
+                            else
+                                o.v[k] = T(0.25) * x;
                         }
                         if (RB) o = rb_keep(o, old, row, parity);
                         u[r] = o;
@@ -330,10 +340,18 @@ __device__ __forceinline__ void reg_sweep_rows(const pk_kargs& a, int n, int& cu
 // kernel instance it runs: each instance holds one row count's registers.
 template <typename T, bool HAS_B, bool RB, int RT, bool TRACE>
 __device__ __forceinline__ void reg_sweep_task(const pk_kargs& a, int n, int& cur, BarrierCtx& bc, T* lds) {
-    if (a.reg_cw == 1)
-        reg_sweep_rows<T, HAS_B, RB, RT, true, TRACE>(a, n, cur, bc, lds);
-    else
-        reg_sweep_rows<T, HAS_B, RB, RT, false, TRACE>(a, n, cur, bc, lds);
+    const bool aln = a.nx % VecW<T>::W == 0;
+    if (a.reg_cw == 1) {
+        if (aln)
+            reg_sweep_rows<T, HAS_B, RB, RT, true, true, TRACE>(a, n, cur, bc, lds);
+        else
+            reg_sweep_rows<T, HAS_B, RB, RT, true, false, TRACE>(a, n, cur, bc, lds);
+    } else {
+        if (aln)
+            reg_sweep_rows<T, HAS_B, RB, RT, false, true, TRACE>(a, n, cur, bc, lds);
+        else
+            reg_sweep_rows<T, HAS_B, RB, RT, false, false, TRACE>(a, n, cur, bc, lds);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -656,7 +674,7 @@ __device__ __forceinline__ double residual_round(const pk_kargs& a, int cur, Bar
     return r;
 }
 
-// The streaming kernel's passes keep up to 8 levels of the march in registers:
+// The streaming kernel's passes keep up to 12 levels of the march in registers:
 // blocks of at most 512 threads give it 256 VGPRs per lane.
 // (Two waves per SIMD already keep its vector unit busy: 768-thread blocks, which
 // the fp32 Laplace passes would fit, measured slower, 6.5 against 5.3 us per
