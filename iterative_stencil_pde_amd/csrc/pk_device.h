@@ -1082,9 +1082,11 @@ __device__ __forceinline__ double stream_pass_k(const pk_kargs& a, const T* __re
         if (r0 >= r1) continue;
         const int c0 = strip * stride - ov * W;
         // the first band marches down from the top ring, the last up from the
-        // bottom ring, the others alternate, so that neighbouring bands read the
-        // halo rows they share at about the same time (and hit in the XCD's L2)
-        const int dir = band == 0 ? 1 : (band == a.pbands - 1 ? -1 : ((band & 1) ? -1 : 1));
+        // bottom ring; the others march down (march_down: HBM-bound passes) or
+        // alternate, so that neighbouring bands read the halo rows they share at
+        // about the same time (and hit in the XCD's L2)
+        const int dir = band == 0 ? 1
+                        : (band == a.pbands - 1 ? -1 : (a.march_down || !(band & 1) ? 1 : -1));
         // the march meets a ring row only in its first 2L steps unless the band
         // ends within L rows of the far ring (a single band, or a short last band)
         const bool rows_late = dir > 0 ? r1 + L > a.ny : r0 < L;

@@ -38,6 +38,7 @@ struct Plan {
     int exchange = 0;  // RESIDENT: PK_EXCHANGE_BARRIER or PK_EXCHANGE_NEIGHBOR
     int pass_sweeps = 1;
     int pband_rows = 1, pbands = 1;
+    int march_down = 0;
     int occ = 0;  // blocks per CU allowed by the occupancy query
 };
 
@@ -393,8 +394,14 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
     p.pass_sweeps = 1;
     if (e->mode == PK_PERSISTENT && p.layout == PK_LAYOUT_STREAM) {
         const uint64_t streamed = static_cast<uint64_t>(e->pitch_bytes) * e->ny * (e->has_b ? 3 : 2);
-        const int depth = streamed > kInfinityCacheBytes ? PK_MAX_PASS : PK_SHALLOW_PASS;
-        p.pass_sweeps = o.pass_sweeps > 0 ? o.pass_sweeps : depth;
+        const bool hbm = streamed > kInfinityCacheBytes;
+        p.pass_sweeps = o.pass_sweeps > 0 ? o.pass_sweeps : (hbm ? PK_MAX_PASS : PK_SHALLOW_PASS);
+        // march direction: where the passes stream from HBM, every band but the
+        // last marches down (8192^2 fp64 Poisson: 31.8 -> 30.9 us per sweep);
+        // where the arrays sit in the Infinity Cache, neighbouring bands march in
+        // opposite directions and meet on the halo rows they share, in L2
+        // (4096^2: 4.15 against 4.18 us with all bands down)
+        p.march_down = hbm ? 1 : 0;
     }
     {
         const int k = p.pass_sweeps;
@@ -463,6 +470,7 @@ void fill_kargs(pk_engine* e) {
     a.barrier_kind = p.barrier_kind;
     a.pass_sweeps = p.pass_sweeps;
     a.pband_rows = p.pband_rows;
+    a.march_down = p.march_down;
     a.pbands = p.pbands;
     a.flags = e->flags;
     a.st = e->d_st;

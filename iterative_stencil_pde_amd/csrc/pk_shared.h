@@ -155,6 +155,7 @@ struct pk_kargs {
     // passes of several sweeps: rows per band and bands (strips depend on k)
     int pass_sweeps;       // sweeps per pass in the stream layout (1 = one per barrier)
     int pband_rows, pbands;
+    int march_down;        // passes: every band but the last marches down (else directions alternate)
     // resident and register geometry: one band per block, the interior split
     // into bands of res_q or res_q + 1 rows (the first res_rem bands are longer)
     int res_q, res_rem;
