@@ -515,7 +515,8 @@ def main():
     ap.add_argument("--halo", type=int, default=0)
     ap.add_argument("--barrier", default="auto", choices=["auto", "flat", "two_level", "xcd"])
     ap.add_argument("--exchange", default="auto", choices=["auto", "barrier", "neighbor", "tagged"],
-                    help="tile layouts: halo exchange by grid barrier, neighbour flags or tagged words")
+                    help="tile layouts: halo exchange by grid barrier, neighbour flags or tagged words; "
+                         "streaming passes: grid barrier or neighbour counters per XCD")
     ap.add_argument("--pass-sweeps", type=int, default=0, help="stream layout: sweeps per pass")
     ap.add_argument("--band-rows", type=int, default=0, help="stream passes: rows per band")
     ap.add_argument("--launch-steps", type=int, default=0,

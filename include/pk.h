@@ -168,7 +168,16 @@ extern "C" {
  *   which they publish only after reading e. The last exchange of every task
  *   is a grid barrier, as above.
  * AUTO: the cheaper of the kinds the layout supports by the cost model, or
- *   BARRIER under PK_DBG_BROKEN_BARRIER.                                      */
+ *   BARRIER under PK_DBG_BROKEN_BARRIER.
+ * STREAM (persistent), between the passes of one task: BARRIER, a grid
+ *   barrier after every pass. NEIGHBOR: after a full-depth pass followed by
+ *   another, neighbour counters kept per XCD: every block arrives at its XCD's
+ *   counter, the XCD's last block writes the XCD's L2 back once and publishes
+ *   the pass count, and each block waits only for the XCDs that run the blocks
+ *   whose units border its own (up and down by the halo's reach in bands, left
+ *   and right by one strip; looked up once at launch); the other passes, and
+ *   the last pass of every task, end with the grid barrier. AUTO: NEIGHBOR from
+ *   16 blocks on (BARRIER under PK_DBG_BROKEN_BARRIER). TAGGED is refused.   */
 #define PK_EXCHANGE_AUTO 0
 #define PK_EXCHANGE_BARRIER 1
 #define PK_EXCHANGE_NEIGHBOR 2
@@ -201,7 +210,7 @@ typedef struct pk_opts {
                            /* (12 -> 4 + 8), as are red-black passes                */
     int band_rows;         /* STREAM passes: rows per band (a unit is a band x one  */
                            /* strip, one per wave); 0 = automatic                   */
-    int exchange;          /* RESIDENT, REGISTER: PK_EXCHANGE_*                      */
+    int exchange;          /* PK_EXCHANGE_* (tiles; STREAM: BARRIER or NEIGHBOR)   */
     int reserved[4];       /* must be zero                                           */
 } pk_opts;
 
@@ -233,7 +242,7 @@ typedef struct pk_info {
     int strips;             /* STREAM: column strips                                     */
     int barrier;            /* PK_BARRIER_FLAT, _TWO_LEVEL or _XCD                       */
     int pass_sweeps;        /* STREAM: sweeps per pass                                   */
-    int exchange;           /* tiles: PK_EXCHANGE_BARRIER, _NEIGHBOR or _TAGGED; else 0  */
+    int exchange;           /* PK_EXCHANGE_BARRIER, _NEIGHBOR or _TAGGED; LAUNCH: 0      */
     size_t lds_bytes;       /* dynamic LDS per block                                     */
     double kernel_ms;       /* PERSISTENT: launch-to-exit time of the kernel (HIP        */
                             /* events on its stream), valid after EXIT; LAUNCH: total   */

@@ -359,6 +359,16 @@ struct BarrierCtx {
     // device trace (thread 0's view), in the block's shared memory: the state
     // is touched only when an event is recorded, so it takes no registers
     struct TraceState* trace;
+    // streaming passes under neighbour counters, in the block's shared memory
+    // (kernel arguments read inside the task loop would be kept in registers
+    // across every pass)
+    struct PassNbr* pn;
+};
+
+// Neighbour counters between streaming passes: the XCDs this block's neighbours
+// run on, one bit each (0: the passes keep the grid barrier).
+struct PassNbr {
+    uint32_t mask;
 };
 
 // XCD barrier groups as thread 0 sees them: this block's XCD, the blocks on it,
@@ -515,6 +525,67 @@ __device__ __forceinline__ void neighbor_sync(BarrierCtx& bc, uint32_t* nbr, int
                 spin_until(bc, nbr + static_cast<size_t>(lb + d) * PK_NBR_WORDS, target);
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    trace_event(bc, PK_TR_SYNC_LEAVE, 1);
+    bc.nbr_epoch = target;
+    __syncthreads();
+}
+
+// Point-to-point sync between two streaming passes of the same unit
+// decomposition, by neighbour counters kept per XCD. Unit u (band u / strips,
+// strip u % strips) runs on logical block u mod G, so the units whose rows or
+// columns a pass reads, or whose reads of the previous pass the next pass
+// overwrites, sit on the blocks lb + d * strips + e (mod G) for bands d =
+// -dist..dist and strips e = -1..1; at launch every block notes the XCDs those
+// blocks run on (`pn->mask`). After a pass every wave waits for its stores to
+// reach its XCD's L2, thread 0 adds 1 to its XCD's arrival counter, and the
+// XCD's last block writes the L2 back once (agent-scope release) and publishes
+// the pass count for the XCD; the block then waits only for the XCDs in its mask
+// (wave 0, one lane per XCD, one round of loads per poll, bounded in time) and
+// acquires. A block is at most one pass ahead of any block it reads from, which
+// the two field buffers allow. Blocks meet their neighbours' XCDs, never the
+// whole grid ("Persistent Kernels", "Reflections and next steps", GPU-side
+// scheduling on neighbour step counters; "Grid-Wide Barriers and Persistent Work
+// Queues", "What the barrier buys", on every block waiting for the slowest).
+__device__ __forceinline__ void pass_neighbor_sync(BarrierCtx& bc, uint32_t mask) {
+    wait_vm();
+    __syncthreads();
+    const uint32_t target = bc.nbr_epoch + 1;
+    trace_event(bc, PK_TR_SYNC_ARRIVE, 1);
+    if (threadIdx.x < 64) {  // wave 0
+        const int lane = static_cast<int>(threadIdx.x);
+        pk_dev_state* st = bc.st;
+        bool faulted = __shfl(static_cast<int>(bc.faulted), 0, 64) != 0;
+        if (lane == 0 && !faulted) {
+            const uint32_t g = bc.xs->g;
+            const uint32_t old = __hip_atomic_fetch_add(&st->xpass_count[g].v, 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            if (old == target * bc.xs->members - 1u) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __hip_atomic_store(&st->xpass_gen[g].v, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        const bool watch = lane < 8 && ((mask >> lane) & 1u);
+        if (!faulted) {
+            const uint64_t t0 = wall_clock64();
+            for (;;) {
+                const bool ok = !watch ||
+                                static_cast<int32_t>(__hip_atomic_load(&st->xpass_gen[lane & 7].v, __ATOMIC_RELAXED,
+                                                                       __HIP_MEMORY_SCOPE_AGENT) -
+                                                     target) >= 0;
+                if (__all(ok)) break;
+                __builtin_amdgcn_s_sleep(1);
+                if (wall_clock64() - t0 > bc.spin_ticks) {
+                    faulted = true;
+                    if (lane == 0)
+                        __hip_atomic_store(&st->fault, static_cast<uint32_t>(PK_FAULT_BARRIER_TIMEOUT),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        if (lane == 0) bc.faulted = faulted;
     }
     trace_event(bc, PK_TR_SYNC_LEAVE, 1);
     bc.nbr_epoch = target;
@@ -1190,9 +1261,12 @@ __device__ __forceinline__ double stream_residual_block(const pk_kargs& a, const
 // Fixed-order total of the per-block partials, by the first wave of a block;
 // the result is valid in thread 0.
 __device__ __forceinline__ double sum_partials(const double* partials, int grid) {
-    const int lane = threadIdx.x & 63;
+    // the lane's address is formed here, not hoisted out of the task loop and
+    // kept (or spilled) across every other task
+    const int t = thread_id_here();
+    const int lane = t & 63;
     double v = 0.0;
-    if (threadIdx.x < 64)
+    if (t < 64)
         for (int k = lane; k < grid; k += 64) v += partials[k];
     return wave_sum(v);
 }

@@ -35,10 +35,11 @@ struct Plan {
     size_t lds_bytes = 0;
     int xcd_remap = 0;
     int barrier_kind = PK_BARRIER_FLAT;
-    int exchange = 0;  // RESIDENT: PK_EXCHANGE_BARRIER or PK_EXCHANGE_NEIGHBOR
+    int exchange = 0;  // tiles: PK_EXCHANGE_*; persistent STREAM: between passes; LAUNCH: 0
     int pass_sweeps = 1;
     int pband_rows = 1, pbands = 1;
     int march_down = 0;
+    int pass_nbr_strips = 0, pass_nbr_dist = 0;  // STREAM passes under PK_EXCHANGE_NEIGHBOR
     int occ = 0;  // blocks per CU allowed by the occupancy query
 };
 
@@ -361,6 +362,7 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         }
     }
     if (!tiled) {
+        if (o.exchange == PK_EXCHANGE_TAGGED) return PK_EINVAL;  // the register tile's only
         p.layout = PK_LAYOUT_STREAM;
         // the persistent streaming kernel's blocks are as large as its register
         // budget allows (its passes keep up to 12 levels of the march in registers)
@@ -402,6 +404,13 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         // opposite directions and meet on the halo rows they share, in L2
         // (4096^2: 4.15 against 4.18 us with all bands down)
         p.march_down = hbm ? 1 : 0;
+        // how a task's passes meet: neighbour counters per XCD (auto from 16
+        // blocks on; 4096^2 fp32: 4.10 against 4.24 us per sweep with a grid
+        // barrier after every pass, 8192^2 fp64 Poisson: the same), else the
+        // grid barrier (the negative control keeps the barrier it weakens)
+        p.exchange = o.exchange == PK_EXCHANGE_NEIGHBOR || o.exchange == PK_EXCHANGE_BARRIER ? o.exchange
+                     : (p.grid >= 16 && !(o.flags & PK_DBG_BROKEN_BARRIER) ? PK_EXCHANGE_NEIGHBOR
+                                                                              : PK_EXCHANGE_BARRIER);
     }
     {
         const int k = p.pass_sweeps;
@@ -418,6 +427,16 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         if (lim < static_cast<uint64_t>(2 * (k + 1) + 1)) return PK_EINVAL;
         p.pband_rows = static_cast<int>(std::min<uint64_t>(p.pband_rows, lim - 2 * (k + 1)));
         p.pbands = ceil_div(interior, p.pband_rows);
+        // neighbour counters between two full-depth passes: the units of such a
+        // pass and the bands its k-row halo reaches; beyond PK_PASS_NBR_DIST bands
+        // (very short bands) the passes keep the grid barrier
+        if (p.layout == PK_LAYOUT_STREAM && p.exchange == PK_EXCHANGE_NEIGHBOR) {
+            const int dist = ceil_div(k, p.pband_rows);
+            if (dist <= PK_PASS_NBR_DIST) {
+                p.pass_nbr_strips = strips_k;
+                p.pass_nbr_dist = dist;
+            }
+        }
     }
 
     // occupancy of the kernel that will be resident, at its LDS footprint
@@ -471,6 +490,8 @@ void fill_kargs(pk_engine* e) {
     a.pass_sweeps = p.pass_sweeps;
     a.pband_rows = p.pband_rows;
     a.march_down = p.march_down;
+    a.pass_nbr_strips = p.pass_nbr_strips;
+    a.pass_nbr_dist = p.pass_nbr_dist;
     a.pbands = p.pbands;
     a.flags = e->flags;
     a.st = e->d_st;

@@ -634,7 +634,17 @@ __device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, i
                 const double p = block_sum(acc, s_red);
                 if (threadIdx.x == 0) a.partials[static_cast<size_t>(rs.round & 1u) * a.grid + blockIdx.x] = p;
             }
-            grid_barrier(bc, bc.broken);  // also orders the partials before any read
+            // between two full-depth passes (the same units), neighbour counters may
+            // stand in for the grid barrier; a task's last pass, and the passes next
+            // to a shallower one, end with the barrier (it also orders the partials
+            // before any read)
+            const uint32_t nbr_mask = __builtin_amdgcn_readfirstlane(bc.pn->mask);
+            if (nbr_mask != 0 && k == a.pass_sweeps && !res && s + k < n &&
+                pass_depth(a.pass_sweeps, n - s - k, rb) == a.pass_sweeps &&
+                (rb || s + k + a.pass_sweeps < n))
+                pass_neighbor_sync(bc, nbr_mask);
+            else
+                grid_barrier(bc, bc.broken);
             cur ^= 1;
             s += k;
             rs.ready = res;
@@ -734,12 +744,22 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
         s_trace.count = 0;
     }
     bc.trace = &s_trace;
-    if (a.barrier_kind == PK_BARRIER_XCD && a.grid > 1 && !bc.broken) {
-        // count the blocks on each XCD (one flat barrier, generation 1), then
-        // switch to the XCD barrier, whose counters start from zero
+    __shared__ PassNbr s_pn;
+    if (threadIdx.x == 0) s_pn.mask = 0;
+    bc.pn = &s_pn;
+    // neighbour counters between streaming passes (more than one block)
+    const bool pass_nbr = LAYOUT == PK_LAYOUT_STREAM && a.pass_nbr_dist > 0 && a.grid > 1 && !bc.broken;
+    if ((a.barrier_kind == PK_BARRIER_XCD || pass_nbr) && a.grid > 1 && !bc.broken) {
+        // count the blocks on each XCD (one grid barrier of the flat or two-level
+        // kind); the XCD barrier's counters start from zero after it. Under pass
+        // neighbour counters each block also notes its XCD beside its flag.
+        const int lb = logical_block(a.xcd_remap, a.grid);
         if (threadIdx.x == 0) {
             s_xcd.g = __builtin_amdgcn_s_getreg((3 << 11) | 20) & 7u;  // hwreg(HW_REG_XCC_ID, 0, 4)
             __hip_atomic_fetch_add(&a.st->xmembers[s_xcd.g].v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (pass_nbr)
+                __hip_atomic_store(a.nbr + static_cast<size_t>(lb) * PK_NBR_WORDS + 1, s_xcd.g, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
         grid_barrier(bc);
         if (threadIdx.x == 0) {
@@ -751,8 +771,28 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
                                             __HIP_MEMORY_SCOPE_AGENT) > 0u ? 1u : 0u;
             s_xcd.groups = groups;
         }
-        bc.epoch = 0;
-        bc.xcd = true;
+        if (pass_nbr && threadIdx.x < 64) {
+            // the XCDs of the blocks whose units border this block's (see
+            // pass_neighbor_sync): lane i looks up one of them
+            const int lane = static_cast<int>(threadIdx.x), dist = a.pass_nbr_dist, g = a.grid;
+            const int d = lane / 3 - dist, e = lane % 3 - 1;
+            uint32_t x = 8;
+            if (lane < 3 * (2 * dist + 1)) {
+                int q = static_cast<int>((static_cast<int64_t>(lb) + static_cast<int64_t>(d) * a.pass_nbr_strips + e) % g);
+                if (q < 0) q += g;
+                if (q != lb)
+                    x = __hip_atomic_load(a.nbr + static_cast<size_t>(q) * PK_NBR_WORDS + 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+            }
+            uint32_t mask = 0;
+            for (uint32_t k = 0; k < 8; ++k)
+                if (__any(x == k)) mask |= 1u << k;
+            if (lane == 0) s_pn.mask = mask;
+        }
+        if (a.barrier_kind == PK_BARRIER_XCD) {
+            bc.epoch = 0;
+            bc.xcd = true;
+        }
     }
 
     const bool leader = (blockIdx.x == 0) && (threadIdx.x == 0);

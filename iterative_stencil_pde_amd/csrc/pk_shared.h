@@ -138,12 +138,22 @@ struct pk_dev_state {
     pk_word256 xmembers[8];
     pk_word256 xgrp_count[8];
     pk_word256 xgrp_gen[8];
+    // streaming passes under neighbour counters: arrivals per XCD, and the passes
+    // whose stores the XCD has written back
+    pk_word256 xpass_count[8];
+    pk_word256 xpass_gen[8];
 };
 
 // Kernel arguments (passed by value).
 // Words per neighbour-exchange flag: one 128-byte line per block, so a
-// block's store does not touch the line its neighbours poll.
+// block's store does not touch the line its neighbours poll. (Word 1 holds the
+// block's XCD when the streaming passes use neighbour counters.)
 #define PK_NBR_WORDS 32
+// Streaming passes synchronised by neighbour counters: bands a pass's halo may
+// reach on each side (the 3 (2 d + 1) neighbouring blocks are looked up at launch
+// by the 64 lanes of one wave); deeper reaches (bands shorter than a tenth of the
+// pass depth) keep the grid barrier.
+#define PK_PASS_NBR_DIST 10
 
 struct pk_kargs {
     void* u[2];            // the two field buffers (ny rows x pitch elements)
@@ -156,6 +166,8 @@ struct pk_kargs {
     int pass_sweeps;       // sweeps per pass in the stream layout (1 = one per barrier)
     int pband_rows, pbands;
     int march_down;        // passes: every band but the last marches down (else directions alternate)
+    int pass_nbr_strips;   // passes synchronised by neighbour counters: strips of a full-depth pass
+    int pass_nbr_dist;     // and the bands its halo reaches on each side (0: grid barrier after every pass)
     // resident and register geometry: one band per block, the interior split
     // into bands of res_q or res_q + 1 rows (the first res_rem bands are longer)
     int res_q, res_rem;
@@ -178,7 +190,8 @@ struct pk_kargs {
     void* staging;         // readback target (pinned host, device-visible)
     uint32_t* stamp;       // 2 x grid x 64 words for the visibility check
     uint32_t* nbr;         // neighbour exchange flags, PK_NBR_WORDS words per block
-    int exchange;          // PK_EXCHANGE_BARRIER, _NEIGHBOR or _TAGGED (tiles)
+    int exchange;          // tiles: PK_EXCHANGE_BARRIER, _NEIGHBOR or _TAGGED; STREAM
+                           // (persistent): _BARRIER or _NEIGHBOR between passes
     uint64_t* tag;         // tagged halo words: 2 parities x ny rows x tag_pitch words
     int tag_pitch;         // words per row: 4 planes of one word per 16-byte vector
     uint64_t tag_ticks;    // longest wait for a tagged halo word (device clock ticks)

@@ -173,8 +173,10 @@ AUTO_PLANS = {
     "laplace64": dict(layout=pk.PK_LAYOUT_RESIDENT, grid_blocks=1),
     "poisson256": dict(layout=pk.PK_LAYOUT_REGISTER, exchange=pk.PK_EXCHANGE_TAGGED, threads=1024),
     "laplace1024": dict(layout=pk.PK_LAYOUT_REGISTER, exchange=pk.PK_EXCHANGE_TAGGED, threads=1024),
-    "laplace4096": dict(layout=pk.PK_LAYOUT_STREAM, pass_sweeps=8, threads=512, grid_blocks=256),
-    "poisson8192": dict(layout=pk.PK_LAYOUT_STREAM, pass_sweeps=12, threads=512, grid_blocks=256),
+    "laplace4096": dict(layout=pk.PK_LAYOUT_STREAM, pass_sweeps=8, threads=512, grid_blocks=256,
+                        exchange=pk.PK_EXCHANGE_NEIGHBOR),
+    "poisson8192": dict(layout=pk.PK_LAYOUT_STREAM, pass_sweeps=12, threads=512, grid_blocks=256,
+                        exchange=pk.PK_EXCHANGE_NEIGHBOR),
 }
 
 
@@ -228,6 +230,35 @@ def test_device_trace(name, layout):
     say(f"  {name}: layout={info.layout} events/block={sorted(counts)[:3]} work={s['work'].get('mean')} "
         f"wait={s['sync_wait'].get('mean')} tag={s['tag_wait'].get('mean')} period={s['period'].get('mean')}")
     assert s["work"]["count"] > 0
+
+
+def test_stream_neighbor_counters_replace_the_pass_barriers():
+    """Under PK_EXCHANGE_NEIGHBOR the streaming passes of one task meet through
+    neighbour counters: 40 sweeps in passes of 4 take 8 neighbour syncs (between
+    full-depth passes) and grid barriers only around the task's last two passes
+    (the last one sums the residual, one level deeper); the field is the oracle's."""
+    from iterative_stencil_pde_amd import trace
+    w = inputs.make("laplace1024")
+    with pk.Engine(w.u0, w.f, h=w.h, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=4,
+                   exchange=pk.PK_EXCHANGE_NEIGHBOR, flags=pk.PK_DBG_TRACE) as e:
+        info = e.info()
+        assert info.exchange == pk.PK_EXCHANGE_NEIGHBOR
+        e.sweep(40)
+        got = e.readback()
+        e.wait(e.submit(pk.PK_EXIT))
+        raw = e.trace()
+    ref, _ = oracle.jacobi(w.u0, 40, f=w.f, h=w.h)
+    assert np.array_equal(got, ref)
+    blocks = trace.decode(raw, info.grid_blocks, info.trace_capacity)
+    for ev in blocks:
+        kinds = [int(k) for k in ev["kind"]]
+        aux = [int(a) for a in ev["aux"]]
+        nbr = sum(1 for k, a in zip(kinds, aux) if k == trace.SYNC_ARRIVE and a == 1)
+        assert nbr == 8, nbr
+        assert kinds.count(trace.SYNC_ARRIVE) == kinds.count(trace.SYNC_LEAVE)
+    s = trace.summarize(raw, info.grid_blocks, info.trace_capacity, info.wall_clock_khz)
+    say(f"  G={info.grid_blocks} k={info.pass_sweeps} work={s['work'].get('mean')} "
+        f"wait={s['sync_wait'].get('mean')}")
 
 
 def test_trace_needs_the_flag():

@@ -25,6 +25,8 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 MODES = {
     "persistent-auto": dict(mode=pk.PK_PERSISTENT),
     "persistent-stream": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM),
+    "stream-neighbor": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, exchange=pk.PK_EXCHANGE_NEIGHBOR),
+    "stream-barrier": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, exchange=pk.PK_EXCHANGE_BARRIER),
     "launch": dict(mode=pk.PK_LAUNCH),
 }
 
@@ -133,13 +135,17 @@ def test_resident_layout_refused_when_bands_do_not_fit():
 @pytest.mark.parametrize("barrier", [pk.PK_BARRIER_FLAT, pk.PK_BARRIER_TWO_LEVEL, pk.PK_BARRIER_XCD],
                          ids=["flat", "two_level", "xcd"])
 @pytest.mark.parametrize("layout", [pk.PK_LAYOUT_STREAM, pk.PK_LAYOUT_RESIDENT], ids=["stream", "resident"])
-def test_both_barrier_kinds(barrier, layout):
+@pytest.mark.parametrize("exchange", [pk.PK_EXCHANGE_BARRIER, pk.PK_EXCHANGE_NEIGHBOR], ids=["barrier", "neighbor"])
+def test_both_barrier_kinds(barrier, layout, exchange):
+    """Every grid barrier kind, with passes (or tile exchanges) meeting at the
+    barrier or through neighbour counters (which count the blocks per XCD at
+    launch with a barrier of the engine's kind)."""
     w = inputs.laplace_random_interior(1024, 0)
     w.script = [("residual",), ("sweep", 37), ("residual",), ("sweep", 100), ("residual",), ("readback",)]
     ref = run_oracle_script(w)
-    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=layout, barrier=barrier)
-    assert got["info"].barrier == barrier
-    check_against_oracle(w, got, ref, f"barrier{barrier}/layout{layout}")
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=layout, barrier=barrier, exchange=exchange)
+    assert got["info"].barrier == barrier and got["info"].exchange == exchange
+    check_against_oracle(w, got, ref, f"barrier{barrier}/layout{layout}/exchange{exchange}")
 
 
 @pytest.mark.parametrize("name,sweeps", [("laplace4096", 30), ("poisson8192", 4)])
@@ -147,7 +153,7 @@ def test_xcd_barrier_full_size(name, sweeps):
     w = inputs.make(name)
     w.script = [("sweep", sweeps), ("residual",), ("readback",)]
     ref = run_oracle_script(w)
-    got = run_engine_script(w, mode=pk.PK_PERSISTENT, barrier=pk.PK_BARRIER_XCD)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, barrier=pk.PK_BARRIER_XCD, exchange=pk.PK_EXCHANGE_BARRIER)
     assert got["info"].barrier == pk.PK_BARRIER_XCD and got["info"].grid_blocks == 256
     check_against_oracle(w, got, ref, f"{name}/xcd")
 
@@ -194,6 +200,35 @@ def test_deep_pass_splitting(shape, dtype, poisson):
     check_against_oracle(w, got, ref, f"deep/{ny}x{nx}/{np.dtype(dtype).name}")
 
 
+NBR_SCRIPT = [("sweep", 40), ("residual",), ("sweep", 29), ("sweep_rb", 9), ("residual",), ("sweep", 3),
+              ("residual",), ("sweep", 64), ("readback",)]
+
+
+@pytest.mark.parametrize("k,band_rows,blocks", [(8, 0, 0), (3, 0, 0), (12, 0, 0), (1, 0, 7), (8, 2, 0),
+                                                (12, 3, 0), (4, 1, 5), (12, 1, 0), (8, 0, 3)],
+                         ids=lambda v: str(v))
+@pytest.mark.parametrize("poisson", [False, True], ids=["laplace", "poisson"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("shape", [(130, 257), (200, 517), (61, 1030)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_stream_neighbor_counters(shape, dtype, poisson, k, band_rows, blocks):
+    """Streaming passes that meet their neighbours through pass counters instead
+    of a grid barrier: bands of 1 to 3 rows (the halo reaching up to 12 bands; past
+    10 the passes keep the barrier), several units per wave, grids that are not
+    multiples of 8 blocks, red-black tasks and tasks whose last passes are
+    shallower, against the oracle."""
+    ny, nx = shape
+    u, f = _random_case(ny, nx, dtype, poisson, seed=13 * ny + nx + k)
+    w = inputs.Workload(f"nbr{ny}x{nx}", nx, ny, dtype, 0.013, u, f, list(NBR_SCRIPT), "")
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=k,
+                            band_rows=band_rows, max_blocks=blocks, exchange=pk.PK_EXCHANGE_NEIGHBOR)
+    info = got["info"]
+    assert info.pass_sweeps == k and info.exchange == pk.PK_EXCHANGE_NEIGHBOR
+    if blocks:
+        assert info.grid_blocks == blocks
+    check_against_oracle(w, got, ref, f"nbr/k{k}/rows{band_rows}/g{info.grid_blocks}/{ny}x{nx}")
+
+
 @pytest.mark.parametrize("name,sweeps,k", [("laplace4096", 41, 4), ("laplace4096", 23, 3), ("laplace4096", 37, 8),
                                            ("poisson8192", 5, 2), ("poisson8192", 7, 3), ("poisson8192", 9, 4),
                                            ("poisson8192", 13, 8), ("poisson8192", 11, 6),
@@ -203,9 +238,10 @@ def test_stream_passes_full_size(name, sweeps, k):
     w = inputs.make(name)
     w.script = [("sweep", sweeps), ("residual",), ("readback",)]
     ref = run_oracle_script(w)
-    got = run_engine_script(w, mode=pk.PK_PERSISTENT, pass_sweeps=k)
-    assert got["info"].pass_sweeps == k
-    check_against_oracle(w, got, ref, f"{name}/pass{k}")
+    for exchange in (pk.PK_EXCHANGE_BARRIER, pk.PK_EXCHANGE_NEIGHBOR):
+        got = run_engine_script(w, mode=pk.PK_PERSISTENT, pass_sweeps=k, exchange=exchange)
+        assert got["info"].pass_sweeps == k and got["info"].exchange == exchange
+        check_against_oracle(w, got, ref, f"{name}/pass{k}/exchange{exchange}")
 
 
 @pytest.mark.parametrize("layout", [pk.PK_LAYOUT_REGISTER, pk.PK_LAYOUT_RESIDENT], ids=["register", "lds"])
@@ -394,6 +430,8 @@ def _tol_between(w, every, j):
 UNTIL_MODES = {
     "auto": dict(mode=pk.PK_PERSISTENT),
     "stream3": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=3),
+    "stream3-neighbor": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=3,
+                             exchange=pk.PK_EXCHANGE_NEIGHBOR),
     "register": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_REGISTER, max_blocks=32),
     "tagged": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_REGISTER, max_blocks=64, halo_depth=9,
                    exchange=pk.PK_EXCHANGE_TAGGED),
@@ -499,6 +537,8 @@ RB_MODES = {
     "stream3": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=3),
     "stream4": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=4),
     "stream7": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=7),
+    "stream4-neighbor": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=4,
+                             exchange=pk.PK_EXCHANGE_NEIGHBOR),
     "register": dict(mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_REGISTER),
     "launch": dict(mode=pk.PK_LAUNCH),
 }
@@ -646,7 +686,7 @@ def _check_every_cell(w, field, g, tol_rel):
     assert err <= tol_rel * rng
 
 
-@pytest.mark.parametrize("mode", ["persistent-auto", "launch"])
+@pytest.mark.parametrize("mode", ["persistent-auto", "stream-barrier", "launch"])
 def test_laplace4096_full(mode):
     w = inputs.make("laplace4096")
     g = _golden("laplace4096")
@@ -661,7 +701,7 @@ def test_laplace4096_full(mode):
     assert np.array_equal(f, f[:, ::-1])
 
 
-@pytest.mark.parametrize("mode", ["persistent-auto", "launch"])
+@pytest.mark.parametrize("mode", ["persistent-auto", "stream-barrier", "launch"])
 def test_poisson8192_full(mode):
     w = inputs.make("poisson8192")
     g = _golden("poisson8192")
@@ -678,7 +718,7 @@ def test_full_size_short_run_whole_array(name, sweeps):
     w.script = [("residual",), ("sweep", sweeps // 2), ("residual",), ("sweep", sweeps - sweeps // 2),
                 ("residual",), ("readback",)]
     ref = run_oracle_script(w)
-    for mode in ("persistent-auto", "launch"):
+    for mode in ("persistent-auto", "stream-barrier", "launch"):
         got = run_engine_script(w, **MODES[mode])
         check_against_oracle(w, got, ref, f"{name}/{mode}")
 
