@@ -53,19 +53,23 @@ def intervals(blocks: list, tick_us: float) -> dict:
     """Durations in us, pooled over blocks:
       work      from a task's start or a sync's departure to the next arrival
       sync_wait from arrival at a grid barrier or neighbour sync to departure
+                (also split: barrier_wait, neighbor_wait; the event's aux is 0
+                for a grid barrier, 1 for a neighbour sync)
       tag_wait  wave 0's polls for tagged halo words
       period    a tile period, from its start to the next period, tag poll or sync
     and, per synchronization (the i-th of every block), the spread of the blocks'
     arrival times (the slowest block's lead over the fastest)."""
     work, wait, tag, period = [], [], [], []
+    by_kind = {0: [], 1: []}
     arrivals = []
     for ev in blocks:
         t_from = None      # start of the current work interval
         t_arrive = None
+        a_arrive = 0
         t_tag = None
         t_period = None
         mine = []
-        for t, kind, _aux in ev:
+        for t, kind, aux in ev:
             t = int(t)
             if kind == TASK_BEGIN:
                 t_from = t
@@ -76,10 +80,12 @@ def intervals(blocks: list, tick_us: float) -> dict:
                     period.append(t - t_period)
                     t_period = None
                 t_arrive = t
+                a_arrive = int(aux)
                 mine.append(t)
             elif kind == SYNC_LEAVE:
                 if t_arrive is not None:
                     wait.append(t - t_arrive)
+                    by_kind.setdefault(a_arrive, []).append(t - t_arrive)
                 t_arrive = None
                 t_from = t
             elif kind == TAG_WAIT:
@@ -105,8 +111,9 @@ def intervals(blocks: list, tick_us: float) -> dict:
         arr = np.array([a[:n] for a in arrivals], dtype=np.float64)
         spread = list(arr.max(axis=0) - arr.min(axis=0))
     scale = lambda v: np.asarray(v, dtype=np.float64) * tick_us  # noqa: E731
-    return {"work": scale(work), "sync_wait": scale(wait), "tag_wait": scale(tag),
-            "period": scale(period), "arrival_spread": scale(spread)}
+    return {"work": scale(work), "sync_wait": scale(wait), "barrier_wait": scale(by_kind[0]),
+            "neighbor_wait": scale(by_kind[1]), "tag_wait": scale(tag), "period": scale(period),
+            "arrival_spread": scale(spread)}
 
 
 def stats(v: np.ndarray, bins: int = 8) -> dict:
@@ -137,9 +144,14 @@ def main():
     ap.add_argument("--sweeps", type=int, default=400)
     ap.add_argument("--residual-every", type=int, default=0,
                     help="a RESIDUAL task after every this many sweeps (0: none)")
+    ap.add_argument("--exchange", default="auto", choices=["auto", "barrier", "neighbor"],
+                    help="how passes (or tile exchanges) meet: the planner's choice, grid barrier, "
+                         "or neighbour counters")
     args = ap.parse_args()
     w = inputs.make(args.workload)
-    with pk.Engine(w.u0, w.f, h=w.h, flags=pk.PK_DBG_TRACE) as e:
+    exchange = {"auto": pk.PK_EXCHANGE_AUTO, "barrier": pk.PK_EXCHANGE_BARRIER,
+                "neighbor": pk.PK_EXCHANGE_NEIGHBOR}[args.exchange]
+    with pk.Engine(w.u0, w.f, h=w.h, flags=pk.PK_DBG_TRACE, exchange=exchange) as e:
         info = e.info()
         e.sweep(8)  # warm-up, then one traced stretch
         every = args.residual_every or args.sweeps

@@ -37,6 +37,7 @@ def test_intervals_work_wait_and_arrival_spread():
     assert np.allclose(sorted(iv["work"]), [0.9, 1.0, 1.0, 1.05])
     assert np.allclose(sorted(iv["sync_wait"]), [0.05, 0.05, 0.1, 0.15])
     assert np.allclose(iv["arrival_spread"], [0.05, 0.1])
+    assert np.allclose(sorted(iv["barrier_wait"]), [0.05, 0.05, 0.1, 0.15]) and len(iv["neighbor_wait"]) == 0
     s = T.summarize(raw, 2, 8, wall_clock_khz=100000)
     assert s["events"] == 12 and s["wrapped_blocks"] == 0
     assert abs(s["sync_wait_share"] - 0.35 / (0.35 + 3.95)) < 1e-4  # rounded to 4 digits
@@ -54,3 +55,16 @@ def test_intervals_tile_periods_and_tag_polls():
     assert len(iv["arrival_spread"]) == 0  # one block: no spread
     st = T.stats(iv["period"], bins=2)
     assert st["count"] == 3 and st["max"] == 40 and sum(st["histogram"]["counts"]) == 3
+
+
+def test_waits_split_by_synchronization_kind():
+    """aux 0 marks a grid barrier, aux 1 a neighbour sync (tile exchanges and the
+    streaming passes' neighbour counters)."""
+    T = trace
+    blk = [(0, T.TASK_BEGIN, 1), (100, T.SYNC_ARRIVE, 1), (104, T.SYNC_LEAVE, 1),
+           (200, T.SYNC_ARRIVE, 1), (203, T.SYNC_LEAVE, 1), (300, T.SYNC_ARRIVE, 0),
+           (320, T.SYNC_LEAVE, 0), (321, T.TASK_END, 1)]
+    iv = T.intervals(T.decode(ring(blk, 16), 1, 16), tick_us=1.0)
+    assert list(iv["neighbor_wait"]) == [4, 3] and list(iv["barrier_wait"]) == [20]
+    assert sorted(iv["sync_wait"]) == [3, 4, 20]
+    assert list(iv["work"]) == [100, 96, 97]
