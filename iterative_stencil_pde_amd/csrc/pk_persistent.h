@@ -638,11 +638,10 @@ __device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, i
             // stand in for the grid barrier; a task's last pass, and the passes next
             // to a shallower one, end with the barrier (it also orders the partials
             // before any read)
-            const uint32_t nbr_mask = __builtin_amdgcn_readfirstlane(bc.pn->mask);
-            if (nbr_mask != 0 && k == a.pass_sweeps && !res && s + k < n &&
+            if (__builtin_amdgcn_readfirstlane(bc.pn->on) && k == a.pass_sweeps && !res && s + k < n &&
                 pass_depth(a.pass_sweeps, n - s - k, rb) == a.pass_sweeps &&
                 (rb || s + k + a.pass_sweeps < n))
-                pass_neighbor_sync(bc, nbr_mask);
+                pass_neighbor_sync(bc, __builtin_amdgcn_readfirstlane(bc.pn->mask));
             else
                 grid_barrier(bc, bc.broken);
             cur ^= 1;
@@ -745,7 +744,10 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
     }
     bc.trace = &s_trace;
     __shared__ PassNbr s_pn;
-    if (threadIdx.x == 0) s_pn.mask = 0;
+    if (threadIdx.x == 0) {
+        s_pn.on = 0;
+        s_pn.mask = 0;
+    }
     bc.pn = &s_pn;
     // neighbour counters between streaming passes (more than one block)
     const bool pass_nbr = LAYOUT == PK_LAYOUT_STREAM && a.pass_nbr_dist > 0 && a.grid > 1 && !bc.broken;
@@ -772,22 +774,43 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
             s_xcd.groups = groups;
         }
         if (pass_nbr && threadIdx.x < 64) {
-            // the XCDs of the blocks whose units border this block's (see
-            // pass_neighbor_sync): lane i looks up one of them
+            // the XCDs of the blocks holding the units next to this block's units in
+            // a full-depth pass (see pass_neighbor_sync): for each unit of the
+            // block, lane i looks up one neighbour (band d, strip e) and, where that
+            // is a split edge unit, the block of its bottom half too
             const int lane = static_cast<int>(threadIdx.x), dist = a.pass_nbr_dist, g = a.grid;
+            const int S = a.pass_nbr_strips, NB = a.pbands, units = S * NB;
+            const bool split = pass_split_edges(S, NB, g * (static_cast<int>(blockDim.x) >> 6));
+            const int total = units + (split ? 2 * NB : 0);
             const int d = lane / 3 - dist, e = lane % 3 - 1;
-            uint32_t x = 8;
-            if (lane < 3 * (2 * dist + 1)) {
-                int q = static_cast<int>((static_cast<int64_t>(lb) + static_cast<int64_t>(d) * a.pass_nbr_strips + e) % g);
-                if (q < 0) q += g;
-                if (q != lb)
-                    x = __hip_atomic_load(a.nbr + static_cast<size_t>(q) * PK_NBR_WORDS + 1, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-            }
             uint32_t mask = 0;
-            for (uint32_t k = 0; k < 8; ++k)
-                if (__any(x == k)) mask |= 1u << k;
-            if (lane == 0) s_pn.mask = mask;
+            for (int u = lb; u < total; u += g) {
+                int band, strip, half;
+                pass_unit_place(u, S, units, band, strip, half);
+                const int b2 = band + d, s2 = strip + e;
+                uint32_t x0 = 8, x1 = 8;
+                if (lane < 3 * (2 * dist + 1) && b2 >= 0 && b2 < NB && s2 >= 0 && s2 < S) {
+                    const int q0 = (b2 * S + s2) % g;
+                    if (q0 != lb)
+                        x0 = __hip_atomic_load(a.nbr + static_cast<size_t>(q0) * PK_NBR_WORDS + 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    if (split && (s2 == 0 || s2 == S - 1)) {
+                        const int q1 = (units + 2 * b2 + (s2 == 0 ? 0 : 1)) % g;
+                        if (q1 != lb)
+                            x1 = __hip_atomic_load(a.nbr + static_cast<size_t>(q1) * PK_NBR_WORDS + 1,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+                for (uint32_t k = 0; k < 8; ++k)
+                    if (__any(x0 == k || x1 == k)) mask |= 1u << k;
+            }
+            // and its own XCD: a block must not arrive at its XCD's counter for the
+            // next pass before every block of that XCD has arrived for this one (the
+            // last-arrival test counts arrivals pass by pass)
+            if (lane == 0) {
+                s_pn.on = 1;
+                s_pn.mask = mask | (1u << s_xcd.g);
+            }
         }
         if (a.barrier_kind == PK_BARRIER_XCD) {
             bc.epoch = 0;
