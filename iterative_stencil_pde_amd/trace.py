@@ -153,16 +153,28 @@ def main():
                 "neighbor": pk.PK_EXCHANGE_NEIGHBOR}[args.exchange]
     with pk.Engine(w.u0, w.f, h=w.h, flags=pk.PK_DBG_TRACE, exchange=exchange) as e:
         info = e.info()
-        e.sweep(8)  # warm-up, then one traced stretch
+        # a warm-up task, then the traced stretch, queued ahead of the device (up to
+        # 48 tasks in flight, within the 64-slot ring), so that no task waits for
+        # the host between them
+        pending = []
+
+        def queue(kind, n=0):
+            if len(pending) >= 48:
+                e.wait(pending.pop(0))
+            pending.append(e.submit(kind, n))
+
+        queue(pk.PK_SWEEP, 8)
         every = args.residual_every or args.sweeps
         done = 0
         while done < args.sweeps:
             k = min(every, args.sweeps - done)
-            e.sweep(k)
+            queue(pk.PK_SWEEP, k)
             if args.residual_every:
-                e.residual()
+                queue(pk.PK_RESIDUAL)
             done += k
-        e.wait(e.submit(pk.PK_EXIT))
+        queue(pk.PK_EXIT)
+        for t in pending:
+            e.wait(t)
         raw = e.trace()
         info = e.info()
     out = {"workload": w.name, "sweeps": args.sweeps, "residual_every": args.residual_every,

@@ -229,6 +229,25 @@ def test_stream_neighbor_counters(shape, dtype, poisson, k, band_rows, blocks):
     check_against_oracle(w, got, ref, f"nbr/k{k}/rows{band_rows}/g{info.grid_blocks}/{ny}x{nx}")
 
 
+@pytest.mark.parametrize("blocks", [12, 24, 40])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
+def test_stream_neighbor_counters_blocks_without_units(blocks, dtype):
+    """More blocks than units (a 130x257 grid in passes of 12: 3 strips x 2 bands,
+    the 4 edge units split in halves): the blocks that hold no unit, and blocks
+    whose neighbours all run on other XCDs, still wait for their own XCD after
+    every pass, so no block arrives at its XCD's counter for the next pass before
+    the rest of its XCD has arrived for this one."""
+    ny, nx = 130, 257
+    u, f = _random_case(ny, nx, dtype, False, seed=blocks)
+    w = inputs.Workload(f"idle{ny}x{nx}", nx, ny, dtype, 0.013, u, f,
+                        [("sweep", 61), ("residual",), ("sweep", 37), ("readback",)], "")
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=12,
+                            max_blocks=blocks, exchange=pk.PK_EXCHANGE_NEIGHBOR)
+    assert got["info"].grid_blocks == blocks and got["info"].exchange == pk.PK_EXCHANGE_NEIGHBOR
+    check_against_oracle(w, got, ref, f"idle-blocks/{blocks}/{np.dtype(dtype).name}")
+
+
 @pytest.mark.parametrize("name,sweeps,k", [("laplace4096", 41, 4), ("laplace4096", 23, 3), ("laplace4096", 37, 8),
                                            ("poisson8192", 5, 2), ("poisson8192", 7, 3), ("poisson8192", 9, 4),
                                            ("poisson8192", 13, 8), ("poisson8192", 11, 6),
