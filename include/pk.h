@@ -203,8 +203,8 @@ typedef struct pk_opts {
     int barrier;           /* PK_BARRIER_*                                           */
     int pass_sweeps;       /* STREAM: sweeps per pass, 1..8 or 12 (else            */
                            /* PK_EINVAL): each wave carries k levels of its band in */
-                           /* registers, so the field crosses HBM and the grid      */
-                           /* barrier once per k sweeps; 0 = 12 where u, u' and b   */
+                           /* registers, so the field crosses HBM and the blocks    */
+                           /* meet once per k sweeps; 0 = 12 where u, u' and b      */
                            /* exceed the 256 MiB Infinity Cache, else 8 (pk_info    */
                            /* reports it). A task's last pass is at most 8 deep     */
                            /* (12 -> 4 + 8), as are red-black passes                */
