@@ -860,9 +860,9 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
 //     padding column, so the march keeps just that one element (one per-lane
 //     blend a level) instead of checking every element: padding and outside
 //     columns feed only the ring columns, which are kept.
-//     (The edge strips' waves finish last and hold the pass's barrier: with
-//     them on the INNER march's cost, 4096^2 ran 14% faster; with one blend a
-//     level, 4.48 -> 4.22 us per sweep.)
+//     (The edge strips' waves finish last and hold up the pass: with them on
+//     the INNER march's cost, 4096^2 ran 14% faster; with one blend a level,
+//     4.48 -> 4.22 us per sweep.)
 //
 // RES: the pass also sums rho^2 of its result (the residual of the field it
 // stores, as a RESIDUAL task would compute it, element by element the same

@@ -163,7 +163,7 @@ struct pk_kargs {
     // stream geometry: unit = (band, strip); strip = 64 lanes x vector width
     int strips, bands, band_rows;
     // passes of several sweeps: rows per band and bands (strips depend on k)
-    int pass_sweeps;       // sweeps per pass in the stream layout (1 = one per barrier)
+    int pass_sweeps;       // sweeps per pass in the stream layout (1 = a pass per sweep)
     int pband_rows, pbands;
     int march_down;        // passes: every band but the last marches down (else directions alternate)
     int pass_nbr_strips;   // passes synchronised by neighbour counters: strips of a full-depth pass
