@@ -225,24 +225,72 @@ def default_depth(w):
     return pk.PK_MAX_PASS if streamed > MALL_BYTES else SHALLOW_PASS
 
 
-def script_counts(w, pass_sweeps):
+def fuses(w, pass_sweeps):
+    """Whether a persistent streaming engine runs a SWEEP task's last pass on into
+    the next SWEEP task (a RESIDUAL between them summed inside that pass): the fp64
+    kernels at depth 12, where the tasks are queued ahead (the bench keeps the ring
+    full)."""
+    return np.dtype(w.dtype) == np.float64 and pass_sweeps == pk.PK_MAX_PASS
+
+
+def script_counts(w, pass_sweeps, fuse=None, stats=None):
     """(sweeps, passes, residual reads) of one step of a persistent streaming
-    engine: each SWEEP task runs the passes of pass_depths (k = 1: one pass per
-    sweep); a RESIDUAL right after a Jacobi SWEEP task of n > 0 sweeps reads
-    nothing (its partials were summed by that task's last pass), any other reads
-    u and b."""
-    sweeps = passes = residuals = 0
-    fused = False
-    for s in step_tasks(w):
-        if s[0] == "residual":
-            residuals += 0 if fused else 1
-            fused = False
-        else:
-            rb = s[0] == "sweep_rb"
-            n = s[1] * (2 if rb else 1)  # red-black: two half-sweeps
-            sweeps += s[1]
-            passes += len(pass_depths(n, max(1, pass_sweeps), rb))
-            fused = not rb and n > 0 and pass_sweeps > 1
+    engine, as the kernel plans it: each SWEEP task runs the passes of pass_depths
+    (k = 1: one pass per sweep); a RESIDUAL right after a Jacobi SWEEP task of
+    n > 0 sweeps reads nothing (its partials were summed by that task's last pass),
+    any other reads u and b. With fusion (fuses()): a SWEEP task with more than P
+    sweeps left runs P-deep passes (exactly P left: an 8-deep pass first), and where
+    its tail of fewer than P sweeps is followed by a RESIDUAL and a SWEEP of at
+    least the rest of a pass, that tail runs as one P-deep pass that also applies
+    the first sweeps of the later task and sums the RESIDUAL on the way. `stats`
+    (a dict), if given, receives the number of such fused tails ("fused")."""
+    if fuse is None:
+        fuse = fuses(w, pass_sweeps)
+    tasks = step_tasks(w)
+    P = max(1, pass_sweeps)
+    sweeps = passes = residuals = fused_tails = 0
+    ready = False  # the last pass summed the residual of the field as it is now
+    pre = 0        # sweeps of the next SWEEP task already applied
+    for idx, t in enumerate(tasks):
+        if t[0] == "residual":
+            residuals += 0 if ready else 1
+            ready = False
+            continue
+        rb = t[0] == "sweep_rb"
+        sweeps += t[1]
+        n = t[1] * (2 if rb else 1)  # red-black: two half-sweeps
+        if not rb:
+            n -= pre
+        pre = 0
+        fz = fuse and not rb and P == pk.PK_MAX_PASS
+        s, fused, ran = 0, False, False
+        while s < n:
+            left = n - s
+            if fused:
+                k = P
+            elif fz and left == P:
+                k = SHALLOW_PASS
+            elif fz and left > P:
+                k = P
+            else:
+                k = pass_depths(left, P, rb)[0]
+            own = left if fused else k
+            passes += 1
+            ran = True
+            res = not fused and s + k >= n and not rb and P > 1
+            if fused:
+                pre = P - left
+                fused_tails += 1
+            decide = fz and not fused and s + own < n and n - (s + own) < P
+            ready = res or fused
+            s += own
+            nxt = tasks[idx + 1:idx + 3]
+            fused = decide and len(nxt) == 2 and nxt[0][0] == "residual" and nxt[1][0] == "sweep" \
+                and nxt[1][1] >= P - (n - s)
+        if rb and ran:
+            ready = False
+    if stats is not None:
+        stats["fused"] = fused_tails
     return sweeps, passes, residuals
 
 
@@ -358,6 +406,8 @@ def roofline_stream(w, r, steps, warmup, traffic_key):
     per_sweep, step_pass = algorithmic_bytes(w, k)
     pure_pass = algorithmic_bytes(sweeps_only(w), k)[1]
     n_script = steps + warmup
+    model = {}
+    script_counts(w, k, stats=model)
     launch_alg = n_script * step_pass + (steps * pure_pass if r["pure_dt"] is not None else 0)
     launch_sweeps = w.sweeps * (n_script + (steps if r["pure_dt"] is not None else 0))
     kernel_s = end.kernel_ms / 1e3
@@ -378,6 +428,9 @@ def roofline_stream(w, r, steps, warmup, traffic_key):
         "algorithmic_unit": "one pass of up to k sweeps: u read and written once, b read once; a residual "
                             "not summed by the pass before it reads u and b",
         "algorithmic_bytes_per_launch": launch_alg,
+        # SWEEP tasks whose tail ran on into the next SWEEP task: the pass count above
+        # assumes the model's number, the device reports how many it fused
+        "fused_tails": {"model": model["fused"] * n_script, "device": int(end.tasks_fused)},
         "counter_GBps": round(traffic / kernel_s / 1e9, 2) if traffic else None,
         "counter_frac": round(traffic / kernel_s / 1e9 / HBM_PEAK_GBS, 4) if traffic else None,
         "counter_to_algorithmic": round(traffic / launch_alg, 4) if traffic else None,
@@ -659,7 +712,8 @@ def run(args, w, opts, traffic_key, rt):
             "speedup_persistent": round(value / lvalue, 3),
             "speedup_persistent_vs_graph": round(lgraph / us_iter, 3) if lgraph else None,
         },
-        "overheads": dict(fixed, tasks_carried=int(end.tasks_carried), tasks_done=int(end.tasks_done)),
+        "overheads": dict(fixed, tasks_carried=int(end.tasks_carried), tasks_done=int(end.tasks_done),
+                          tasks_fused=int(end.tasks_fused)),
         "roofline": roof,
     }
     if not args.no_extra and args.workload == "poisson8192" and args.method == "jacobi":

@@ -256,6 +256,10 @@ typedef struct pk_info {
     int wall_clock_khz;      /* rate of the device wall clock that task times and the   */
                              /* trace count in                                           */
     int trace_capacity;      /* PK_DBG_TRACE: events each block's ring holds; else 0   */
+    int64_t tasks_fused;     /* PERSISTENT, STREAM: SWEEP tasks whose last pass ran on  */
+                             /* into the SWEEP task two slots later, the RESIDUAL task */
+                             /* between them summed inside that pass (the host had     */
+                             /* queued both ahead)                                      */
 } pk_info;
 
 typedef struct pk_engine pk_engine;

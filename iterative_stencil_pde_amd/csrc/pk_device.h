@@ -870,6 +870,11 @@ __device__ __forceinline__ void stream_sweep(const pk_kargs& a, const T* __restr
 // stencil, accumulated in double per lane over the band's rows and the strip's
 // stored lanes, so every interior node counts once. The unit then reaches K+1
 // halo rows and needs K+1 overlap columns.
+// TAP: the pass also sums rho^2 of an intermediate level, h0 (0..K-1: the field
+// after h0 of its K sweeps, h0 = 0 the field it reads), from the operands of
+// level h0 + 1's stencil, over the same rows and lanes as RES: a residual taken
+// inside a pass whose later levels run on (a RESIDUAL task between two SWEEP
+// tasks, computed in the pass that crosses from one to the other).
 //
 // Memory: rows go in chunks of CH, loaded one chunk ahead of their use. With
 // DEFER, a chunk's level-K rows are stored at the start of the next chunk
@@ -944,7 +949,7 @@ struct RingSlot {
     static constexpr int value = P;
 };
 
-template <typename T, bool HAS_B, int K, int DIR, bool RB, int MODE, bool RES>
+template <typename T, bool HAS_B, int K, int DIR, bool RB, int MODE, bool RES, bool TAP = false>
 __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T* __restrict__ dst,
                                                    const T* __restrict__ bsrc, int nx, int ny,
                                                    int pitch, int c0, int ov, int r0, int r1, int h0) {
@@ -1050,6 +1055,15 @@ __device__ __forceinline__ double stream_pass_unit(const T* __restrict__ src, T*
                     rm[j - 1] = x;
                 }
             };
+            if constexpr (TAP) {
+                // rho of level h0's row t - dir j (the field after h0 of the pass's
+                // sweeps), from the operands of level h0 + 1's stencil at this step
+                const int row = t - dir * j;
+                if (j == h0 + 1 && (!head || 2 * j <= q) && row >= r0 && row < r1) {  // wave-uniform
+                    const double r2 = pass_rho2<T, HAS_B, MODE != PASS_INNER>(up, mid, inc, bq[j - 1], col, nx);
+                    if (store_lane) acc += r2;
+                }
+            }
             if (RES && j == L) {  // rho of level K's row t - dir L, if it is a band row
                 const int row = t - dir * j;
                 if ((!head || 2 * j <= q) && row >= r0 && row < r1) {  // wave-uniform
@@ -1159,10 +1173,20 @@ __device__ __forceinline__ void pass_unit_place(int u, int strips, int units, in
     }
 }
 
+// One unit of a Jacobi pass in a given ring mode, marching down or up.
+template <typename T, bool HAS_B, int K, int MODE, bool TAP>
+__device__ __forceinline__ double pass_unit_dir(int dir, const T* __restrict__ src, T* __restrict__ dst,
+                                                const T* __restrict__ bsrc, int nx, int ny, int pt, int c0,
+                                                int ov, int r0, int r1, int h0) {
+    return dir > 0 ? stream_pass_unit<T, HAS_B, K, 1, false, MODE, false, TAP>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0)
+                   : stream_pass_unit<T, HAS_B, K, -1, false, MODE, false, TAP>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+}
+
 // One pass of k sweeps (a depth PK_PASS_DEPTH_OK accepts) over all units, src -> dst.
-// h0 >= 0: the k levels are red-black half-sweeps, level j of colour (h0+j-1) mod 2.
-// RES: also this lane's rho^2 of the result (returned; 0 otherwise).
-template <typename T, bool HAS_B, int K, bool RB, bool RES>
+// h0 >= 0: the k levels are red-black half-sweeps, level j of colour (h0+j-1) mod 2
+// (RB), or the level whose rho^2 is summed (TAP).
+// RES, TAP: also this lane's rho^2 of the result, or of level h0 (returned; 0 otherwise).
+template <typename T, bool HAS_B, int K, bool RB, bool RES, bool TAP = false>
 __device__ __forceinline__ double stream_pass_k(const pk_kargs& a, const T* __restrict__ src,
                                                 T* __restrict__ dst, int h0) {
     constexpr int W = VecW<T>::W;
@@ -1206,33 +1230,35 @@ __device__ __forceinline__ double stream_pass_k(const pk_kargs& a, const T* __re
         if constexpr (RB || RES || K < PK_SHALLOW_PASS) {
             if (dir > 0) acc += stream_pass_unit<T, HAS_B, K, 1, RB, PASS_CHECKED, RES>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
             else acc += stream_pass_unit<T, HAS_B, K, -1, RB, PASS_CHECKED, RES>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-        } else if (rows_late) {
-            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_CHECKED, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_CHECKED, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-        } else if (!HAS_B && lo != hi && nx % W == 0) {  // (with b the register file is full at depth 12)
-            if (lo) {
-                if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_EDGE_LO, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-                else stream_pass_unit<T, HAS_B, K, -1, false, PASS_EDGE_LO, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-            } else {
-                if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_EDGE_HI, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-                else stream_pass_unit<T, HAS_B, K, -1, false, PASS_EDGE_HI, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-            }
-        } else if (lo || hi) {
-            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_COLS, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_COLS, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
         } else {
-            if (dir > 0) stream_pass_unit<T, HAS_B, K, 1, false, PASS_INNER, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
-            else stream_pass_unit<T, HAS_B, K, -1, false, PASS_INNER, false>(src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            double r;
+            if (rows_late)
+                r = pass_unit_dir<T, HAS_B, K, PASS_CHECKED, TAP>(dir, src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            else if (!HAS_B && lo != hi && nx % W == 0) {  // (with b the register file is full at depth 12)
+                if (lo)
+                    r = pass_unit_dir<T, HAS_B, K, PASS_EDGE_LO, TAP>(dir, src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+                else
+                    r = pass_unit_dir<T, HAS_B, K, PASS_EDGE_HI, TAP>(dir, src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            } else if (lo || hi)
+                r = pass_unit_dir<T, HAS_B, K, PASS_COLS, TAP>(dir, src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            else
+                r = pass_unit_dir<T, HAS_B, K, PASS_INNER, TAP>(dir, src, dst, bsrc, nx, ny, pt, c0, ov, r0, r1, h0);
+            if constexpr (TAP) acc += r;
         }
     }
     return acc;
 }
 
 // One pass of k sweeps; res (Jacobi only): also returns this lane's rho^2 of
-// the result (the residual march of the last pass of a task).
+// the result (the residual march of the last pass of a task); tap >= 0 (Jacobi,
+// fp64, k = PK_MAX_PASS): returns this lane's rho^2 of the field after `tap` of
+// the pass's sweeps instead.
 template <typename T, bool HAS_B>
 __device__ __forceinline__ double stream_pass(const pk_kargs& a, const T* __restrict__ src,
-                                              T* __restrict__ dst, int k, int h0, bool res) {
+                                              T* __restrict__ dst, int k, int h0, bool res, int tap = -1) {
+    if constexpr (sizeof(T) == 8) {  // (the fp32 kernels do not fuse tasks)
+        if (tap >= 0) return stream_pass_k<T, HAS_B, PK_MAX_PASS, false, false, true>(a, src, dst, tap);
+    }
     // red-black passes are their own instances: the colour mask stays out of the
     // Jacobi march
     if (h0 >= 0) {

@@ -1062,6 +1062,7 @@ int pk_get_info(pk_engine* e, pk_info* info) {
         info->sweeps_done = e->ring.sweeps_seen();
         info->tasks_done = static_cast<int64_t>(e->ring.done_seen());
         info->tasks_carried = static_cast<int64_t>(e->ring.carried_seen());
+        info->tasks_fused = static_cast<int64_t>(e->ring.fused_seen());
         // once the kernel has said it is leaving, its end event completes promptly
         if (__atomic_load_n(&e->h_mail->exited, __ATOMIC_ACQUIRE) &&
             hipEventSynchronize(e->ev_end) == hipSuccess) {

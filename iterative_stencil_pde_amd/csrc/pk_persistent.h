@@ -592,6 +592,18 @@ struct ResidualState {
     bool ready;
 };
 
+// Task fusion across a RESIDUAL task (streaming layout), in the block's shared
+// memory (read at task boundaries only): the SWEEP task two slots after task
+// `from_seq` starts with `pre` of its sweeps already applied by that task's last
+// pass; `dec` is the decision for the task under way, as read after the grid
+// barrier that published it.
+struct FuseState {
+    uint64_t from_seq;
+    uint64_t cur_seq;  // the task under way (thread 0's copy)
+    int pre;
+    int dec;
+};
+
 // Depth of the next streaming pass with `left` sweeps (or red-black
 // half-sweeps) to go: the engine's depth, or `left` when fewer. A depth the
 // kernel does not carry (9..11) runs 8 first. A task's last Jacobi pass also
@@ -607,9 +619,16 @@ __device__ __forceinline__ int pass_depth(int depth, int left, bool rb) {
 
 // n sub-sweeps of the field in u[cur] in the engine's layout (cur flips):
 // Jacobi sweeps, or (rb) red-black half-sweeps, red first.
+// fusable (streaming layout, fp64): a plain SWEEP task (fs->cur_seq) that may
+// run its last pass on into a later SWEEP task; returns the sweeps of that later
+// task applied here (0 if none). The fp32 kernels leave fusion out: its code cost
+// their passes 10% (4096^2 fp32 Laplace, 4.48 against 4.08 us per sweep) in
+// register pressure, and the fp32 workloads that stream run one long task.
 template <typename T, bool HAS_B, int LAYOUT, int RT, bool TRACE>
-__device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, int& cur, BarrierCtx& bc,
-                                            T* lds, ResidualState& rs, double* s_red) {
+__device__ __forceinline__ int sweeps_task(const pk_kargs& a, int n, bool rb, int& cur, BarrierCtx& bc,
+                                           T* lds, ResidualState& rs, double* s_red, bool fusable,
+                                           FuseState* fs) {
+    int ahead = 0;
     if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
         if (rb)
             resident_sweep_task<T, HAS_B, true, TRACE>(a, n, cur, bc, lds);
@@ -621,35 +640,83 @@ __device__ __forceinline__ void sweeps_task(const pk_kargs& a, int n, bool rb, i
         else
             reg_sweep_task<T, HAS_B, false, RT, TRACE>(a, n, cur, bc, lds);
     } else {
+        // Fusion: where the task's last pass would run fewer than P sweeps and
+        // the two tasks after it are a RESIDUAL and a SWEEP of at least the rest
+        // of a pass (the leader reads their slots just before the grid barrier
+        // ahead of that pass), the pass runs P sweeps: the task's own, then the
+        // first sweeps of that later SWEEP task, and sums rho^2 of the field at
+        // the task's end on the way (a tap at that level), the RESIDUAL's value.
+        // The field the task ends with is never stored; every stored value is
+        // still the same expression on the same operands. A task of exactly P
+        // sweeps left runs a shallower pass first, so that a tail remains.
+        const int P = a.pass_sweeps;
+        const bool fz = sizeof(T) == 8 && fusable && !rb && !bc.broken && P == PK_MAX_PASS;
+        bool fused = false;  // the decision for the coming pass (uniform)
         for (int s = 0; s < n;) {
-            const int k = pass_depth(a.pass_sweeps, n - s, rb);
+            const int left = n - s;
+            int k;
+            if (fused) k = P;
+            else if (fz && left == P) k = PK_SHALLOW_PASS;
+            else if (fz && left > P) k = P;
+            else k = pass_depth(P, left, rb);
+            const int own = fused ? left : k;  // sweeps of this task in the pass
             // the last Jacobi pass of a task also sums rho^2 of its result, so a
             // RESIDUAL that follows need not read the field again ("Grid-Wide
             // Barriers", "What the barrier buys": the convergence check as a
             // reduction at the barrier); not under the negative control
-            const bool res = s + k >= n && !rb && !bc.broken;
+            const bool res = !fused && s + k >= n && !rb && !bc.broken;
             const double acc = stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]),
-                                                     static_cast<T*>(a.u[cur ^ 1]), k, rb ? (s & 1) : -1, res);
-            if (res) {
+                                                     static_cast<T*>(a.u[cur ^ 1]), k, rb ? (s & 1) : -1, res,
+                                                     fused ? left : -1);
+            if (res || fused) {
                 const double p = block_sum(acc, s_red);
                 if (threadIdx.x == 0) a.partials[static_cast<size_t>(rs.round & 1u) * a.grid + blockIdx.x] = p;
+            }
+            // the barrier ahead of a tail of fewer than P sweeps decides whether it
+            // fuses (the leader publishes the decision before arriving)
+            const bool decide = fz && !fused && s + own < n && n - (s + own) < P;
+            if (decide && blockIdx.x == 0 && threadIdx.x == 0) {
+                const uint64_t seq = *reinterpret_cast<volatile unsigned long long*>(&fs->cur_seq);
+                const pk_mailbox* mail = a.mail;
+                const uint64_t w1 = __hip_atomic_load(&mail->slot[(seq + 1) % PK_RING].word, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_SYSTEM);
+                const uint64_t w2 = __hip_atomic_load(&mail->slot[(seq + 2) % PK_RING].word, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_SYSTEM);
+                const int tail = n - (s + own);
+                const bool ok = static_cast<uint32_t>(w1 >> 32) == static_cast<uint32_t>(seq + 1) &&
+                                static_cast<int>((w1 >> 28) & 0xF) == PK_RESIDUAL &&
+                                static_cast<uint32_t>(w2 >> 32) == static_cast<uint32_t>(seq + 2) &&
+                                static_cast<int>((w2 >> 28) & 0xF) == PK_SWEEP &&
+                                static_cast<int>(w2 & PK_TASK_N_MAX) >= P - tail;
+                __hip_atomic_store(&a.st->fuse_seq, ok ? seq : 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             // between two full-depth passes (the same units), neighbour counters may
             // stand in for the grid barrier; a task's last pass, and the passes next
             // to a shallower one, end with the barrier (it also orders the partials
             // before any read)
-            if (__builtin_amdgcn_readfirstlane(bc.pn->on) && k == a.pass_sweeps && !res && s + k < n &&
-                pass_depth(a.pass_sweeps, n - s - k, rb) == a.pass_sweeps &&
-                (rb || s + k + a.pass_sweeps < n))
+            if (__builtin_amdgcn_readfirstlane(bc.pn->on) && k == P && !res && !fused && s + k < n &&
+                pass_depth(P, n - s - k, rb) == P && (rb || s + k + P < n))
                 pass_neighbor_sync(bc, __builtin_amdgcn_readfirstlane(bc.pn->mask));
             else
                 grid_barrier(bc, bc.broken);
             cur ^= 1;
-            s += k;
-            rs.ready = res;
+            rs.ready = res || fused;
+            if (fused) ahead = P - left;
+            s += own;
+            if (decide) {
+                if (threadIdx.x == 0)
+                    fs->dec = __hip_atomic_load(&a.st->fuse_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                              *reinterpret_cast<volatile unsigned long long*>(&fs->cur_seq);
+                __syncthreads();
+                fused = fs->dec != 0;
+                __syncthreads();
+            } else {
+                fused = false;
+            }
         }
     }
     if (rb && n > 0) rs.ready = false;  // the field changed, no partials of it
+    return ahead;
 }
 
 // One residual round: each block's partial goes to the half of `partials` of
@@ -744,9 +811,14 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
     }
     bc.trace = &s_trace;
     __shared__ PassNbr s_pn;
+    __shared__ FuseState s_fuse;
     if (threadIdx.x == 0) {
         s_pn.on = 0;
         s_pn.mask = 0;
+        s_fuse.from_seq = 0;
+        s_fuse.cur_seq = 0;
+        s_fuse.pre = 0;
+        s_fuse.dec = 0;
     }
     bc.pn = &s_pn;
     // neighbour counters between streaming passes (more than one block)
@@ -932,6 +1004,7 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
         double res = 0.0;
         int64_t errs = 0;
         int status = PK_OK;
+        int fused_task = 0;  // the task's last pass ran on into the SWEEP task two slots later
         if (kind == PK_SWEEP || kind == PK_SWEEP_RB || kind == PK_RESIDUAL || kind == PK_SWEEP_UNTIL) {
             // The sweeping tasks share one loop (one copy of the sweep and
             // residual code in the kernel): an optional residual check, then up
@@ -939,7 +1012,10 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
             const bool rb = kind == PK_SWEEP_RB;
             const bool until = kind == PK_SWEEP_UNTIL;
             const bool check = until || kind == PK_RESIDUAL;
-            const int budget = kind == PK_RESIDUAL ? 0 : n;
+            // a SWEEP task may start with some of its sweeps already applied by
+            // the fused last pass of the SWEEP task two slots before it
+            const int pre = (kind == PK_SWEEP && s_fuse.from_seq + 2 == seq) ? s_fuse.pre : 0;
+            const int budget = kind == PK_RESIDUAL ? 0 : n - pre;
             double tol = -1.0;  // R >= 0: never stops a plain residual
             int every = budget;
             if (until) {
@@ -968,11 +1044,25 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
                     // red-black: k iterations = 2k half-sweeps, each computed into
                     // the other buffer with the other colour copied (the in-place
                     // result: a node never reads its own colour)
-                    sweeps_task<T, HAS_B, LAYOUT, RT, TRACE>(a, rb ? 2 * k : k, rb, cur, bc, reinterpret_cast<T*>(pk_lds),
-                                                  rs, s_red);
+                    const bool fusable = LAYOUT == PK_LAYOUT_STREAM && sizeof(T) == 8 && kind == PK_SWEEP;
+                    if (fusable && threadIdx.x == 0)
+                        s_fuse.cur_seq = *reinterpret_cast<volatile unsigned long long*>(&s_seq);
+                    const int ahead = sweeps_task<T, HAS_B, LAYOUT, RT, TRACE>(
+                        a, rb ? 2 * k : k, rb, cur, bc, reinterpret_cast<T*>(pk_lds), rs, s_red, fusable, &s_fuse);
+                    if (ahead > 0) {  // uniform: the SWEEP task at seq + 2 is ahead by that much
+                        fused_task = 1;
+                        __syncthreads();
+                        if (threadIdx.x == 0) {
+                            // copied from shared memory here: a register copy of the
+                            // sequence made for this store was kept, and spilled,
+                            // across the task
+                            s_fuse.from_seq = *reinterpret_cast<volatile unsigned long long*>(&s_seq);
+                            s_fuse.pre = ahead;
+                        }
+                    }
                     done += k;
                 }
-                sweeps += done;
+                sweeps += done + pre;
             }
         } else if (kind == PK_TASK_READBACK) {
             readback_task<T>(a, cur);
@@ -1007,7 +1097,7 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
         may_carry = !bc.broken && bc.nbar != nbar0;
         if (leader) {
             write_done(&mail->done[seq % PK_RING], seq, kind, bc.faulted ? PK_EDEVICE : status, res, sweeps,
-                       s_carry.t_task, wall_clock64(), errs, cur, s_carried);
+                       s_carry.t_task, wall_clock64(), errs, cur, s_carried | (fused_task << 1));
             __hip_atomic_store(&mail->done_seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
         }
         next_seq = seq + 1;

@@ -48,6 +48,7 @@ public:
         next_ = 1;
         harvested_ = 0;
         carried_ = 0;
+        fused_ = 0;
         done_.assign(1, DoneInfo{});
     }
 
@@ -79,8 +80,9 @@ public:
             x.t_end = r.t_end;
             x.errors = r.errors;
             x.cur = r.cur;
-            x.carried = r.carried;
-            carried_ += r.carried ? 1 : 0;
+            x.carried = r.carried & 1;
+            carried_ += (r.carried & 1) ? 1 : 0;
+            fused_ += (r.carried & 2) ? 1 : 0;
             done_.push_back(x);
             harvested_ = s;
         }
@@ -119,12 +121,14 @@ public:
     int64_t sweeps_seen() const { return harvested_ ? done_[harvested_].sweeps_done : 0; }
     int last_cur() const { return harvested_ ? done_[harvested_].cur : 0; }
     uint64_t carried_seen() const { return carried_; }
+    uint64_t fused_seen() const { return fused_; }
 
 private:
     pk_mailbox* m_ = nullptr;
     uint64_t next_ = 1;
     uint64_t harvested_ = 0;
     uint64_t carried_ = 0;
+    uint64_t fused_ = 0;
     std::vector<DoneInfo> done_;  // index = ticket
 };
 

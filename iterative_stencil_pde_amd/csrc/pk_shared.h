@@ -77,8 +77,10 @@ struct alignas(PK_LINE) pk_done_rec {
     uint64_t t_begin;  // device wall clock ticks
     uint64_t t_end;
     int64_t errors;
-    int32_t cur;  // buffer index that holds the whole field after this task
-    int32_t carried;  // 1: the task was handed on by the previous task's barrier
+    int32_t cur;  // buffer index that holds the whole field after this task (after
+                  // its last pass, where that pass ran on into a later task)
+    int32_t carried;  // bit 0: the task was handed on by the previous task's barrier;
+                      // bit 1: its last pass ran on into the SWEEP task two slots later
 };
 
 // Parameters of a PK_SWEEP_UNTIL task, written by the host before it releases
@@ -142,6 +144,11 @@ struct pk_dev_state {
     // whose stores the XCD has written back
     pk_word256 xpass_count[8];
     pk_word256 xpass_gen[8];
+    // a streaming SWEEP task whose last pass runs on into the SWEEP task two
+    // slots later, summing the RESIDUAL task between them inside that pass: the
+    // leader's decision (the task's sequence, 0 for none), published through the
+    // grid barrier before that pass
+    alignas(PK_LINE) uint64_t fuse_seq;
 };
 
 // Kernel arguments (passed by value).

@@ -71,7 +71,7 @@ class pk_info(ctypes.Structure):
                 ("kernel_ms", ctypes.c_double), ("sweeps_done", ctypes.c_int64),
                 ("tasks_done", ctypes.c_int64), ("kernel_launches", ctypes.c_int64),
                 ("tasks_carried", ctypes.c_int64), ("wall_clock_khz", ctypes.c_int),
-                ("trace_capacity", ctypes.c_int)]
+                ("trace_capacity", ctypes.c_int), ("tasks_fused", ctypes.c_int64)]
 
 
 class PkError(RuntimeError):

@@ -81,6 +81,7 @@ int main(void) {
   P(pk_opts, reserved);
   P(pk_result, residual); P(pk_result, errors); P(pk_result, status);
   P(pk_info, exchange); P(pk_info, lds_bytes); P(pk_info, tasks_carried); P(pk_info, kernel_ms); P(pk_info, kernel_launches);
+  P(pk_info, tasks_fused);
   return 0;
 }
 """)

@@ -55,7 +55,7 @@ def test_script_counts_fused_residuals():
     # residual reads the field, the others were summed by the pass before them
     script = [("residual",)] + [("sweep", 50), ("residual",)] * 10 + [("readback",)]
     w = _shape_only(8192, 8192, np.float64, True, script)
-    assert bench.script_counts(w, 12) == (500, 50, 1)
+    assert bench.script_counts(w, 12, fuse=False) == (500, 50, 1)
     assert bench.script_counts(w, 8) == (500, 70, 1)
     # one pass per sweep (launch-style plans) fuses nothing
     assert bench.script_counts(w, 1) == (500, 500, 11)
@@ -63,3 +63,32 @@ def test_script_counts_fused_residuals():
     w = _shape_only(64, 64, np.float32, False,
                     [("sweep", 9), ("residual",), ("sweep_rb", 3), ("residual",), ("sweep", 0), ("residual",)])
     assert bench.script_counts(w, 8) == (12, 2 + 1, 2)
+
+
+def test_script_counts_fused_tails():
+    """fp64 at depth 12: a SWEEP task's tail runs on into the next SWEEP task when a
+    RESIDUAL and a long enough SWEEP follow. The 8192^2 script's ten 50-sweep tasks:
+    12 x 4 + a tail of 2 fused (5 passes), then 40, 42, 44, 46 sweeps left (3 passes
+    and a fused tail each), 48 (12 x 3, an 8-deep pass, a fused tail of 4), 42, 44,
+    46, and the last, 48 with nothing to fuse into (12 x 3, 8, then 4 that sums the
+    residual): 43 passes for 500 sweeps."""
+    script = [("residual",)] + [("sweep", 50), ("residual",)] * 10 + [("readback",)]
+    w = _shape_only(8192, 8192, np.float64, True, script)
+    assert bench.fuses(w, 12) and not bench.fuses(w, 8)
+    assert bench.script_counts(w, 12) == (500, 43, 1)
+    # the same script in fp32 runs every task on its own
+    w32 = _shape_only(8192, 8192, np.float32, True, script)
+    assert not bench.fuses(w32, 12)
+    assert bench.script_counts(w32, 12) == (500, 50, 1)
+    # a next task shorter than the rest of the pass, and a red-black task next, do not
+    # fuse: 30 -> 12, 12 and a tail of 6, which would need a SWEEP of at least 6 next
+    # (5 is too short: the tail runs alone and sums the residual); 5 -> 5; 20 -> 12,
+    # then its tail of 8 runs on 4 sweeps into the next 30 -> 26 left -> 12, 12 and a
+    # tail of 2 (a red-black task follows); the red-black task -> one pass
+    script = [("sweep", 30), ("residual",), ("sweep", 5), ("residual",), ("sweep", 20), ("residual",),
+              ("sweep", 30), ("residual",), ("sweep_rb", 2), ("residual",)]
+    w = _shape_only(300, 514, np.float64, True, script)
+    sweeps, passes, reads = bench.script_counts(w, 12)
+    assert sweeps == 87
+    assert passes == 3 + 1 + 2 + 3 + 1
+    assert reads == 1  # only the residual after the red-black task reads the field

@@ -229,6 +229,37 @@ def test_stream_neighbor_counters(shape, dtype, poisson, k, band_rows, blocks):
     check_against_oracle(w, got, ref, f"nbr/k{k}/rows{band_rows}/g{info.grid_blocks}/{ny}x{nx}")
 
 
+FUSE_SCRIPT = [("residual",), ("sweep", 30), ("residual",), ("sweep", 25), ("residual",), ("sweep", 12),
+               ("residual",), ("sweep", 7), ("residual",), ("sweep", 40), ("residual",), ("sweep", 16),
+               ("residual",), ("sweep", 8), ("residual",), ("sweep", 3), ("residual",), ("sweep", 1),
+               ("residual",), ("sweep", 24), ("residual",), ("residual",), ("sweep", 50), ("residual",),
+               ("sweep_rb", 5), ("residual",), ("sweep", 26), ("residual",), ("sweep", 11)]
+
+
+@pytest.mark.parametrize("k", [12, 8])
+@pytest.mark.parametrize("poisson", [False, True], ids=["laplace", "poisson"])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
+@pytest.mark.parametrize("shape", [(130, 257), (67, 1030), (300, 514)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_fused_task_tails(shape, dtype, poisson, k):
+    """Tasks queued ahead (SWEEP, RESIDUAL, SWEEP, ...): a SWEEP task's last pass
+    runs on into the next SWEEP task and sums the RESIDUAL between them inside the
+    pass (fp64 kernels at depth 12; otherwise every task runs on its own). Tails of every
+    length, next tasks shorter and longer than the rest of a pass, back-to-back
+    residuals and a red-black task between: same fields and residuals as the
+    oracle."""
+    ny, nx = shape
+    u, f = _random_case(ny, nx, dtype, poisson, seed=17 * ny + nx + k)
+    w = inputs.Workload(f"fuse{ny}x{nx}", nx, ny, dtype, 0.013, u, f, list(FUSE_SCRIPT), "")
+    ref = run_oracle_pipelined(w)
+    got = run_engine_pipelined(w, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM, pass_sweeps=k)
+    say(f"  fused tasks: {got['info_end'].tasks_fused}")
+    if dtype == np.float64 and k == pk.PK_MAX_PASS:
+        assert got["info_end"].tasks_fused > 0
+    else:  # fusion runs in the fp64 kernels at depth 12 only
+        assert got["info_end"].tasks_fused == 0
+    check_against_oracle(w, got, ref, f"fuse/k{k}/{ny}x{nx}/{np.dtype(dtype).name}")
+
+
 @pytest.mark.parametrize("blocks", [12, 24, 40])
 @pytest.mark.parametrize("dtype", [np.float32, np.float64], ids=["f32", "f64"])
 def test_stream_neighbor_counters_blocks_without_units(blocks, dtype):
@@ -726,6 +757,20 @@ def test_poisson8192_full(mode):
     g = _golden("poisson8192")
     got = run_engine_script(w, timeout_s=300, **MODES[mode])
     say(f"  grid={got['info'].grid_blocks} layout={got['info'].layout} ({got['seconds']:.1f}s)")
+    _check_golden(w, got["final"], got["residuals"], g, 1e-12)
+    _check_every_cell(w, got["final"], g, 1e-12)
+
+
+def test_poisson8192_full_pipelined():
+    """The full 8192^2 fp64 Poisson script queued ahead, as the bench runs it: the
+    SWEEP tasks' last passes run on into the next SWEEP task (fused tails), and
+    every cell of the final field and every residual still match the oracle's."""
+    w = inputs.make("poisson8192")
+    g = _golden("poisson8192")
+    w.script = [s for s in w.script if s[0] != "readback"]
+    got = run_engine_pipelined(w, timeout_s=300, mode=pk.PK_PERSISTENT)
+    say(f"  fused tasks: {got['info_end'].tasks_fused}")
+    assert got["info_end"].tasks_fused >= 1
     _check_golden(w, got["final"], got["residuals"], g, 1e-12)
     _check_every_cell(w, got["final"], g, 1e-12)
 
