@@ -87,7 +87,12 @@ extern "C" {
 /* ---- tasks -------------------------------------------------------------- */
 #define PK_SWEEP 1    /* n Jacobi sweeps (n >= 0)                                   */
 #define PK_RESIDUAL 2 /* R = sqrt(sum over interior of rho^2),                      */
-                      /*   rho = (((W+E)+(S+N)) + b) - 4u, all in double            */
+                      /*   rho = (((W+E)+(S+N)) + b) - 4u, all in double. Between   */
+                      /*   two SWEEP tasks queued ahead, an fp64 streaming engine   */
+                      /*   at depth 12 may sum it inside the pass that runs on from  */
+                      /*   the first into the second (pk_info.tasks_fused): the     */
+                      /*   same R, fields and done records; the field at the first  */
+                      /*   task's end is then never stored                          */
 #define PK_EXIT 3     /* the persistent kernel returns; the engine stays readable   */
 #define PK_BARRIER 4  /* n grid barriers and nothing else (persistent only; timing) */
 #define PK_STAMP 5    /* n rounds of the barrier visibility check (persistent only):*/
