@@ -617,6 +617,24 @@ __device__ __forceinline__ int pass_depth(int depth, int left, bool rb) {
     return k;
 }
 
+// Leader only, before the grid barrier ahead of a task's tail: whether the two
+// tasks after the SWEEP task fs->cur_seq are a RESIDUAL and a SWEEP of at least
+// `need` sweeps, both already published by the host; the decision (the task's
+// sequence number, or 0) goes to a device word that the barrier publishes.
+__device__ __forceinline__ void fuse_decide(const pk_kargs& a, FuseState* fs, int need) {
+    const uint64_t seq = *reinterpret_cast<volatile unsigned long long*>(&fs->cur_seq);
+    const pk_mailbox* mail = a.mail;
+    const uint64_t w1 = __hip_atomic_load(&mail->slot[(seq + 1) % PK_RING].word, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint64_t w2 = __hip_atomic_load(&mail->slot[(seq + 2) % PK_RING].word, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_SYSTEM);
+    const bool ok = static_cast<uint32_t>(w1 >> 32) == static_cast<uint32_t>(seq + 1) &&
+                    static_cast<int>((w1 >> 28) & 0xF) == PK_RESIDUAL &&
+                    static_cast<uint32_t>(w2 >> 32) == static_cast<uint32_t>(seq + 2) &&
+                    static_cast<int>((w2 >> 28) & 0xF) == PK_SWEEP && static_cast<int>(w2 & PK_TASK_N_MAX) >= need;
+    __hip_atomic_store(&a.st->fuse_seq, ok ? seq : 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // n sub-sweeps of the field in u[cur] in the engine's layout (cur flips):
 // Jacobi sweeps, or (rb) red-black half-sweeps, red first.
 // fusable (streaming layout, fp64): a plain SWEEP task (fs->cur_seq) that may
@@ -651,58 +669,41 @@ __device__ __forceinline__ int sweeps_task(const pk_kargs& a, int n, bool rb, in
         // sweeps left runs a shallower pass first, so that a tail remains.
         const int P = a.pass_sweeps;
         const bool fz = sizeof(T) == 8 && fusable && !rb && !bc.broken && P == PK_MAX_PASS;
-        bool fused = false;  // the decision for the coming pass (uniform)
-        for (int s = 0; s < n;) {
+        bool fused = false;  // the leader's decision for the tail (uniform)
+        int s = 0;
+        while (s < n) {
             const int left = n - s;
             int k;
-            if (fused) k = P;
-            else if (fz && left == P) k = PK_SHALLOW_PASS;
+            if (fz && left == P) k = PK_SHALLOW_PASS;
             else if (fz && left > P) k = P;
             else k = pass_depth(P, left, rb);
-            const int own = fused ? left : k;  // sweeps of this task in the pass
             // the last Jacobi pass of a task also sums rho^2 of its result, so a
             // RESIDUAL that follows need not read the field again ("Grid-Wide
             // Barriers", "What the barrier buys": the convergence check as a
             // reduction at the barrier); not under the negative control
-            const bool res = !fused && s + k >= n && !rb && !bc.broken;
+            const bool res = s + k >= n && !rb && !bc.broken;
             const double acc = stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]),
-                                                     static_cast<T*>(a.u[cur ^ 1]), k, rb ? (s & 1) : -1, res,
-                                                     fused ? left : -1);
-            if (res || fused) {
+                                                     static_cast<T*>(a.u[cur ^ 1]), k, rb ? (s & 1) : -1, res);
+            if (res) {
                 const double p = block_sum(acc, s_red);
                 if (threadIdx.x == 0) a.partials[static_cast<size_t>(rs.round & 1u) * a.grid + blockIdx.x] = p;
             }
             // the barrier ahead of a tail of fewer than P sweeps decides whether it
             // fuses (the leader publishes the decision before arriving)
-            const bool decide = fz && !fused && s + own < n && n - (s + own) < P;
-            if (decide && blockIdx.x == 0 && threadIdx.x == 0) {
-                const uint64_t seq = *reinterpret_cast<volatile unsigned long long*>(&fs->cur_seq);
-                const pk_mailbox* mail = a.mail;
-                const uint64_t w1 = __hip_atomic_load(&mail->slot[(seq + 1) % PK_RING].word, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_SYSTEM);
-                const uint64_t w2 = __hip_atomic_load(&mail->slot[(seq + 2) % PK_RING].word, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_SYSTEM);
-                const int tail = n - (s + own);
-                const bool ok = static_cast<uint32_t>(w1 >> 32) == static_cast<uint32_t>(seq + 1) &&
-                                static_cast<int>((w1 >> 28) & 0xF) == PK_RESIDUAL &&
-                                static_cast<uint32_t>(w2 >> 32) == static_cast<uint32_t>(seq + 2) &&
-                                static_cast<int>((w2 >> 28) & 0xF) == PK_SWEEP &&
-                                static_cast<int>(w2 & PK_TASK_N_MAX) >= P - tail;
-                __hip_atomic_store(&a.st->fuse_seq, ok ? seq : 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            const bool decide = fz && s + k < n && n - (s + k) < P;
+            if (decide && blockIdx.x == 0 && threadIdx.x == 0) fuse_decide(a, fs, P - (n - (s + k)));
             // between two full-depth passes (the same units), neighbour counters may
             // stand in for the grid barrier; a task's last pass, and the passes next
             // to a shallower one, end with the barrier (it also orders the partials
             // before any read)
-            if (__builtin_amdgcn_readfirstlane(bc.pn->on) && k == P && !res && !fused && s + k < n &&
+            if (__builtin_amdgcn_readfirstlane(bc.pn->on) && k == P && !res && s + k < n &&
                 pass_depth(P, n - s - k, rb) == P && (rb || s + k + P < n))
                 pass_neighbor_sync(bc, __builtin_amdgcn_readfirstlane(bc.pn->mask));
             else
                 grid_barrier(bc, bc.broken);
             cur ^= 1;
-            rs.ready = res || fused;
-            if (fused) ahead = P - left;
-            s += own;
+            rs.ready = res;
+            s += k;
             if (decide) {
                 if (threadIdx.x == 0)
                     fs->dec = __hip_atomic_load(&a.st->fuse_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -710,9 +711,21 @@ __device__ __forceinline__ int sweeps_task(const pk_kargs& a, int n, bool rb, in
                 __syncthreads();
                 fused = fs->dec != 0;
                 __syncthreads();
-            } else {
-                fused = false;
+                if (fused) break;
             }
+        }
+        if (fused) {
+            // the fused tail: this task's last t sweeps and the later task's first
+            // P - t in one pass, rho^2 of level t summed for the RESIDUAL between
+            const int t = n - s;
+            const double acc = stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]),
+                                                     static_cast<T*>(a.u[cur ^ 1]), P, -1, false, t);
+            const double p = block_sum(acc, s_red);
+            if (threadIdx.x == 0) a.partials[static_cast<size_t>(rs.round & 1u) * a.grid + blockIdx.x] = p;
+            grid_barrier(bc, bc.broken);  // also orders the partials before any read
+            cur ^= 1;
+            rs.ready = true;
+            ahead = P - t;
         }
     }
     if (rb && n > 0) rs.ready = false;  // the field changed, no partials of it
