@@ -239,11 +239,12 @@ def script_counts(w, pass_sweeps, fuse=None, stats=None):
     (k = 1: one pass per sweep); a RESIDUAL right after a Jacobi SWEEP task of
     n > 0 sweeps reads nothing (its partials were summed by that task's last pass),
     any other reads u and b. With fusion (fuses()): a SWEEP task with more than P
-    sweeps left runs P-deep passes (exactly P left: an 8-deep pass first), and where
-    its tail of fewer than P sweeps is followed by a RESIDUAL and a SWEEP of at
-    least the rest of a pass, that tail runs as one P-deep pass that also applies
-    the first sweeps of the later task and sums the RESIDUAL on the way. `stats`
-    (a dict), if given, receives the number of such fused tails ("fused")."""
+    sweeps left runs P-deep passes, and where its last t <= P sweeps are followed
+    by a RESIDUAL and a SWEEP of at least P - t sweeps (t = P: at least P), they
+    run as one P-deep pass that also applies the first P - t sweeps of the later
+    task and sums the RESIDUAL on the way (t = P: a pass of their own, then the
+    later task's first P sweeps with the residual of level 0). `stats` (a dict), if
+    given, receives the number of such fused tails ("fused")."""
     if fuse is None:
         fuse = fuses(w, pass_sweeps)
     tasks = step_tasks(w)
@@ -266,27 +267,28 @@ def script_counts(w, pass_sweeps, fuse=None, stats=None):
         s, fused, ran = 0, False, False
         while s < n:
             left = n - s
-            if fused:
-                k = P
-            elif fz and left == P:
-                k = SHALLOW_PASS
-            elif fz and left > P:
-                k = P
-            else:
-                k = pass_depths(left, P, rb)[0]
-            own = left if fused else k
+            k = P if fz and left > P else pass_depths(left, P, rb)[0]
             passes += 1
             ran = True
-            res = not fused and s + k >= n and not rb and P > 1
-            if fused:
-                pre = P - left
-                fused_tails += 1
-            decide = fz and not fused and s + own < n and n - (s + own) < P
-            ready = res or fused
-            s += own
-            nxt = tasks[idx + 1:idx + 3]
-            fused = decide and len(nxt) == 2 and nxt[0][0] == "residual" and nxt[1][0] == "sweep" \
-                and nxt[1][1] >= P - (n - s)
+            res = s + k >= n and not rb and P > 1
+            ready = res
+            s += k
+            rest = n - s
+            if fz and 0 < rest <= P:
+                nxt = tasks[idx + 1:idx + 3]
+                fused = len(nxt) == 2 and nxt[0][0] == "residual" and nxt[1][0] == "sweep" \
+                    and nxt[1][1] >= (P - rest if rest < P else P)
+                if fused:
+                    break
+        if fused:
+            t = n - s
+            if t == P:  # a pass of its own, then the later task's first P sweeps tap level 0
+                passes += 1
+                t = 0
+            passes += 1
+            pre = P - t
+            fused_tails += 1
+            ready = True
         if rb and ran:
             ready = False
     if stats is not None:

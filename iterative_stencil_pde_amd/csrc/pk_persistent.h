@@ -674,8 +674,7 @@ __device__ __forceinline__ int sweeps_task(const pk_kargs& a, int n, bool rb, in
         while (s < n) {
             const int left = n - s;
             int k;
-            if (fz && left == P) k = PK_SHALLOW_PASS;
-            else if (fz && left > P) k = P;
+            if (fz && left > P) k = P;
             else k = pass_depth(P, left, rb);
             // the last Jacobi pass of a task also sums rho^2 of its result, so a
             // RESIDUAL that follows need not read the field again ("Grid-Wide
@@ -688,10 +687,11 @@ __device__ __forceinline__ int sweeps_task(const pk_kargs& a, int n, bool rb, in
                 const double p = block_sum(acc, s_red);
                 if (threadIdx.x == 0) a.partials[static_cast<size_t>(rs.round & 1u) * a.grid + blockIdx.x] = p;
             }
-            // the barrier ahead of a tail of fewer than P sweeps decides whether it
-            // fuses (the leader publishes the decision before arriving)
-            const bool decide = fz && s + k < n && n - (s + k) < P;
-            if (decide && blockIdx.x == 0 && threadIdx.x == 0) fuse_decide(a, fs, P - (n - (s + k)));
+            // the barrier ahead of the task's last P or fewer sweeps decides whether
+            // they fuse (the leader publishes the decision before arriving)
+            const int rest = n - (s + k);
+            const bool decide = fz && rest > 0 && rest <= P;
+            if (decide && blockIdx.x == 0 && threadIdx.x == 0) fuse_decide(a, fs, rest < P ? P - rest : P);
             // between two full-depth passes (the same units), neighbour counters may
             // stand in for the grid barrier; a task's last pass, and the passes next
             // to a shallower one, end with the barrier (it also orders the partials
@@ -716,8 +716,17 @@ __device__ __forceinline__ int sweeps_task(const pk_kargs& a, int n, bool rb, in
         }
         if (fused) {
             // the fused tail: this task's last t sweeps and the later task's first
-            // P - t in one pass, rho^2 of level t summed for the RESIDUAL between
-            const int t = n - s;
+            // P - t in one pass, rho^2 of level t summed for the RESIDUAL between.
+            // A tail of exactly P runs as a pass of its own, and the later task's
+            // first P sweeps then tap level 0 (the field this task ends with).
+            int t = n - s;
+            if (t == P) {
+                stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]), static_cast<T*>(a.u[cur ^ 1]), P, -1,
+                                      false);
+                grid_barrier(bc, bc.broken);
+                cur ^= 1;
+                t = 0;
+            }
             const double acc = stream_pass<T, HAS_B>(a, static_cast<const T*>(a.u[cur]),
                                                      static_cast<T*>(a.u[cur ^ 1]), P, -1, false, t);
             const double p = block_sum(acc, s_red);

@@ -66,16 +66,19 @@ def test_script_counts_fused_residuals():
 
 
 def test_script_counts_fused_tails():
-    """fp64 at depth 12: a SWEEP task's tail runs on into the next SWEEP task when a
-    RESIDUAL and a long enough SWEEP follow. The 8192^2 script's ten 50-sweep tasks:
-    12 x 4 + a tail of 2 fused (5 passes), then 40, 42, 44, 46 sweeps left (3 passes
-    and a fused tail each), 48 (12 x 3, an 8-deep pass, a fused tail of 4), 42, 44,
-    46, and the last, 48 with nothing to fuse into (12 x 3, 8, then 4 that sums the
-    residual): 43 passes for 500 sweeps."""
+    """fp64 at depth 12: a SWEEP task's last t <= 12 sweeps run on into the next
+    SWEEP task when a RESIDUAL and a long enough SWEEP follow. The 8192^2 script's
+    ten 50-sweep tasks: 12 x 4 and a fused tail of 2 (5 passes), then 40, 42, 44,
+    46 sweeps left (12 x 3 and a fused tail each), 48 (12 x 3, then its last 12 as
+    a pass of their own and the next task's first 12 summing the residual of level
+    0: 5 passes), 38, 40, 42, and the last, 44 with nothing to fuse into (12 x 3,
+    then 8 that sums the residual): 42 passes for 500 sweeps."""
     script = [("residual",)] + [("sweep", 50), ("residual",)] * 10 + [("readback",)]
     w = _shape_only(8192, 8192, np.float64, True, script)
     assert bench.fuses(w, 12) and not bench.fuses(w, 8)
-    assert bench.script_counts(w, 12) == (500, 43, 1)
+    stats = {}
+    assert bench.script_counts(w, 12, stats=stats) == (500, 42, 1)
+    assert stats["fused"] == 9
     # the same script in fp32 runs every task on its own
     w32 = _shape_only(8192, 8192, np.float32, True, script)
     assert not bench.fuses(w32, 12)

@@ -232,7 +232,8 @@ def test_stream_neighbor_counters(shape, dtype, poisson, k, band_rows, blocks):
 FUSE_SCRIPT = [("residual",), ("sweep", 30), ("residual",), ("sweep", 25), ("residual",), ("sweep", 12),
                ("residual",), ("sweep", 7), ("residual",), ("sweep", 40), ("residual",), ("sweep", 16),
                ("residual",), ("sweep", 8), ("residual",), ("sweep", 3), ("residual",), ("sweep", 1),
-               ("residual",), ("sweep", 24), ("residual",), ("residual",), ("sweep", 50), ("residual",),
+               ("residual",), ("sweep", 24), ("residual",), ("sweep", 30), ("residual",), ("residual",),
+               ("sweep", 50), ("residual",),
                ("sweep_rb", 5), ("residual",), ("sweep", 26), ("residual",), ("sweep", 11)]
 
 
@@ -244,9 +245,10 @@ def test_fused_task_tails(shape, dtype, poisson, k):
     """Tasks queued ahead (SWEEP, RESIDUAL, SWEEP, ...): a SWEEP task's last pass
     runs on into the next SWEEP task and sums the RESIDUAL between them inside the
     pass (fp64 kernels at depth 12; otherwise every task runs on its own). Tails of every
-    length, next tasks shorter and longer than the rest of a pass, back-to-back
-    residuals and a red-black task between: same fields and residuals as the
-    oracle."""
+    length up to a whole pass (which then runs alone and the next task's first
+    pass sums the residual of its level 0), next tasks shorter and longer than the
+    rest of a pass, back-to-back residuals and a red-black task between: same
+    fields and residuals as the oracle."""
     ny, nx = shape
     u, f = _random_case(ny, nx, dtype, poisson, seed=17 * ny + nx + k)
     w = inputs.Workload(f"fuse{ny}x{nx}", nx, ny, dtype, 0.013, u, f, list(FUSE_SCRIPT), "")
