@@ -617,10 +617,11 @@ __device__ __forceinline__ int pass_depth(int depth, int left, bool rb) {
     return k;
 }
 
-// Leader only, before the grid barrier ahead of a task's tail: whether the two
-// tasks after the SWEEP task fs->cur_seq are a RESIDUAL and a SWEEP of at least
-// `need` sweeps, both already published by the host; the decision (the task's
-// sequence number, or 0) goes to a device word that the barrier publishes.
+// Leader only, before the grid barrier ahead of a task's last P or fewer
+// sweeps: whether the two tasks after the SWEEP task fs->cur_seq are a RESIDUAL
+// and a SWEEP of at least `need` sweeps, both already published by the host; the
+// decision (the task's sequence number, or 0) goes to a device word that the
+// barrier publishes.
 __device__ __forceinline__ void fuse_decide(const pk_kargs& a, FuseState* fs, int need) {
     const uint64_t seq = *reinterpret_cast<volatile unsigned long long*>(&fs->cur_seq);
     const pk_mailbox* mail = a.mail;
@@ -658,15 +659,15 @@ __device__ __forceinline__ int sweeps_task(const pk_kargs& a, int n, bool rb, in
         else
             reg_sweep_task<T, HAS_B, false, RT, TRACE>(a, n, cur, bc, lds);
     } else {
-        // Fusion: where the task's last pass would run fewer than P sweeps and
-        // the two tasks after it are a RESIDUAL and a SWEEP of at least the rest
-        // of a pass (the leader reads their slots just before the grid barrier
-        // ahead of that pass), the pass runs P sweeps: the task's own, then the
-        // first sweeps of that later SWEEP task, and sums rho^2 of the field at
-        // the task's end on the way (a tap at that level), the RESIDUAL's value.
-        // The field the task ends with is never stored; every stored value is
-        // still the same expression on the same operands. A task of exactly P
-        // sweeps left runs a shallower pass first, so that a tail remains.
+        // Fusion: where the task's last t <= P sweeps are followed by a RESIDUAL
+        // and a SWEEP of at least P - t sweeps (t = P: at least P; the leader
+        // reads their slots just before the grid barrier ahead of those sweeps),
+        // they run as one P-deep pass: the task's own t, then the first P - t of
+        // that later SWEEP task, summing rho^2 of level t on the way (a tap), the
+        // RESIDUAL's value; a tail of exactly P runs as a pass of its own first,
+        // and the tap is then at level 0 of the later task's first pass. The field
+        // the task ends with is never stored; every stored value is still the
+        // same expression on the same operands.
         const int P = a.pass_sweeps;
         const bool fz = sizeof(T) == 8 && fusable && !rb && !bc.broken && P == PK_MAX_PASS;
         bool fused = false;  // the leader's decision for the tail (uniform)
