@@ -243,8 +243,10 @@ def script_counts(w, pass_sweeps, fuse=None, stats=None):
     by a RESIDUAL and a SWEEP of at least P - t sweeps (t = P: at least P), they
     run as one P-deep pass that also applies the first P - t sweeps of the later
     task and sums the RESIDUAL on the way (t = P: a pass of their own, then the
-    later task's first P sweeps with the residual of level 0). `stats` (a dict), if
-    given, receives the number of such fused tails ("fused")."""
+    later task's first P sweeps with the residual of level 0). A RESIDUAL of a
+    field no pass has summed, followed by a SWEEP of at least P, runs that task's
+    first pass and sums its level 0 instead of reading the field. `stats` (a dict),
+    if given, receives the number of such fused tasks ("fused")."""
     if fuse is None:
         fuse = fuses(w, pass_sweeps)
     tasks = step_tasks(w)
@@ -254,7 +256,14 @@ def script_counts(w, pass_sweeps, fuse=None, stats=None):
     pre = 0        # sweeps of the next SWEEP task already applied
     for idx, t in enumerate(tasks):
         if t[0] == "residual":
-            residuals += 0 if ready else 1
+            nxt = tasks[idx + 1:idx + 2]
+            if not ready and fuse and P == pk.PK_MAX_PASS and nxt and nxt[0][0] == "sweep" and nxt[0][1] >= P:
+                # the next SWEEP task's first pass runs here and sums level 0
+                passes += 1
+                pre = P
+                fused_tails += 1
+            else:
+                residuals += 0 if ready else 1
             ready = False
             continue
         rb = t[0] == "sweep_rb"

@@ -87,12 +87,12 @@ extern "C" {
 /* ---- tasks -------------------------------------------------------------- */
 #define PK_SWEEP 1    /* n Jacobi sweeps (n >= 0)                                   */
 #define PK_RESIDUAL 2 /* R = sqrt(sum over interior of rho^2),                      */
-                      /*   rho = (((W+E)+(S+N)) + b) - 4u, all in double. Between   */
-                      /*   two SWEEP tasks queued ahead, an fp64 streaming engine   */
-                      /*   at depth 12 may sum it inside the pass that runs on from  */
-                      /*   the first into the second (pk_info.tasks_fused): the     */
-                      /*   same R, fields and done records; the field at the first  */
-                      /*   task's end is then never stored                          */
+                      /*   rho = (((W+E)+(S+N)) + b) - 4u, all in double. With a   */
+                      /*   SWEEP task queued after it, an fp64 streaming engine at  */
+                      /*   depth 12 may sum it inside a pass that runs on into that  */
+                      /*   task (pk_info.tasks_fused): the same R, fields and done  */
+                      /*   records; the field a fused SWEEP task ends with is then  */
+                      /*   never stored                                              */
 #define PK_EXIT 3     /* the persistent kernel returns; the engine stays readable   */
 #define PK_BARRIER 4  /* n grid barriers and nothing else (persistent only; timing) */
 #define PK_STAMP 5    /* n rounds of the barrier visibility check (persistent only):*/
@@ -261,10 +261,12 @@ typedef struct pk_info {
     int wall_clock_khz;      /* rate of the device wall clock that task times and the   */
                              /* trace count in                                           */
     int trace_capacity;      /* PK_DBG_TRACE: events each block's ring holds; else 0   */
-    int64_t tasks_fused;     /* PERSISTENT, STREAM: SWEEP tasks whose last pass ran on  */
-                             /* into the SWEEP task two slots later, the RESIDUAL task */
-                             /* between them summed inside that pass (the host had     */
-                             /* queued both ahead)                                      */
+    int64_t tasks_fused;     /* PERSISTENT, STREAM: tasks that ran sweeps of a later    */
+                             /* SWEEP task: a SWEEP task whose last pass ran on into   */
+                             /* the SWEEP task two slots later (the RESIDUAL between   */
+                             /* them summed inside that pass), or a RESIDUAL task that */
+                             /* ran the next SWEEP task's first pass and summed its    */
+                             /* level 0 (the host had queued them ahead)                */
 } pk_info;
 
 typedef struct pk_engine pk_engine;

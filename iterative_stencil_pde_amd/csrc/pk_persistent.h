@@ -636,17 +636,29 @@ __device__ __forceinline__ void fuse_decide(const pk_kargs& a, FuseState* fs, in
     __hip_atomic_store(&a.st->fuse_seq, ok ? seq : 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Leader only, at the start of a RESIDUAL task of a field no pass has summed:
+// whether the next task is a SWEEP of at least PK_MAX_PASS sweeps, already
+// published by the host (the decision, as for fuse_decide, through a barrier).
+__device__ __forceinline__ void fuse_decide_next(const pk_kargs& a, uint64_t seq) {
+    const uint64_t w = __hip_atomic_load(&a.mail->slot[(seq + 1) % PK_RING].word, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_SYSTEM);
+    const bool ok = static_cast<uint32_t>(w >> 32) == static_cast<uint32_t>(seq + 1) &&
+                    static_cast<int>((w >> 28) & 0xF) == PK_SWEEP && static_cast<int>(w & PK_TASK_N_MAX) >= PK_MAX_PASS;
+    __hip_atomic_store(&a.st->fuse_seq, ok ? seq : 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // n sub-sweeps of the field in u[cur] in the engine's layout (cur flips):
 // Jacobi sweeps, or (rb) red-black half-sweeps, red first.
 // fusable (streaming layout, fp64): a plain SWEEP task (fs->cur_seq) that may
-// run its last pass on into a later SWEEP task; returns the sweeps of that later
-// task applied here (0 if none). The fp32 kernels leave fusion out: its code cost
+// run its last pass on into a later SWEEP task; run_ahead (n = 0): run the next
+// task's first pass with the residual of its level 0; returns the sweeps of that
+// later task applied here (0 if none). The fp32 kernels leave fusion out: its code cost
 // their passes 10% (4096^2 fp32 Laplace, 4.48 against 4.08 us per sweep) in
 // register pressure, and the fp32 workloads that stream run one long task.
 template <typename T, bool HAS_B, int LAYOUT, int RT, bool TRACE>
 __device__ __forceinline__ int sweeps_task(const pk_kargs& a, int n, bool rb, int& cur, BarrierCtx& bc,
                                            T* lds, ResidualState& rs, double* s_red, bool fusable,
-                                           FuseState* fs) {
+                                           FuseState* fs, bool run_ahead = false) {
     int ahead = 0;
     if constexpr (LAYOUT == PK_LAYOUT_RESIDENT) {
         if (rb)
@@ -670,7 +682,8 @@ __device__ __forceinline__ int sweeps_task(const pk_kargs& a, int n, bool rb, in
         // same expression on the same operands.
         const int P = a.pass_sweeps;
         const bool fz = sizeof(T) == 8 && fusable && !rb && !bc.broken && P == PK_MAX_PASS;
-        bool fused = false;  // the leader's decision for the tail (uniform)
+        // (run_ahead: n = 0, a RESIDUAL task running the next task's first pass)
+        bool fused = run_ahead;  // the leader's decision for the tail (uniform)
         int s = 0;
         while (s < n) {
             const int left = n - s;
@@ -1027,7 +1040,7 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
         double res = 0.0;
         int64_t errs = 0;
         int status = PK_OK;
-        int fused_task = 0;  // the task's last pass ran on into the SWEEP task two slots later
+        int fused_task = 0;  // the task ran sweeps of a later SWEEP task (fused)
         if (kind == PK_SWEEP || kind == PK_SWEEP_RB || kind == PK_RESIDUAL || kind == PK_SWEEP_UNTIL) {
             // The sweeping tasks share one loop (one copy of the sweep and
             // residual code in the kernel): an optional residual check, then up
@@ -1055,15 +1068,34 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
                 tol = s_tol;
                 every = s_every;
             }
+            // A RESIDUAL of a field no pass has summed, with a SWEEP of at least a
+            // pass queued right after it: that SWEEP task's first pass runs here (as
+            // the tail of a SWEEP task fused into it does, through the one call of
+            // sweeps_task below) and sums the residual of its level 0, the field as
+            // it is now, instead of a pass that only reads the field; the SWEEP task
+            // then starts with those sweeps applied.
+            bool run_ahead = false;
+            if constexpr (LAYOUT == PK_LAYOUT_STREAM && sizeof(T) == 8) {
+                if (kind == PK_RESIDUAL && !rs.ready && !bc.broken && a.pass_sweeps == PK_MAX_PASS) {
+                    if (leader) fuse_decide_next(a, seq);
+                    grid_barrier(bc);
+                    if (threadIdx.x == 0)
+                        s_fuse.dec = __hip_atomic_load(&a.st->fuse_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                                     *reinterpret_cast<volatile unsigned long long*>(&s_seq);
+                    __syncthreads();
+                    run_ahead = s_fuse.dec != 0;
+                    __syncthreads();
+                }
+            }
             {
                 int done = 0;
                 for (;;) {  // the same decisions in every block
-                    if (check) {
+                    if (check && !run_ahead) {
                         res = residual_round<T, HAS_B>(a, cur, bc, rs, s_red, until);
                         if (res <= tol) break;
                     }
-                    if (done >= budget) break;
-                    const int k = min(every, budget - done);
+                    if (!run_ahead && done >= budget) break;
+                    const int k = run_ahead ? 0 : min(every, budget - done);
                     // red-black: k iterations = 2k half-sweeps, each computed into
                     // the other buffer with the other colour copied (the in-place
                     // result: a node never reads its own colour)
@@ -1071,17 +1103,24 @@ __global__ void __launch_bounds__((PkMaxThreads<T, HAS_B, LAYOUT>::value)) pk_pe
                     if (fusable && threadIdx.x == 0)
                         s_fuse.cur_seq = *reinterpret_cast<volatile unsigned long long*>(&s_seq);
                     const int ahead = sweeps_task<T, HAS_B, LAYOUT, RT, TRACE>(
-                        a, rb ? 2 * k : k, rb, cur, bc, reinterpret_cast<T*>(pk_lds), rs, s_red, fusable, &s_fuse);
-                    if (ahead > 0) {  // uniform: the SWEEP task at seq + 2 is ahead by that much
+                        a, rb ? 2 * k : k, rb, cur, bc, reinterpret_cast<T*>(pk_lds), rs, s_red, fusable, &s_fuse,
+                        run_ahead);
+                    if (ahead > 0) {  // uniform: a later SWEEP task is ahead by that much
                         fused_task = 1;
                         __syncthreads();
                         if (threadIdx.x == 0) {
-                            // copied from shared memory here: a register copy of the
-                            // sequence made for this store was kept, and spilled,
-                            // across the task
-                            s_fuse.from_seq = *reinterpret_cast<volatile unsigned long long*>(&s_seq);
+                            // the task two slots after this SWEEP task, or the one right
+                            // after this RESIDUAL (copied from shared memory here: a
+                            // register copy of the sequence made for this store was
+                            // kept, and spilled, across the task)
+                            s_fuse.from_seq = *reinterpret_cast<volatile unsigned long long*>(&s_seq) -
+                                              (kind == PK_RESIDUAL ? 1u : 0u);
                             s_fuse.pre = ahead;
                         }
+                    }
+                    if (run_ahead) {  // then the residual round sums what that pass summed
+                        run_ahead = false;
+                        continue;
                     }
                     done += k;
                 }

@@ -80,7 +80,7 @@ struct alignas(PK_LINE) pk_done_rec {
     int32_t cur;  // buffer index that holds the whole field after this task (after
                   // its last pass, where that pass ran on into a later task)
     int32_t carried;  // bit 0: the task was handed on by the previous task's barrier;
-                      // bit 1: its last pass ran on into the SWEEP task two slots later
+                      // bit 1: it ran sweeps of a later SWEEP task (fused)
 };
 
 // Parameters of a PK_SWEEP_UNTIL task, written by the host before it releases

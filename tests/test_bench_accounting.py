@@ -72,13 +72,15 @@ def test_script_counts_fused_tails():
     46 sweeps left (12 x 3 and a fused tail each), 48 (12 x 3, then its last 12 as
     a pass of their own and the next task's first 12 summing the residual of level
     0: 5 passes), 38, 40, 42, and the last, 44 with nothing to fuse into (12 x 3,
-    then 8 that sums the residual): 42 passes for 500 sweeps."""
+    then 8 that sums the residual). The step's first RESIDUAL (of a field no pass
+    has summed) runs the first task's first pass and sums its level 0, so that task
+    starts 12 sweeps ahead: 42 passes for 500 sweeps and no pass that only reads."""
     script = [("residual",)] + [("sweep", 50), ("residual",)] * 10 + [("readback",)]
     w = _shape_only(8192, 8192, np.float64, True, script)
     assert bench.fuses(w, 12) and not bench.fuses(w, 8)
     stats = {}
-    assert bench.script_counts(w, 12, stats=stats) == (500, 42, 1)
-    assert stats["fused"] == 9
+    assert bench.script_counts(w, 12, stats=stats) == (500, 42, 0)
+    assert stats["fused"] == 10
     # the same script in fp32 runs every task on its own
     w32 = _shape_only(8192, 8192, np.float32, True, script)
     assert not bench.fuses(w32, 12)
