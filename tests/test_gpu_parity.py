@@ -229,7 +229,9 @@ def test_stream_neighbor_counters(shape, dtype, poisson, k, band_rows, blocks):
     check_against_oracle(w, got, ref, f"nbr/k{k}/rows{band_rows}/g{info.grid_blocks}/{ny}x{nx}")
 
 
-FUSE_SCRIPT = [("residual",), ("sweep", 30), ("residual",), ("sweep", 25), ("residual",), ("sweep", 12),
+# (the first task is long, so that the host has queued the rest before the device
+# reaches the first fusion point)
+FUSE_SCRIPT = [("sweep", 200), ("residual",), ("residual",), ("sweep", 30), ("residual",), ("sweep", 25), ("residual",), ("sweep", 12),
                ("residual",), ("sweep", 7), ("residual",), ("sweep", 40), ("residual",), ("sweep", 16),
                ("residual",), ("sweep", 8), ("residual",), ("sweep", 3), ("residual",), ("sweep", 1),
                ("residual",), ("sweep", 24), ("residual",), ("sweep", 30), ("residual",), ("residual",),
