@@ -64,8 +64,10 @@ extern "C" {
 #define PK_LAUNCH 1     /* one kernel launch per sweep (baseline)               */
 
 /* Work layout of the persistent sweeping tasks.
- * STREAM: every sweep streams the field through HBM (grid-stride over bands
- *   of rows x 64-lane column strips, 128-bit row loads, 3-row register window).
+ * STREAM: passes of up to pass_sweeps sweeps stream the field through HBM once
+ *   each: the field is cut into units (a band of rows x a 64-lane column strip,
+ *   16-byte row loads), one per wave, and each wave marches its unit keeping
+ *   every sweep level of the pass in registers.
  * RESIDENT: each block keeps its band of rows (plus halo rows) in LDS for the
  *   whole task; only the halo rows go through HBM, once every halo_depth sweeps
  *   (the wider-halo scheme of "Persistent Kernels", "Reflections and next
@@ -212,7 +214,9 @@ typedef struct pk_opts {
                            /* meet once per k sweeps; 0 = 12 where u, u' and b      */
                            /* exceed the 256 MiB Infinity Cache, else 8 (pk_info    */
                            /* reports it). A task's last pass is at most 8 deep     */
-                           /* (12 -> 4 + 8), as are red-black passes                */
+                           /* (12 -> 4 + 8), as are red-black passes, except an    */
+                           /* fp64 pass of 12 that runs on into a queued SWEEP task */
+                           /* (see PK_RESIDUAL)                                      */
     int band_rows;         /* STREAM passes: rows per band (a unit is a band x one  */
                            /* strip, one per wave); 0 = automatic                   */
     int exchange;          /* PK_EXCHANGE_* (tiles; STREAM: BARRIER or NEIGHBOR)   */
@@ -222,8 +226,10 @@ typedef struct pk_opts {
 #define PK_TASK_N_MAX 0x0FFFFFFF /* largest n of one task */
 
 typedef struct pk_task {
-    int kind; /* PK_SWEEP, PK_RESIDUAL, PK_EXIT, PK_BARRIER, PK_STAMP */
-    int n;    /* count for SWEEP, BARRIER and STAMP; ignored otherwise */
+    int kind; /* PK_SWEEP, PK_SWEEP_RB, PK_RESIDUAL, PK_EXIT, PK_BARRIER,  */
+              /* PK_STAMP or PK_BLOCKSYNC (PK_SWEEP_UNTIL: pk_submit_until)  */
+    int n;    /* count for SWEEP, SWEEP_RB, BARRIER, STAMP and BLOCKSYNC;   */
+              /* ignored otherwise                                         */
 } pk_task;
 
 typedef struct pk_result {
