@@ -853,3 +853,62 @@ def test_fused_residual_after_streaming_passes(shape, dtype, poisson, k):
     assert np.array_equal(got["final"], launch["final"])
     for x, y in zip(got["residuals"], launch["residuals"]):
         assert abs(x - y) <= 1e-12 * y, (x, y)
+
+
+# ---- field buffers past 4 GiB ------------------------------------------------
+# 1030 rows of 4 MiB (about 4.3 GB per field buffer): fp32 Laplace with 2^20 + 5
+# columns, fp64 Poisson with 2^19 + 3
+BIG_CASES = {"f32-laplace": (1030, (1 << 20) + 5, np.float32, False),
+             "f64-poisson": (1030, (1 << 19) + 3, np.float64, True)}
+BIG_SCRIPT = [("residual",), ("sweep", 29), ("residual",)]
+
+
+@pytest.fixture(scope="module")
+def big_cache():
+    return {}
+
+
+def _compare_rows(got, ref, rows=32):
+    """Cells that differ in any bit, and max |got - ref|, a block of rows at a
+    time (whole-array float64 copies of these fields would take tens of GB)."""
+    ui = np.uint32 if ref.dtype == np.float32 else np.uint64
+    nonbit, err = 0, 0.0
+    for r0 in range(0, ref.shape[0], rows):
+        g, r = got[r0:r0 + rows], ref[r0:r0 + rows]
+        nonbit += int(np.count_nonzero(g.view(ui) != r.view(ui)))
+        err = max(err, float(np.max(np.abs(g.astype(np.float64) - r.astype(np.float64)))))
+    return nonbit, err
+
+
+@pytest.mark.parametrize("mode", ["persistent-auto", "launch"])
+@pytest.mark.parametrize("case", list(BIG_CASES))
+def test_field_buffers_past_4GiB(case, mode, big_cache):
+    """Field buffers larger than 4 GiB. The streaming passes address a unit's
+    rows (its band and 2 (k + 1) halo rows) through 32-bit buffer offsets, so the
+    planner cuts the bands short enough for that window to stay within 4 GiB; the
+    other kernels (single sweeps, residual, readback, the source's scaling) index
+    rows with 64-bit offsets. Every cell and both residuals against the oracle."""
+    ny, nx, dtype, poisson = BIG_CASES[case]
+    if case not in big_cache:
+        big_cache.clear()  # one case's arrays at a time
+        u, f = _random_case(ny, nx, dtype, poisson, seed=4242)
+        w = inputs.Workload(f"big{ny}x{nx}", nx, ny, dtype, 0.013, u, f, list(BIG_SCRIPT), "")
+        big_cache[case] = (w, run_oracle_script(w))
+    w, ref = big_cache[case]
+    got = run_engine_script(w, timeout_s=300, **MODES[mode])
+    info = got["info"]
+    pitch_bytes = info.pitch * np.dtype(dtype).itemsize
+    assert pitch_bytes * ny > (1 << 32)
+    if mode == "persistent-auto":
+        assert info.layout == pk.PK_LAYOUT_STREAM and info.pass_sweeps == pk.PK_MAX_PASS
+        window = (info.band_rows + 2 * (info.pass_sweeps + 1)) * pitch_bytes
+        say(f"  bands of {info.band_rows} rows: a unit's window {window / 2**30:.3f} GiB")
+        assert window <= 0xFFFFFFFF and info.band_rows < ny - 2
+    rng = float(ref["final"].max()) - float(ref["final"].min())
+    tol = 1e-5 * rng if dtype == np.float32 else 1e-12 * rng
+    nonbit, err = _compare_rows(got["final"], ref["final"])
+    say(f"  {case}/{mode}: max_abs={err:.3e} tol={tol:.3e} non_bitwise={nonbit}")
+    assert err <= tol
+    ok, worst = residual_gate(got["residuals"], ref["residuals"], dtype)
+    say(f"  {case}/{mode} residuals: worst/tol={worst:.3e}")
+    assert ok
