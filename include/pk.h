@@ -212,11 +212,15 @@ typedef struct pk_opts {
                            /* PK_EINVAL): each wave carries k levels of its band in */
                            /* registers, so the field crosses HBM and the blocks    */
                            /* meet once per k sweeps; 0 = 12 where u, u' and b      */
-                           /* exceed the 256 MiB Infinity Cache, else 8 (pk_info    */
-                           /* reports it). A task's last pass is at most 8 deep     */
-                           /* (12 -> 4 + 8), as are red-black passes, except an    */
-                           /* fp64 pass of 12 that runs on into a queued SWEEP task */
-                           /* (see PK_RESIDUAL)                                      */
+                           /* exceed the 256 MiB Infinity Cache, else 8, shallower  */
+                           /* where the field passes 4 GiB and its rows are so long */
+                           /* that a unit's rows (its band and 2 (k + 1) halo rows) */
+                           /* would pass the 4 GiB a pass addresses (pk_info        */
+                           /* reports it); an explicit depth whose window cannot    */
+                           /* fit is PK_EINVAL. A task's last                       */
+                           /* pass is at most 8 deep (12 -> 4 + 8), as are         */
+                           /* red-black passes, except an fp64 pass of 12 that runs */
+                           /* on into a queued SWEEP task (see PK_RESIDUAL)         */
     int band_rows;         /* STREAM passes: rows per band (a unit is a band x one  */
                            /* strip, one per wave); 0 = automatic                   */
     int exchange;          /* PK_EXCHANGE_* (tiles; STREAM: BARRIER or NEIGHBOR)   */
@@ -294,7 +298,9 @@ void pk_opts_default(pk_opts* o);
  * In PK_PERSISTENT mode the cooperative kernel is launched before returning, once,
  * with a grid sized from the occupancy query ("@persistent" page, "What it
  * promises"; "Grid-Wide Barriers", "The residency requirement").
- * Errors: PK_EINVAL (sizes, opts, NULL bc or out, h <= 0 when required),
+ * Errors: PK_EINVAL (sizes, opts, NULL bc or out, h <= 0 when required; rows
+ * longer than 1 GiB; a field taller than 4 GiB of its rows whose rows are too
+ * long for a pass's 4 GiB window, about 850 MB even at a depth of 1),
  * PK_ENOMEM, PK_ELAUNCH (grid not co-resident / launch refused), PK_EDEVICE.
  * On error *out is left unchanged and nothing stays allocated. */
 int pk_create(int nx, int ny, const void* bc, const void* src, const pk_opts* o,

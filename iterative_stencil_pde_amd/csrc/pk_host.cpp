@@ -398,6 +398,15 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         const uint64_t streamed = static_cast<uint64_t>(e->pitch_bytes) * e->ny * (e->has_b ? 3 : 2);
         const bool hbm = streamed > kInfinityCacheBytes;
         p.pass_sweeps = o.pass_sweeps > 0 ? o.pass_sweeps : (hbm ? PK_MAX_PASS : PK_SHALLOW_PASS);
+        // rows so long that a unit's window at that depth (2 (k + 1) halo rows and
+        // at least one band row, addressed with 32-bit byte offsets) would pass
+        // 4 GiB where the field itself is taller than that: the deepest depth
+        // whose window fits (checked again below)
+        const uint64_t fit = 0xFFFFFFFFull / e->pitch_bytes;
+        if (o.pass_sweeps == 0 && static_cast<uint64_t>(e->ny) > fit) {
+            while (p.pass_sweeps > 1 && fit < static_cast<uint64_t>(2 * (p.pass_sweeps + 1) + 1))
+                p.pass_sweeps = p.pass_sweeps == PK_MAX_PASS ? PK_SHALLOW_PASS : p.pass_sweeps - 1;
+        }
         // march direction: where the passes stream from HBM, every band but the
         // last marches down (8192^2 fp64 Poisson: 31.8 -> 30.9 us per sweep);
         // where the arrays sit in the Infinity Cache, neighbouring bands march in
@@ -421,11 +430,14 @@ int plan_engine(pk_engine* e, const pk_opts& o, const hipDeviceProp_t& prop) {
         bands = std::min(bands, std::max(1, interior / (4 * k)));
         p.pband_rows = o.band_rows > 0 ? std::min(o.band_rows, interior) : ceil_div(interior, bands);
         // a pass addresses a unit's rows (band + 2L halo rows, L <= k + 1 levels:
-        // a task's last pass also sums the residual) through 32-bit byte offsets:
-        // shorter bands for very wide rows, and refuse what cannot fit
+        // a task's last pass also sums the residual, and never past the field's
+        // own rows) through 32-bit byte offsets: where the field is taller than
+        // 4 GiB of rows, shorter bands for very wide rows, and refuse what cannot fit
         const uint64_t lim = 0xFFFFFFFFull / e->pitch_bytes;
-        if (lim < static_cast<uint64_t>(2 * (k + 1) + 1)) return PK_EINVAL;
-        p.pband_rows = static_cast<int>(std::min<uint64_t>(p.pband_rows, lim - 2 * (k + 1)));
+        if (static_cast<uint64_t>(e->ny) > lim) {
+            if (lim < static_cast<uint64_t>(2 * (k + 1) + 1)) return PK_EINVAL;
+            p.pband_rows = static_cast<int>(std::min<uint64_t>(p.pband_rows, lim - 2 * (k + 1)));
+        }
         p.pbands = ceil_div(interior, p.pband_rows);
         // neighbour counters between two full-depth passes: the units of such a
         // pass and the bands its k-row halo reaches; beyond PK_PASS_NBR_DIST bands

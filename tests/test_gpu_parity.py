@@ -912,3 +912,35 @@ def test_field_buffers_past_4GiB(case, mode, big_cache):
     ok, worst = residual_gate(got["residuals"], ref["residuals"], dtype)
     say(f"  {case}/{mode} residuals: worst/tol={worst:.3e}")
     assert ok
+
+
+def test_rows_too_long_for_a_deep_pass():
+    """A field taller than 4 GiB of its rows, with rows of 160 MB (fp32, 40,000,001
+    columns, 28 rows: 4.5 GB a buffer, so the automatic depth would be 12). At
+    depth 12 a unit's window (a band row and 26 halo rows) would pass the 4 GiB a
+    pass addresses, so the planner takes depth 8, with bands short enough for the
+    26 rows that fit, and an explicit depth of 12 is refused. Every cell and both
+    residuals against the oracle."""
+    ny, nx = 28, 40_000_001
+    u, _ = _random_case(ny, nx, np.float32, False, seed=77)
+    w = inputs.Workload(f"long{ny}x{nx}", nx, ny, np.float32, 0.013, u, None,
+                        [("residual",), ("sweep", 13), ("residual",)], "")
+    with pytest.raises(pk.PkError) as refused:
+        pk.Engine(w.u0, None, h=w.h, mode=pk.PK_PERSISTENT, layout=pk.PK_LAYOUT_STREAM,
+                  pass_sweeps=pk.PK_MAX_PASS)
+    assert refused.value.status == pk.PK_EINVAL
+    ref = run_oracle_script(w)
+    got = run_engine_script(w, timeout_s=300, mode=pk.PK_PERSISTENT)
+    info = got["info"]
+    pitch_bytes = info.pitch * 4
+    window = (info.band_rows + 2 * (info.pass_sweeps + 1)) * pitch_bytes
+    say(f"  depth {info.pass_sweeps}, bands of {info.band_rows} rows: a unit's window {window / 2**30:.3f} GiB")
+    assert pitch_bytes * ny > (1 << 32)
+    assert info.layout == pk.PK_LAYOUT_STREAM and info.pass_sweeps == 8 and window <= 0xFFFFFFFF
+    rng = float(ref["final"].max()) - float(ref["final"].min())
+    nonbit, err = _compare_rows(got["final"], ref["final"], rows=2)
+    say(f"  long rows: max_abs={err:.3e} tol={1e-5 * rng:.3e} non_bitwise={nonbit}")
+    assert err <= 1e-5 * rng
+    ok, worst = residual_gate(got["residuals"], ref["residuals"], np.float32)
+    say(f"  long rows residuals: worst/tol={worst:.3e}")
+    assert ok
