@@ -914,13 +914,14 @@ def test_field_buffers_past_4GiB(case, mode, big_cache):
     assert ok
 
 
-def test_rows_too_long_for_a_deep_pass():
+def test_rows_too_long_for_a_deep_pass(big_cache):
     """A field taller than 4 GiB of its rows, with rows of 160 MB (fp32, 40,000,001
     columns, 28 rows: 4.5 GB a buffer, so the automatic depth would be 12). At
     depth 12 a unit's window (a band row and 26 halo rows) would pass the 4 GiB a
     pass addresses, so the planner takes depth 8, with bands short enough for the
     26 rows that fit, and an explicit depth of 12 is refused. Every cell and both
     residuals against the oracle."""
+    big_cache.clear()  # the arrays of the cases above are no longer needed
     ny, nx = 28, 40_000_001
     u, _ = _random_case(ny, nx, np.float32, False, seed=77)
     w = inputs.Workload(f"long{ny}x{nx}", nx, ny, np.float32, 0.013, u, None,
